@@ -1,0 +1,12 @@
+"""MI355X-native Kimi Delta Attention (KDA) chunked forward.
+
+The compute lives in libkda.so (hand-written HIP for gfx950, C ABI in
+include/kda.h).  This package is a thin ctypes binding: it turns torch tensors
+into C descriptors and passes the current HIP stream; every step of the forward
+pass runs in the library's kernels.  There is no fallback: if libkda.so is
+missing or the tensors are not on the GPU, the call raises.
+"""
+from .binding import (KdaError, kda_fwd, kda_fwd_trace, kda_dv_slices, library_path,  # noqa: F401
+                      load_library)
+
+__all__ = ["KdaError", "kda_fwd", "kda_fwd_trace", "kda_dv_slices", "library_path", "load_library"]

@@ -1,0 +1,145 @@
+"""ctypes binding of libkda.so (argument marshalling only).
+
+Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_trace,
+kda_status_string, kda_dv_slices.  Tensors are passed as kda_tensor_t
+descriptors built from torch tensors (data pointer, dtype, shape, strides); the
+stream is torch's current HIP stream unless one is given.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
+_DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
+STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
+                "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP"]
+EXPORTED = ["kda_fwd", "kda_fwd_trace", "kda_status_string", "kda_dv_slices"]
+
+
+class KdaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class KdaTrace(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("G", "Aqk", "Akk", "T", "W", "U", "v_new", "h")]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+        self.name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library(path=None):
+    """Loads libkda.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with gated_delta_rule_35_amd/build.py "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    tp = ctypes.POINTER(KdaTensor)
+    lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p]
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp,
+                                  ctypes.POINTER(KdaTrace), ctypes.c_void_p]
+    lib.kda_fwd_trace.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_dv_slices.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.kda_dv_slices.restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def describe(t):
+    """kda_tensor_t for a torch tensor (or None).  No copies and no checks: the C
+    library validates dtype, shape, layout and alignment."""
+    if t is None:
+        return None
+    d = KdaTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _DTYPES.get(t.dtype, 99)
+    d.ndim = t.dim()
+    if t.dim() > 4:
+        raise ValueError("kda tensors have at most 4 dimensions")
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def _stream_handle(stream, tensors):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    dev = next((t.device for t in tensors if t is not None and t.is_cuda), None)
+    if dev is None:
+        raise ValueError("kda_fwd needs its tensors on the GPU")
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(lib, status):
+    if status != 0:
+        raise KdaError(status, lib.kda_status_string(status).decode())
+
+
+def kda_dv_slices(num_sequences, num_value_heads):
+    return int(load_library().kda_dv_slices(num_sequences, num_value_heads))
+
+
+def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace):
+    lib = load_library()
+    tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kda_fwd needs every tensor on the GPU")
+    descs = [describe(t) for t in tensors]
+    s = _stream_handle(stream, tensors)
+    args = [_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]), float(scale),
+            _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8])]
+    if trace is None:
+        _check(lib, lib.kda_fwd(*args, s))
+    else:
+        tr = KdaTrace(**{n: (t.data_ptr() if t is not None else None) for n, t in trace.items()})
+        _check(lib, lib.kda_fwd_trace(*args, ctypes.byref(tr), s))
+
+
+def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+            stream=None):
+    """KDA forward.  Returns (out, final_state); allocates them when not given
+    (final_state is allocated only when `final_state=True` is passed)."""
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    if final_state is True:
+        n = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        final_state = torch.empty((n, v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=v.device)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None)
+    return out, final_state
+
+
+def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state=None, out=None,
+                  final_state=None, stream=None):
+    """kda_fwd that also fills the fp32 intermediate dumps in `trace`, a dict with
+    any of the keys G, Aqk, Akk, T, W, U, v_new, h (see include/kda.h)."""
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace)
+    return out, final_state

@@ -1,0 +1,174 @@
+// C-ABI front end of the KDA forward library: argument checks and launch.
+//
+// Every check runs on the host before any HIP call, so a rejected call enqueues
+// nothing.  The number of sequences comes from the shape of cu_seqlens; the host
+// never reads device memory and never synchronises.  The checks restate the
+// input contract the pages describe for the public forward path ("cuLA PR #135",
+// review of the KDA index helpers: chunk size and sorted cu_seqlens; "cuLA PR
+// #131", review of the public forward: inputs made contiguous after validation).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "../../include/kda.h"
+#include "kda_kernel.h"
+
+namespace {
+
+constexpr int64_t kHeadDim = 128;
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;  // 512 threads each: grid stays below 2^31 work-items
+
+int64_t numel(const kda_tensor_t* t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+size_t elem_size(kda_dtype_t d) { return (d == KDA_BF16 || d == KDA_F16) ? 2 : 4; }
+
+bool contiguous(const kda_tensor_t* t) {
+    int64_t expect = 1;
+    for (int i = t->ndim - 1; i >= 0; --i) {
+        if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+        expect *= t->shape[i];
+    }
+    return true;
+}
+
+kda_status_t check_tensor(const kda_tensor_t* t, int ndim, kda_dtype_t d0, kda_dtype_t d1, size_t align) {
+    if (!t) return KDA_ERR_NULL;
+    if (t->dtype != d0 && t->dtype != d1) return KDA_ERR_DTYPE;
+    if (t->ndim != ndim) return KDA_ERR_SHAPE;
+    for (int i = 0; i < ndim; ++i)
+        if (t->shape[i] < 0) return KDA_ERR_SHAPE;
+    const int64_t n = numel(t);
+    if (n > 0 && !t->data) return KDA_ERR_NULL;
+    if (!contiguous(t)) return KDA_ERR_LAYOUT;
+    if (n > 0 && (reinterpret_cast<uintptr_t>(t->data) % align) != 0) return KDA_ERR_LAYOUT;
+    return KDA_OK;
+}
+
+bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
+    for (int i = 0; i < nd; ++i)
+        if (a->shape[i] != s[i]) return false;
+    return true;
+}
+
+kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                 const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
+                 const kda_tensor_t* out, const kda_tensor_t* hT, const kda_trace_t* trace, void* stream) {
+    kda_status_t st;
+    if ((st = check_tensor(q, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(k, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(v, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(g, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if (!beta) return KDA_ERR_NULL;
+    if ((st = check_tensor(beta, 3, KDA_BF16, KDA_F32, elem_size(beta->dtype))) != KDA_OK) return st;
+    if ((st = check_tensor(out, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if (cu && (st = check_tensor(cu, 1, KDA_I32, KDA_I32, 4)) != KDA_OK) return st;
+    if (h0 && (st = check_tensor(h0, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if (hT && (st = check_tensor(hT, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+
+    const int64_t B = q->shape[0], T = q->shape[1], Hq = q->shape[2], Hv = v->shape[2];
+    if (q->shape[3] != kHeadDim || v->shape[3] != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if (!same_shape(k, q->shape, 4)) return KDA_ERR_SHAPE;
+    if (v->shape[0] != B || v->shape[1] != T) return KDA_ERR_SHAPE;
+    const int64_t gs[4] = {B, T, Hv, kHeadDim};
+    if (!same_shape(g, gs, 4) || !same_shape(out, gs, 4)) return KDA_ERR_SHAPE;
+    const int64_t bs[3] = {B, T, Hv};
+    if (!same_shape(beta, bs, 3)) return KDA_ERR_SHAPE;
+    if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
+    if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
+    int64_t N = B;
+    if (cu) {
+        if (B != 1) return KDA_ERR_UNSUPPORTED;
+        if (cu->shape[0] < 1) return KDA_ERR_SHAPE;
+        N = cu->shape[0] - 1;
+    }
+    const int64_t ss[4] = {N, Hv, kHeadDim, kHeadDim};
+    if (h0 && !same_shape(h0, ss, 4)) return KDA_ERR_SHAPE;
+    if (hT && !same_shape(hT, ss, 4)) return KDA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
+    if (Hv > (int64_t(1) << 20) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
+    const int S = kda_dv_slices(N, Hv);
+    if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+
+    kda::KdaParams p{};
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.k = static_cast<const uint16_t*>(k->data);
+    p.v = static_cast<const uint16_t*>(v->data);
+    p.g = static_cast<const float*>(g->data);
+    p.beta = beta->data;
+    p.beta_f32 = beta->dtype == KDA_F32 ? 1 : 0;
+    p.cu = cu ? static_cast<const int32_t*>(cu->data) : nullptr;
+    p.h0 = h0 ? static_cast<const float*>(h0->data) : nullptr;
+    p.o = static_cast<uint16_t*>(out->data);
+    p.hT = hT ? static_cast<float*>(hT->data) : nullptr;
+    p.T = T;
+    p.N = static_cast<int32_t>(N);
+    p.Hq = static_cast<int32_t>(Hq);
+    p.Hv = static_cast<int32_t>(Hv);
+    p.scale = scale;
+    if (trace) {
+        p.tr_G = trace->G;
+        p.tr_Aqk = trace->Aqk;
+        p.tr_Akk = trace->Akk;
+        p.tr_T = trace->T;
+        p.tr_W = trace->W;
+        p.tr_U = trace->U;
+        p.tr_vnew = trace->v_new;
+        p.tr_h = trace->h;
+    }
+    if (N == 0 || (T == 0 && !hT)) return KDA_OK;  // nothing to compute or write
+    const hipError_t e = kda::launch_kda_fwd(p, S, trace != nullptr, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (std::getenv("KDA_DEBUG_SYNC")) {
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads) {
+    // Two 64-wide dv slices per head fill the 256 CUs once N * Hv >= 128; below
+    // that, four 32-wide slices.
+    return num_sequences * num_value_heads >= 128 ? 2 : 4;
+}
+
+kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                     const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
+                     const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
+                     void* stream) {
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, nullptr, stream);
+}
+
+kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state, const kda_trace_t* trace,
+                           void* stream) {
+    if (!trace) return KDA_ERR_NULL;
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, trace, stream);
+}
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required descriptor or data pointer is NULL";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unsupported dtype";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: ranks or sizes disagree";
+        case KDA_ERR_LAYOUT: return "KDA_ERR_LAYOUT: tensor not contiguous or not aligned";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported configuration";
+        case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scale must be finite and positive";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+    }
+    return "KDA: unknown status";
+}
+
+}  // extern "C"

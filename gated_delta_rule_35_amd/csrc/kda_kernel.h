@@ -1,0 +1,36 @@
+// Internal interface between the C-ABI front end and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct KdaParams {
+    const uint16_t* q;     // [tokens, Hq, 128] bf16 bits
+    const uint16_t* k;     // [tokens, Hq, 128] bf16 bits
+    const uint16_t* v;     // [tokens, Hv, 128] bf16 bits
+    const float* g;        // [tokens, Hv, 128]
+    const void* beta;      // [tokens, Hv] bf16 bits or fp32
+    const int32_t* cu;     // [N+1] or nullptr (fixed length)
+    const float* h0;       // [N, Hv, 128, 128] or nullptr
+    uint16_t* o;           // [tokens, Hv, 128] bf16 bits
+    float* hT;             // [N, Hv, 128, 128] or nullptr
+    int64_t T;             // tokens per sequence (fixed length) or total tokens (packed)
+    int32_t N, Hq, Hv;
+    int32_t beta_f32;
+    float scale;
+    // Optional fp32 dumps of the intermediates (all nullptr in production launches).
+    float* tr_G;
+    float* tr_Aqk;
+    float* tr_Akk;
+    float* tr_T;
+    float* tr_W;
+    float* tr_U;
+    float* tr_vnew;
+    float* tr_h;
+};
+
+// Enqueues the fused forward kernel: N * Hv * dv_slices work-groups on `stream`.
+hipError_t launch_kda_fwd(const KdaParams& p, int dv_slices, bool trace, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,146 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The library computes the chunked forward pass of KDA, the gated delta rule
+ * with a per-channel decay, whose GPU stages the pages name ("cuLA PR #131:
+ * SM100/SM103 KDA forward to pure CuTeDSL", sections Summary and Numerical
+ * behavior: chunk intra, FP32 Akk inversion, recompute W/U, causal masking, tail
+ * clamping; "cuLA REPO_LAYOUT.md", ops/ entries for the chunk delta-H and
+ * forward-output kernels).  For every sequence n and value head hv the
+ * library returns the outputs of the recurrence
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * evaluated chunk by chunk (chunk length 64) in one fused HIP kernel.
+ *
+ * Tensors are described by kda_tensor_t: a device pointer, a dtype, a rank
+ * and per-dimension sizes and strides counted in elements.  All tensors must
+ * be dense row-major (contiguous) and their data 16-byte aligned (beta and
+ * cu_seqlens: aligned to their element size).  The caller owns all memory;
+ * the library keeps no pointer after a call returns and allocates nothing.
+ *
+ * Shapes (B batch rows, T tokens per row, Hq query/key heads, Hv value heads,
+ * head dimension 128):
+ *   q, k           [B, T, Hq, 128]  bf16
+ *   v              [B, T, Hv, 128]  bf16
+ *   g              [B, T, Hv, 128]  fp32 log-decay (the activated gate, <= 0)
+ *   beta           [B, T, Hv]       bf16 or fp32
+ *   cu_seqlens     [N + 1]          int32, or NULL.  With cu_seqlens, B must be 1
+ *                                   and row 0 packs N sequences back to back:
+ *                                   sequence n covers tokens
+ *                                   [cu_seqlens[n], cu_seqlens[n+1]).  Without it,
+ *                                   N = B and batch row b is sequence b.
+ *   initial_state  [N, Hv, 128, 128] fp32 (key channel, value channel), or NULL
+ *                                   for a zero state
+ *   out            [B, T, Hv, 128]  bf16
+ *   final_state    [N, Hv, 128, 128] fp32, or NULL (not written)
+ * Grouped-value attention: Hq must divide Hv; value head hv reads query/key
+ * head hv / (Hv / Hq).  Every sequence is cut into chunks of 64 tokens from its
+ * own start; the last chunk may be partial.  Output rows of tokens that lie in
+ * no sequence (packed mode) are not written.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_BF16 = 0, KDA_F16 = 1, KDA_F32 = 2, KDA_I32 = 3 } kda_dtype_t;
+
+typedef struct {
+    void* data;          /* device pointer; may be NULL only if the tensor has no elements */
+    kda_dtype_t dtype;
+    int32_t ndim;        /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4];   /* in elements */
+} kda_tensor_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required descriptor or data pointer is NULL */
+    KDA_ERR_DTYPE = 2,       /* a dtype outside the table above */
+    KDA_ERR_SHAPE = 3,       /* ranks or sizes that disagree with each other */
+    KDA_ERR_LAYOUT = 4,      /* non-contiguous strides or misaligned data */
+    KDA_ERR_UNSUPPORTED = 5, /* head dim != 128, Hv % Hq != 0, B != 1 with cu_seqlens, grid too large */
+    KDA_ERR_VALUE = 6,       /* scale not finite or not > 0 */
+    KDA_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} kda_status_t;
+
+/*
+ * kda_fwd -- the KDA forward pass over a batch.
+ *
+ * Enqueues the work on `stream` (a hipStream_t; NULL is the null stream) and
+ * returns without waiting: the host never reads device memory, so the number of
+ * sequences comes from the shape of cu_seqlens, not its values.  Every argument
+ * is checked on the host before any HIP call; on an error nothing is enqueued.
+ * Results are bitwise reproducible from call to call (no atomics; each output
+ * element has exactly one writer and a fixed reduction order).
+ * initial_state may alias final_state (each state tile is read before it is
+ * written, by the same work-group).
+ * cu_seqlens must be non-decreasing with cu_seqlens[0] = 0 and
+ * cu_seqlens[N] <= T.  That is a precondition the host cannot check without a
+ * device read; the kernel clamps every sequence to [0, T) so that malformed
+ * values never cause an out-of-bounds access.
+ * Precision: q, k, v are bf16; the MFMA operands derived from them are fp16
+ * and all accumulation, the gate cumsum, the inversion and the state are
+ * fp32.  A chunk whose decay within a 16-token block exceeds exp(-8) on some
+ * channel takes an exact fp32 path for its diagonal blocks.
+ */
+kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                     const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                     const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                     const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
+
+/*
+ * Optional fp32 dumps of the chunked method's intermediates, for stage-by-stage
+ * checks of kda_fwd_trace.  Any pointer may be NULL.  Ttot = B * T.
+ *   G     [Ttot, Hv, 128]  chunk-local inclusive cumsum of g
+ *   Aqk   [Ttot, Hv, 64]   row of scale * sum_c q_i k_j exp(G_i - G_j), j <= i
+ *   Akk   [Ttot, Hv, 64]   row of beta_i * sum_c k_i k_j exp(G_i - G_j), j < i
+ *   T     [Ttot, Hv, 64]   row of (I + Akk)^{-1}
+ *   W     [Ttot, Hv, 128]  T (beta k exp G)
+ *   U     [Ttot, Hv, 128]  T (beta v)
+ *   v_new [Ttot, Hv, 128]  U - W h
+ *   h     [num_chunks, Hv, 128, 128]  state entering each chunk; chunks are
+ *         numbered by sequence, then by position within the sequence
+ * Row t of a per-token dump belongs to the token's own chunk; columns past the
+ * chunk's length are zero.  Rows of tokens in no sequence are not written.
+ */
+typedef struct {
+    float* G;
+    float* Aqk;
+    float* Akk;
+    float* T;
+    float* W;
+    float* U;
+    float* v_new;
+    float* h;
+} kda_trace_t;
+
+/*
+ * kda_fwd_trace -- kda_fwd plus the dumps above (a test and debugging entry; the
+ * same kernel with the extra stores compiled in).  Same arguments, checks and
+ * results as kda_fwd; `trace` may not be NULL.
+ */
+kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state,
+                           const kda_trace_t* trace, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* kda_status_string(kda_status_t status);
+
+/* Number of dv slices (work-groups per sequence and value head) that kda_fwd
+ * launches for N sequences and Hv value heads: 2 or 4. */
+int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

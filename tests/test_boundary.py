@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before any HIP call (so these run without a GPU;
+the data pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_35_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+FAKE = 0x7f0000000000  # 16-byte aligned, never dereferenced by the checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def T(shape, dtype=binding.KDA_BF16, data=FAKE, strides=None):
+    d = binding.KdaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    st = strides
+    if st is None:
+        st, acc = [], 1
+        for s in reversed(shape):
+            st.insert(0, acc)
+            acc *= s
+    for i, s in enumerate(shape):
+        d.shape[i] = s
+        d.stride[i] = st[i]
+    return d
+
+
+def good(B=1, T_=64, Hq=2, Hv=2, beta_dtype=binding.KDA_F32):
+    return dict(q=T([B, T_, Hq, 128]), k=T([B, T_, Hq, 128]), v=T([B, T_, Hv, 128]),
+                g=T([B, T_, Hv, 128], binding.KDA_F32), beta=T([B, T_, Hv], beta_dtype),
+                out=T([B, T_, Hv, 128]))
+
+
+def call(lib, a, scale=0.088, cu=None, h0=None, hT=None):
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    return lib.kda_fwd(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")),
+                       scale, r(cu), r(h0), r(a.get("out")), r(hT), None)
+
+
+def expect(lib, a, name, **kw):
+    st = call(lib, a, **kw)
+    assert binding.STATUS_NAMES[st] == name, (binding.STATUS_NAMES[st], name)
+
+
+def test_null_descriptor_and_null_data(lib):
+    for key in ("q", "k", "v", "g", "beta", "out"):
+        a = good()
+        a[key] = None
+        expect(lib, a, "KDA_ERR_NULL")
+    a = good()
+    a["q"] = T([1, 64, 2, 128], data=None)
+    expect(lib, a, "KDA_ERR_NULL")
+
+
+def test_dtypes(lib):
+    a = good()
+    a["q"] = T([1, 64, 2, 128], binding.KDA_F16)
+    expect(lib, a, "KDA_ERR_DTYPE")
+    a = good()
+    a["g"] = T([1, 64, 2, 128], binding.KDA_BF16)
+    expect(lib, a, "KDA_ERR_DTYPE")
+    a = good()
+    a["beta"] = T([1, 64, 2], binding.KDA_I32)
+    expect(lib, a, "KDA_ERR_DTYPE")
+    a = good()
+    expect(lib, a, "KDA_ERR_DTYPE", cu=T([3], binding.KDA_F32))
+
+
+def test_shapes(lib):
+    a = good()
+    a["k"] = T([1, 64, 3, 128])
+    expect(lib, a, "KDA_ERR_SHAPE")
+    a = good()
+    a["v"] = T([1, 63, 2, 128])
+    expect(lib, a, "KDA_ERR_SHAPE")
+    a = good()
+    a["beta"] = T([1, 64, 3], binding.KDA_F32)
+    expect(lib, a, "KDA_ERR_SHAPE")
+    a = good()
+    a["out"] = T([1, 64, 2])
+    expect(lib, a, "KDA_ERR_SHAPE")
+    a = good(B=1)
+    expect(lib, a, "KDA_ERR_SHAPE", cu=T([4], binding.KDA_I32), h0=T([2, 2, 128, 128], binding.KDA_F32))
+    a = good(B=2)
+    expect(lib, a, "KDA_ERR_SHAPE", hT=T([3, 2, 128, 128], binding.KDA_F32))
+
+
+def test_unsupported(lib):
+    a = good()
+    a["q"] = T([1, 64, 2, 64])
+    a["k"] = T([1, 64, 2, 64])
+    expect(lib, a, "KDA_ERR_UNSUPPORTED")
+    a = good(Hq=3, Hv=4)
+    expect(lib, a, "KDA_ERR_UNSUPPORTED")
+    a = good(B=2)
+    expect(lib, a, "KDA_ERR_UNSUPPORTED", cu=T([3], binding.KDA_I32))
+
+
+def test_layout(lib):
+    a = good()
+    a["q"] = T([1, 64, 2, 128], strides=[64 * 2 * 128, 128, 64 * 128, 1])  # transposed heads
+    expect(lib, a, "KDA_ERR_LAYOUT")
+    a = good()
+    a["v"] = T([1, 64, 2, 128], data=FAKE + 2)
+    expect(lib, a, "KDA_ERR_LAYOUT")
+    a = good(beta_dtype=binding.KDA_BF16)
+    a["beta"] = T([1, 64, 2], binding.KDA_BF16, data=FAKE + 1)
+    expect(lib, a, "KDA_ERR_LAYOUT")
+
+
+def test_scale_value(lib):
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        expect(lib, good(), "KDA_ERR_VALUE", scale=s)
+
+
+def test_empty_problem_needs_no_launch(lib):
+    a = good(B=1, T_=0)
+    for key in ("q", "k", "v", "g", "beta", "out"):
+        a[key].data = None
+    expect(lib, a, "KDA_OK")
+    expect(lib, good(), "KDA_OK", cu=T([1], binding.KDA_I32))  # zero sequences
+
+
+def test_status_strings(lib):
+    for i, name in enumerate(binding.STATUS_NAMES):
+        assert lib.kda_status_string(i).decode().startswith(name)
+
+
+def test_dv_slices(lib):
+    assert lib.kda_dv_slices(2, 64) == 2
+    assert lib.kda_dv_slices(1, 64) == 4
+    assert lib.kda_dv_slices(14, 64) == 2
+
+
+def test_trace_requires_descriptor(lib):
+    a = good()
+    r = ctypes.byref
+    st = lib.kda_fwd_trace(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["beta"]), 0.1, None, None,
+                           r(a["out"]), None, None, None)
+    assert binding.STATUS_NAMES[st] == "KDA_ERR_NULL"

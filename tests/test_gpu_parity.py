@@ -1,0 +1,262 @@
+"""GPU parity of the HIP library (through the C ABI) against the fp64 CPU oracle.
+
+Each test prints the case it is about to launch before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_35_amd import kda_fwd, kda_fwd_trace, load_library
+from gated_delta_rule_35_amd.inputs import WORKLOADS, make_inputs, workload_inputs, cu_from_lengths
+from tests.kda_check import (O_MAX_ABS, O_REL_F, STATE_REL_F, head_subset, rel_frob_per_head, seq_slices,
+                             state_rel_frob, to_device)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 128 ** -0.5
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    load_library()  # fails loudly if the HIP library is not built
+    yield
+
+
+def run_gpu(x, cu=None, scale=SCALE, want_state=True):
+    d = to_device(x)
+    cu_d = cu.to("cuda") if cu is not None else None
+    o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                    final_state=True if want_state else None)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), (hT.cpu().numpy() if hT is not None else None)
+
+
+def check_against_oracle(x, cu=None, heads=None, Hq=None, Hv=None, scale=SCALE, label=""):
+    o, hT = run_gpu(x, cu, scale)
+    if heads is not None:
+        sub = head_subset(x, heads, Hq, Hv)
+        o = o[:, :, heads]
+        hT = hT[:, heads]
+    else:
+        sub = x
+    o_ref, h_ref = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale,
+                                     cu_seqlens=cu, h0=sub["h0"])
+    slices = seq_slices(cu) if cu is not None else None
+    if cu is not None:
+        covered = np.zeros(o.shape[1], bool)
+        for s in slices:
+            covered[s] = True
+        o, o_ref = o[:, covered], o_ref[:, covered]
+        slices = None if not covered.all() else slices
+    rel = rel_frob_per_head(o, o_ref, slices)
+    mx = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    srel = state_rel_frob(hT, h_ref)
+    _say(f"{label}: o relF={rel:.3e} maxabs={mx:.3e} state relF={srel:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    assert rel <= O_REL_F, rel
+    assert mx <= O_MAX_ABS, mx
+    assert srel <= STATE_REL_F, srel
+    return o, hT
+
+
+def test_tiny_mha_full_oracle():
+    w = WORKLOADS["tiny_b1_h2_t192"]
+    _say(f"{w.name}")
+    x, cu = workload_inputs(w)
+    check_against_oracle(x, cu, label=w.name)
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 127, 130, 200])
+def test_ragged_tails_with_initial_state(T):
+    _say(f"ragged tail B=2 H=3 T={T} with h0")
+    x = make_inputs(2, T, 3, 3, torch.float32, h0=True, seed=100 + T)
+    check_against_oracle(x, label=f"T={T}")
+
+
+def test_gva_small_full_oracle():
+    _say("GVA B=2 Hq=2 Hv=8 T=150")
+    x = make_inputs(2, 150, 2, 8, torch.bfloat16, h0=True, seed=5)
+    check_against_oracle(x, label="gva small")
+
+
+def test_packed_varlen_small_with_empty_sequences():
+    lens = [1, 63, 65, 0, 130, 64, 7]
+    cu = cu_from_lengths(lens)
+    _say(f"varlen lengths={lens}")
+    x = make_inputs(1, int(cu[-1]), 4, 4, torch.float32, h0=True, N=len(lens), seed=11)
+    o, hT = check_against_oracle(x, cu, label="varlen small")
+    assert np.array_equal(hT[3], x["h0"][3].numpy())  # empty sequence keeps its state
+
+
+def test_bf16_beta_and_many_heads_small():
+    _say("MHA B=1 H=160 T=96 bf16 beta (2 dv slices)")
+    x = make_inputs(1, 96, 160, 160, torch.bfloat16, h0=False, seed=12)
+    check_against_oracle(x, label="H=160")
+
+
+def test_strong_decay_takes_exact_path():
+    """Gates down to about -5 per step overflow any single-anchor factorisation of a
+    16-token block; the library must stay finite and accurate."""
+    _say("strong decay g ~ logsigmoid(2 N(0,1) - 2)")
+    x = make_inputs(1, 140, 2, 2, torch.float32, h0=True, seed=13, g_shift=-2.0, g_scale=2.0)
+    assert float(x["g"].min()) < -5.0
+    check_against_oracle(x, label="strong decay")
+
+
+def test_stage_intermediates_match_oracle_chunked_form():
+    """Stage-by-stage parity (gate cumsum, Aqk, Akk, T, W, U, v_new, chunk states)
+    against the oracle's chunked form on a small case with tails."""
+    _say("trace B=1 H=2 T=150")
+    x = make_inputs(1, 150, 2, 2, torch.float32, h0=True, seed=21)
+    d = to_device(x)
+    Tt, H = 150, 2
+    nchunks = 3
+    tr = {n: torch.zeros(shape, dtype=torch.float32, device="cuda") for n, shape in
+          dict(G=(Tt, H, 128), Aqk=(Tt, H, 64), Akk=(Tt, H, 64), T=(Tt, H, 64), W=(Tt, H, 128),
+               U=(Tt, H, 128), v_new=(Tt, H, 128), h=(nchunks, H, 128, 128)).items()}
+    kda_fwd_trace(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, tr, initial_state=d["h0"])
+    torch.cuda.synchronize()
+    _, _, im = oracle.chunked(x["q"], x["k"], x["v"], x["g"], x["beta"], SCALE, h0=x["h0"], chunk=64,
+                              intermediates=True)
+    bounds = dict(G=1e-5, Aqk=2e-3, Akk=2e-3, T=5e-3, W=5e-3, U=5e-3, v_new=1e-2, h=1e-2)
+    for name, bound in bounds.items():
+        got = tr[name].cpu().numpy()
+        ref = im["h_c" if name == "h" else name]
+        err = float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+        _say(f"  stage {name}: rel max err {err:.3e}")
+        assert err <= bound, (name, err)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    _say("determinism B=2 H=64 T=300 + varlen")
+    x = make_inputs(2, 300, 64, 64, torch.float32, h0=True, seed=31)
+    d = to_device(x)
+    outs = []
+    for _ in range(3):
+        o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+        outs.append((o.view(torch.int16).clone(), hT.view(torch.int32).clone()))
+    torch.cuda.synchronize()
+    for o, h in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(h, outs[0][1])
+
+
+def test_gva_equals_repeated_mha_bitwise():
+    _say("GVA vs repeated MHA, B=1 Hq=4 Hv=16 T=200")
+    x = make_inputs(1, 200, 4, 16, torch.bfloat16, h0=True, seed=41)
+    d = to_device(x)
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    qr = d["q"].repeat_interleave(4, dim=2).contiguous()
+    kr = d["k"].repeat_interleave(4, dim=2).contiguous()
+    o2, h2 = kda_fwd(qr, kr, d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
+
+
+def test_packed_equals_separate_calls_bitwise():
+    lens = [70, 1, 129, 64]
+    cu = cu_from_lengths(lens)
+    _say(f"packed vs separate, lengths={lens}, H=130 (same dv slicing in both)")
+    H = 130
+    x = make_inputs(1, int(cu[-1]), H, H, torch.float32, h0=True, N=len(lens), seed=51)
+    d = to_device(x)
+    o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(),
+                    initial_state=d["h0"], final_state=True)
+    for n, s in enumerate(seq_slices(cu)):
+        sl = {k: d[k][:, s].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        on, hn = kda_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], SCALE,
+                         initial_state=d["h0"][n:n + 1].contiguous(), final_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(on.view(torch.int16), o[:, s].view(torch.int16)), n
+        assert torch.equal(hn.view(torch.int32), hT[n:n + 1].view(torch.int32)), n
+
+
+def test_sequence_isolation_and_poisoned_outputs():
+    """Outputs prefilled with NaN are fully overwritten, and NaN-poisoning one
+    sequence's inputs leaves every other sequence bit-for-bit unchanged."""
+    lens = [65, 40, 100]
+    cu = cu_from_lengths(lens)
+    _say(f"isolation lengths={lens}")
+    x = make_inputs(1, int(cu[-1]), 2, 4, torch.float32, h0=True, N=3, seed=61)
+    d = to_device(x)
+    out = torch.full_like(d["v"], float("nan"))
+    hT = torch.full((3, 4, 128, 128), float("nan"), device="cuda")
+    kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(), initial_state=d["h0"],
+            out=out, final_state=hT)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(hT).all()
+    s1 = seq_slices(cu)[1]
+    d2 = {k: (v.clone() if v is not None else None) for k, v in d.items()}
+    for name in ("q", "k", "v", "g"):
+        d2[name][:, s1] = float("nan")
+    out2 = torch.empty_like(out)
+    hT2 = torch.empty_like(hT)
+    kda_fwd(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], SCALE, cu_seqlens=cu.cuda(),
+            initial_state=d2["h0"], out=out2, final_state=hT2)
+    torch.cuda.synchronize()
+    for n, s in enumerate(seq_slices(cu)):
+        if n == 1:
+            continue
+        assert torch.equal(out[:, s].view(torch.int16), out2[:, s].view(torch.int16)), n
+        assert torch.equal(hT[n].view(torch.int32), hT2[n].view(torch.int32)), n
+
+
+def test_initial_state_may_alias_final_state():
+    _say("aliased initial/final state B=2 H=2 T=100")
+    x = make_inputs(2, 100, 2, 2, torch.float32, h0=True, seed=71)
+    d = to_device(x)
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    state = d["h0"].clone()
+    o2, _ = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=state, final_state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), state.view(torch.int32))
+
+
+def test_two_streams_match_serial_runs():
+    _say("two streams, B=2 H=64 T=256")
+    xa = to_device(make_inputs(2, 256, 64, 64, torch.float32, h0=True, seed=81))
+    xb = to_device(make_inputs(2, 256, 64, 64, torch.bfloat16, h0=False, seed=82))
+    ra = kda_fwd(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"], final_state=True)
+    rb = kda_fwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            oa = kda_fwd(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"],
+                         final_state=True)
+        with torch.cuda.stream(sb):
+            ob = kda_fwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa[0].view(torch.int16), ra[0].view(torch.int16))
+        assert torch.equal(oa[1].view(torch.int32), ra[1].view(torch.int32))
+        assert torch.equal(ob[0].view(torch.int16), rb[0].view(torch.int16))
+        assert torch.equal(ob[1].view(torch.int32), rb[1].view(torch.int32))
+
+
+# ---- the named workloads at their full sizes, checked on sampled heads ----
+
+FULL = [
+    ("mha_b2_h64_t4096", [0, 17, 63]),
+    ("mha_b2_h64_t8192", [5, 40]),
+    ("gva_b1_hq16_hv64_t4096", [0, 3, 4, 62]),
+    ("varlen_h64_16k", [2, 33]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL)
+def test_full_size_workloads_on_sampled_heads(name, heads):
+    w = WORKLOADS[name]
+    _say(f"full workload {name}, oracle on heads {heads}")
+    x, cu = workload_inputs(w)
+    check_against_oracle(x, cu, heads=heads, Hq=w.Hq, Hv=w.Hv, scale=w.scale, label=name)
