@@ -52,6 +52,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int kda_oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static int check_sizes(int64_t N, int64_t Hq, int64_t Hv, int64_t dk, int64_t dv, const int64_t* cu) {
     if (N < 0 || Hq <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hq != 0 || !cu) return -1;

@@ -43,6 +43,8 @@ def load(path=None):
     lib.kda_oracle_chunked.restype = ctypes.c_int
     lib.kda_oracle_num_chunks.argtypes = [_ip, i64, i64]
     lib.kda_oracle_num_chunks.restype = i64
+    lib.kda_oracle_threads.argtypes = []
+    lib.kda_oracle_threads.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -81,6 +83,11 @@ def _prepare(q, k, v, g, beta, cu_seqlens, h0, alpha=None):
     if alpha is not None and alpha.shape != beta.shape:
         raise ValueError("alpha shape mismatch")
     return q, k, v, g, beta, alpha, h0, cu, (B, T, Hq, Hv, dk, dv, N)
+
+
+def threads():
+    """OpenMP threads the oracle runs on."""
+    return int(load().kda_oracle_threads())
 
 
 def num_chunks(cu, C):
