@@ -52,6 +52,7 @@ constexpr float GUARD_DECAY = 8.0f;
 constexpr int S136 = 136;    // fp16 rows of 128 (+8 pad)
 constexpr int S72 = 72;      // fp16 rows of 64 (+8 pad)
 constexpr int S68 = 68;      // fp32 rows of 64 (+4 pad)
+constexpr int TS = 20;       // fp32 columns of a 16x16 column-major block (+4 pad)
 
 template <int DV>
 struct Lds {
@@ -66,8 +67,11 @@ struct Lds {
     static constexpr int Aqk = A32 + 64 * S68 * 4;       // [64][72] fp16
     static constexpr int T16 = Aqk + 64 * S72 * 2;       // [64][72] fp16 T diag(beta)
     static constexpr int W = T16 + 64 * S72 * 2;         // [64][136] fp16, -W
-    static constexpr int Xs = W;                         // inversion scratch inside W's slot
-    static constexpr int Toff = Xs + 3 * 256 * 4;        // 6 off-diagonal T blocks, fp32
+    // fp32 inversion scratch inside W's slot, column-major 16x16 blocks (stride TS):
+    static constexpr int TtD = W;                        // 4 diagonal T blocks
+    static constexpr int Yt = TtD + 4 * 16 * TS * 4;     // 2 products A_IJ T_JJ
+    static constexpr int T1t = Yt + 2 * 16 * TS * 4;     // T_10, T_32
+    static constexpr int Xt = T1t + 2 * 16 * TS * 4;     // 4 blocks of the 32x32 step
     static constexpr int VnT = W + 64 * S136 * 2;        // [DV][72] fp16, v_new^T
     static constexpr int Qg = VnT + DV * S72 * 2;        // [64][136] fp16, scale q e^G
     static constexpr int KgT = Qg + 64 * S136 * 2;       // [128][72] fp16, (k e^G)^T
@@ -80,8 +84,9 @@ struct Lds {
     static constexpr int Blk = HT + DV * S136 * 2;       // 3 x [4][128] fp32: g_b, Q_b, tot
     static constexpr int Scal = Blk + 3 * 4 * 128 * 4;   // Eb[4], Khs[4], InvR[4], Lam[6], Gam[1] x 128
     static constexpr int Beta = Scal + 19 * 128 * 4;     // [64] fp32
-    static constexpr int BYTES = Beta + 64 * 4;
-    static_assert(Toff + 6 * 256 * 4 <= VnT, "inversion scratch overflows W slot");
+    static constexpr int Flag = Beta + 64 * 4;           // int: some chunk block decays past the guard
+    static constexpr int BYTES = Flag + 16;
+    static_assert(Xt + 4 * 16 * TS * 4 <= VnT, "inversion scratch overflows W slot");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -122,6 +127,25 @@ __device__ __forceinline__ float fexp(float x) { return __expf(x); }
 
 __device__ __forceinline__ half8 lds_h8(const char* smem, int byte_off) {
     return *reinterpret_cast<const half8*>(smem + byte_off);
+}
+
+// C += A B for 16x16 fp32 blocks on v_mfma_f32_16x16x4f32.  A is row-major (row
+// stride sa), B column-major (Bt[n][k], stride sb).  Instruction s takes the k
+// indices 4*(lane/16) + s, so every lane loads its four A and four B values with
+// one 16-byte read each.  C: lane holds rows 4*(lane/16) .. +3 of column lane%16.
+__device__ __forceinline__ f32x4 mm16(const float* A, int sa, const float* Bt, int sb, f32x4 c, int lane) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(A + (lane & 15) * sa + 4 * (lane >> 4));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(Bt + (lane & 15) * sb + 4 * (lane >> 4));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ void store_colmajor(float* Ct, f32x4 c, int lane) {
+    *reinterpret_cast<f32x4*>(Ct + (lane & 15) * TS + 4 * (lane >> 4)) = c;
+}
+__device__ __forceinline__ void store_rowmajor(float* C, int sc, f32x4 c, int lane) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) C[(4 * (lane >> 4) + e) * sc + (lane & 15)] = c[e];
 }
 
 // Index of an off-diagonal 16x16 block pair (I > J) in 0..5.
@@ -222,7 +246,60 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
     float* sLam = sInvR + 512;
     float* sGam = sLam + 768;
     float* sBeta = reinterpret_cast<float*>(smem + L::Beta);
+    int* sFlag = reinterpret_cast<int*>(smem + L::Flag);
     float* sA32 = reinterpret_cast<float*>(smem + L::A32);
+
+    // Prefetch registers: one chunk's inputs in the a1 thread layout (row = lane,
+    // channels 16*wave ..), loaded one chunk ahead of their use.
+    constexpr int VPT = (CH * DV / 8 + NTHREADS - 1) / NTHREADS;   // 16-byte pieces of v per thread
+    float pf_g[16];
+    uint32_t pf_q[8], pf_k[8];
+    uint4 pf_v[VPT];
+    float pf_b = 0.f;
+    auto prefetch = [&](int64_t cstart, int tid_, int lane_, int wave_) {
+        const int Ln = (int)((len - cstart) < CH ? (len - cstart) : CH);
+        const int64_t t0 = bos + cstart;
+        if (lane_ < Ln) {
+            const int64_t tok = t0 + lane_;
+            const float4* gp = reinterpret_cast<const float4*>(p.g + tok * v_tok + (int64_t)hv * DK + 16 * wave_);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 t4 = gp[i];
+                pf_g[4 * i] = t4.x; pf_g[4 * i + 1] = t4.y; pf_g[4 * i + 2] = t4.z; pf_g[4 * i + 3] = t4.w;
+            }
+            const uint4* qp = reinterpret_cast<const uint4*>(p.q + tok * qk_tok + (int64_t)hq * DK + 16 * wave_);
+            const uint4* kp = reinterpret_cast<const uint4*>(p.k + tok * qk_tok + (int64_t)hq * DK + 16 * wave_);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint4 a = qp[i], b = kp[i];
+                pf_q[4 * i] = a.x; pf_q[4 * i + 1] = a.y; pf_q[4 * i + 2] = a.z; pf_q[4 * i + 3] = a.w;
+                pf_k[4 * i] = b.x; pf_k[4 * i + 1] = b.y; pf_k[4 * i + 2] = b.z; pf_k[4 * i + 3] = b.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pf_g[i] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { pf_q[i] = 0; pf_k[i] = 0; }
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int it = tid_ + NTHREADS * u;
+            const int j = it / (DV / 8), c8 = it % (DV / 8);
+            pf_v[u] = make_uint4(0, 0, 0, 0);
+            if (it < CH * DV / 8 && j < Ln)
+                pf_v[u] = *reinterpret_cast<const uint4*>(p.v + (t0 + j) * v_tok + (int64_t)hv * DK + dv0 + 8 * c8);
+        }
+        if (tid_ < CH) {
+            float b = 0.f;
+            if (tid_ < Ln) {
+                const int64_t idx = (t0 + tid_) * p.Hv + hv;
+                b = p.beta_f32 ? reinterpret_cast<const float*>(p.beta)[idx]
+                               : bf2f(reinterpret_cast<const uint16_t*>(p.beta)[idx]);
+            }
+            pf_b = b;
+        }
+    };
+    if (len > 0) prefetch(0, tid, lane, wave);
 
     int64_t chunk_idx = 0;
     for (int64_t c0 = 0; c0 < len; c0 += CH, ++chunk_idx) {
@@ -251,37 +328,24 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             }
         }
 
-        // ================= a1: loads and gate cumsum =================
+        // ================= a1: gate cumsum (inputs were prefetched) =================
         // Thread layout for this phase: row r = lane (token within the chunk),
         // channel group cg = wave (channels 16cg .. 16cg+15).
         const int r = lane, cg = wave;
         const bool rvalid = r < Lc;
         float gv[16];
         uint32_t qw[8], kw[8];   // 16 bf16 values each, two per word
-        {
-            const int64_t tok = tok0 + r;
-            if (rvalid) {
-                const float4* gp = reinterpret_cast<const float4*>(p.g + tok * v_tok + (int64_t)hv * DK + 16 * cg);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float4 t4 = gp[i];
-                    gv[4 * i] = t4.x; gv[4 * i + 1] = t4.y; gv[4 * i + 2] = t4.z; gv[4 * i + 3] = t4.w;
-                }
-                const uint4* qp = reinterpret_cast<const uint4*>(p.q + tok * qk_tok + (int64_t)hq * DK + 16 * cg);
-                const uint4* kp = reinterpret_cast<const uint4*>(p.k + tok * qk_tok + (int64_t)hq * DK + 16 * cg);
+        for (int i = 0; i < 16; ++i) gv[i] = pf_g[i];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const uint4 a = qp[i], b = kp[i];
-                    qw[4 * i] = a.x; qw[4 * i + 1] = a.y; qw[4 * i + 2] = a.z; qw[4 * i + 3] = a.w;
-                    kw[4 * i] = b.x; kw[4 * i + 1] = b.y; kw[4 * i + 2] = b.z; kw[4 * i + 3] = b.w;
-                }
-            } else {
+        for (int i = 0; i < 8; ++i) { qw[i] = pf_q[i]; kw[i] = pf_k[i]; }
+        const float beta_r = pf_b;
+        uint4 vcur[VPT];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) gv[i] = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { qw[i] = 0; kw[i] = 0; }
-            }
-        }
+        for (int i = 0; i < VPT; ++i) vcur[i] = pf_v[i];
+        // Start the next chunk's loads now; they land while this chunk computes.
+        if (c0 + CH < len) prefetch(c0 + CH, tid, lane, wave);
+
         auto qf = [&](int ch) { return __uint_as_float((ch & 1) ? (qw[ch >> 1] & 0xffff0000u) : (qw[ch >> 1] << 16)); };
         auto kf = [&](int ch) { return __uint_as_float((ch & 1) ? (kw[ch >> 1] & 0xffff0000u) : (kw[ch >> 1] << 16)); };
         // Within each 16-row block: P_r = sum_{b < r' <= r} g (so exp(P) = e^{G_r - G_b}),
@@ -311,38 +375,38 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         if (first_row) {
             const int I = r >> 4;
 #pragma unroll
-            for (int ch = 0; ch < 16; ++ch) {
-                const int c = 16 * cg + ch;
-                sBlkGb[I * 128 + c] = gv[ch];
-                sBlkQb[I * 128 + c] = qb_first[ch];
-                sBlkTot[I * 128 + c] = gv[ch] + qb_first[ch];
-            }
-        }
-        if (tid < CH) {
-            float b = 0.f;
-            if (tid < Lc) {
-                const int64_t idx = (tok0 + tid) * p.Hv + hv;
-                b = p.beta_f32 ? reinterpret_cast<const float*>(p.beta)[idx]
-                               : bf2f(reinterpret_cast<const uint16_t*>(p.beta)[idx]);
-            }
-            sBeta[tid] = b;
-        }
-        // v tile (64 tokens x DV channels of this slice), stored transposed as fp16.
-        for (int it = tid; it < CH * DV / 8; it += NTHREADS) {
-            const int j = it / (DV / 8), c8 = it % (DV / 8);
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (j < Lc) w = *reinterpret_cast<const uint4*>(p.v + (tok0 + j) * v_tok + (int64_t)hv * DK + dv0 + 8 * c8);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            for (int c4 = 0; c4 < 4; ++c4) {
+                f32x4 a, b, t;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t bits = (uint16_t)((ww[e >> 1] >> (16 * (e & 1))) & 0xffff);
-                reinterpret_cast<_Float16*>(smem + L::Vt)[(8 * c8 + e) * S72 + j] = (_Float16)bf2f(bits);
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = gv[4 * c4 + e];
+                    b[e] = qb_first[4 * c4 + e];
+                    t[e] = a[e] + b[e];
+                }
+                *reinterpret_cast<f32x4*>(sBlkGb + I * 128 + 16 * cg + 4 * c4) = a;
+                *reinterpret_cast<f32x4*>(sBlkQb + I * 128 + 16 * cg + 4 * c4) = b;
+                *reinterpret_cast<f32x4*>(sBlkTot + I * 128 + 16 * cg + 4 * c4) = t;
+            }
+        }
+        if (tid < CH) sBeta[tid] = beta_r;
+        if (tid == 0) *sFlag = 0;
+        // v tile (64 tokens x DV channels of this slice), stored transposed as fp16.
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int it = tid + NTHREADS * u;
+            if (it < CH * DV / 8) {
+                const int j = it / (DV / 8), c8 = it % (DV / 8);
+                const uint32_t ww[4] = {vcur[u].x, vcur[u].y, vcur[u].z, vcur[u].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t bits = (uint16_t)((ww[e >> 1] >> (16 * (e & 1))) & 0xffff);
+                    reinterpret_cast<_Float16*>(smem + L::Vt)[(8 * c8 + e) * S72 + j] = (_Float16)bf2f(bits);
+                }
             }
         }
         __syncthreads();
 
         // Per (block I, channel c) factors.  Thread layout: I = tid / 128, c = tid % 128.
-        int guard;
         {
             const int I = tid >> 7, c = tid & 127;
             float tot[4];
@@ -362,21 +426,28 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 acc += tot[J];
             }
             if (I == 0) sGam[c] = fexp(((tot[0] + tot[1]) + tot[2]) + tot[3]);
-            guard = (-qb > GUARD_DECAY) ? 1 : 0;
+            if (-qb > GUARD_DECAY) *sFlag = 1;
         }
-        guard = __syncthreads_or(guard);
+        __syncthreads();
+        const bool guard = *sFlag != 0;   // block-uniform
 
-        // exp factors and intra operands (thread layout: row r, channel group cg).
+        // Intra operands (thread layout: row r, channel group cg).  All LDS reads first.
         {
             const int I = r >> 4;
+            float invR[16];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(sInvR + I * 128 + 16 * cg + 4 * c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) invR[4 * c4 + e] = t[e];
+            }
             half8 aq[2], ak[2], bd[2];
 #pragma unroll
             for (int ch = 0; ch < 16; ++ch) {
-                const int c = 16 * cg + ch;
                 const float qx = qf(ch), kx = kf(ch);
                 aq[ch >> 3][ch & 7] = (_Float16)(qx * Fv[ch]);
                 ak[ch >> 3][ch & 7] = (_Float16)(kx * Fv[ch]);
-                bd[ch >> 3][ch & 7] = (_Float16)(kx * Rv[ch] * sInvR[I * 128 + c]);
+                bd[ch >> 3][ch & 7] = (_Float16)(kx * Rv[ch] * invR[ch]);
             }
             const int off = (r * S136 + 16 * cg) * 2;
             *reinterpret_cast<half8*>(smem + L::Aq + off) = aq[0];
@@ -387,12 +458,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             *reinterpret_cast<half8*>(smem + L::Bd + off + 16) = bd[1];
             for (int I2 = I + 1; I2 < 4; ++I2) {
                 const int pi = pair_index(I2, I);
+                float lam[16];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4*>(sLam + pi * 128 + 16 * cg + 4 * c4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lam[4 * c4 + e] = t[e];
+                }
                 half8 bo[2];
 #pragma unroll
-                for (int ch = 0; ch < 16; ++ch) {
-                    const int c = 16 * cg + ch;
-                    bo[ch >> 3][ch & 7] = (_Float16)(kf(ch) * Rv[ch] * sLam[pi * 128 + c]);
-                }
+                for (int ch = 0; ch < 16; ++ch) bo[ch >> 3][ch & 7] = (_Float16)(kf(ch) * Rv[ch] * lam[ch]);
                 const int o2 = ((16 * pi + (r & 15)) * S136 + 16 * cg) * 2;
                 *reinterpret_cast<half8*>(smem + L::Bo + o2) = bo[0];
                 *reinterpret_cast<half8*>(smem + L::Bo + o2 + 16) = bo[1];
@@ -441,6 +516,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 iacc[u] = acc;
             }
         }
+        // LDS reads for the derived operands below, issued before the barrier.
+        float ebv[16], khs[16];
+        {
+            const int I = r >> 4;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(sEb + I * 128 + 16 * cg + 4 * c4);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(sKhs + I * 128 + 16 * cg + 4 * c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { ebv[4 * c4 + e] = a[e]; khs[4 * c4 + e] = b[e]; }
+            }
+        }
         __syncthreads();
         // Store the lower tiles (masked, scaled), zero the upper ones.
 #pragma unroll
@@ -468,12 +555,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 }
             }
         }
-        for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
-            const int i = idx >> 6, j = idx & 63;
-            if ((j >> 4) > (i >> 4)) {
-                sA32[i * S68 + j] = 0.f;
-                reinterpret_cast<_Float16*>(smem + L::Aqk)[i * S72 + j] = (_Float16)0.f;
-                if (TRACE && p.tr_Aqk && s == 0 && i < Lc) p.tr_Aqk[((tok0 + i) * p.Hv + hv) * CH + j] = 0.f;
+        {
+            // Upper 16x16 tiles (I < J) of Akk (fp32) and Aqk (fp16) are zero.
+            const int tile = tid >> 6, w64 = tid & 63;   // 8 slots, 6 used
+            if (tile < 6) {
+                const int I = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+                const int J = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+                const int m = w64 >> 2, q4 = w64 & 3;
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f32x4*>(smem + L::A32 + ((16 * I + m) * S68 + 16 * J + 4 * q4) * 4) = z4;
+                half4 hz = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+                *reinterpret_cast<half4*>(smem + L::Aqk + ((16 * I + m) * S72 + 16 * J + 4 * q4) * 2) = hz;
+                if (TRACE && p.tr_Aqk && s == 0 && 16 * I + m < Lc) {
+                    float* dst = p.tr_Aqk + ((tok0 + 16 * I + m) * p.Hv + hv) * CH + 16 * J + 4 * q4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[e] = 0.f;
+                }
             }
         }
         if (guard) {
@@ -504,16 +601,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         }
         // Derived operands for W, the output and the state update (row r, channels 16cg..).
         {
-            const int I = r >> 4;
             half8 qg[2];
 #pragma unroll
             for (int ch = 0; ch < 16; ++ch) {
                 const int c = 16 * cg + ch;
-                const float eb = sEb[I * 128 + c];
                 const float kx = kf(ch);
-                qg[ch >> 3][ch & 7] = (_Float16)(p.scale * qf(ch) * Fv[ch] * eb);
-                reinterpret_cast<_Float16*>(smem + L::KgT)[c * S72 + r] = (_Float16)(kx * Fv[ch] * eb);
-                reinterpret_cast<_Float16*>(smem + L::KhT)[c * S72 + r] = (_Float16)(kx * Rv[ch] * sKhs[I * 128 + c]);
+                qg[ch >> 3][ch & 7] = (_Float16)(p.scale * qf(ch) * Fv[ch] * ebv[ch]);
+                reinterpret_cast<_Float16*>(smem + L::KgT)[c * S72 + r] = (_Float16)(kx * Fv[ch] * ebv[ch]);
+                reinterpret_cast<_Float16*>(smem + L::KhT)[c * S72 + r] = (_Float16)(kx * Rv[ch] * khs[ch]);
             }
             const int off = (r * S136 + 16 * cg) * 2;
             *reinterpret_cast<half8*>(smem + L::Qg + off) = qg[0];
@@ -529,6 +624,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
 
         // ================= a3: T = (I + Akk)^{-1} in fp32 =================
         // Diagonal 16x16 blocks: wave 0, lane = (block, column); forward substitution.
+        // Results go back row-major into the diagonal blocks of A32 and column-major
+        // into the TtD scratch (the B-operand layout of the fp32 MFMA products below).
+        float* sTtD = reinterpret_cast<float*>(smem + L::TtD);
+        float* sYt = reinterpret_cast<float*>(smem + L::Yt);
+        float* sT1t = reinterpret_cast<float*>(smem + L::T1t);
+        float* sXt = reinterpret_cast<float*>(smem + L::Xt);
         if (wave == 0) {
             const int B = lane >> 4, j = lane & 15;
             float x[16];
@@ -540,56 +641,81 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 for (int i = kk + 1; i < 16; ++i) x[i] -= sA32[(16 * B + i) * S68 + 16 * B + kk] * x[kk];
             }
             // Diagonal blocks are read only by this wave; write back after all reads.
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
             for (int i = 0; i < 16; ++i) sA32[(16 * B + i) * S68 + 16 * B + j] = x[i];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                f32x4 v4 = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+                *reinterpret_cast<f32x4*>(sTtD + (B * 16 + j) * TS + 4 * i4) = v4;
+            }
         }
         __syncthreads();
-        // Off-diagonal blocks by distance d: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ.
-        {
-            float* sX = reinterpret_cast<float*>(smem + L::Xs);
-            float* sToff = reinterpret_cast<float*>(smem + L::Toff);
-            for (int dd = 1; dd < 4; ++dd) {
-                const int nb = 4 - dd;
-                const int J = wave, I = wave + dd;
-                const int nn = lane & 15, m0 = 4 * (lane >> 4);
-                if (wave < nb) {
-                    float xacc[4] = {0.f, 0.f, 0.f, 0.f};
-                    for (int K = J; K < I; ++K) {
-                        for (int kk = 0; kk < 16; ++kk) {
-                            const float tkj = (K == J) ? sA32[(16 * K + kk) * S68 + 16 * J + nn]
-                                                       : sToff[pair_index(K, J) * 256 + kk * 16 + nn];
+        // Off-diagonal blocks on fp32 MFMA (16x16x4): T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
+        // by doubling: first (1,0) and (3,2), then the lower-left 32x32 block.
+        // mm16 multiplies a row-major A block by a column-major B block.
+        if (wave < 2) {
+            // wave 0: pair (1,0); wave 1: pair (3,2)
+            const int I = wave == 0 ? 1 : 3, J = I - 1;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            y = mm16(sA32 + (16 * I) * S68 + 16 * J, S68, sTtD + J * 16 * TS, TS, y, lane);
+            store_colmajor(sYt + wave * 16 * TS, y, lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            t = mm16(sA32 + (16 * I) * S68 + 16 * I, S68, sYt + wave * 16 * TS, TS, t, lane);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                xacc[e] += sA32[(16 * I + m0 + e) * S68 + 16 * K + kk] * tkj;
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sX[wave * 256 + (m0 + e) * 16 + nn] = xacc[e];
-                }
-                __syncthreads();
-                if (wave < nb) {
-                    float tacc[4] = {0.f, 0.f, 0.f, 0.f};
-                    for (int kk = 0; kk < 16; ++kk) {
-                        const float xv = sX[wave * 256 + kk * 16 + nn];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) tacc[e] += sA32[(16 * I + m0 + e) * S68 + 16 * I + kk] * xv;
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sToff[pair_index(I, J) * 256 + (m0 + e) * 16 + nn] = -tacc[e];
-                }
-                __syncthreads();
+            for (int e = 0; e < 4; ++e) t[e] = -t[e];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            store_rowmajor(sA32 + (16 * I) * S68 + 16 * J, S68, t, lane);   // replaces A_IJ, no longer read
+            store_colmajor(sT1t + wave * 16 * TS, t, lane);
+        }
+        __syncthreads();
+        if (wave < 4) {
+            // X_IJ = sum_{K=J}^{1} A_IK T_KJ for I in {2,3}, J in {0,1}; wave = 2 (I-2) + J
+            const int I = 2 + (wave >> 1), J = wave & 1;
+            f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
+            if (J == 0) {
+                x4 = mm16(sA32 + (16 * I) * S68 + 0, S68, sTtD + 0 * 16 * TS, TS, x4, lane);      // A_I0 T_00
+                x4 = mm16(sA32 + (16 * I) * S68 + 16, S68, sT1t + 0 * 16 * TS, TS, x4, lane);     // A_I1 T_10
+            } else {
+                x4 = mm16(sA32 + (16 * I) * S68 + 16, S68, sTtD + 1 * 16 * TS, TS, x4, lane);     // A_I1 T_11
             }
-            // T diag(beta) as fp16 MFMA operand.
-            for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
-                const int i = idx >> 6, j = idx & 63;
-                const int I = i >> 4, J = j >> 4;
-                float t = 0.f;
-                if (I == J) t = sA32[i * S68 + j];
-                else if (I > J) t = sToff[pair_index(I, J) * 256 + (i & 15) * 16 + (j & 15)];
-                reinterpret_cast<_Float16*>(smem + L::T16)[i * S72 + j] = (_Float16)(t * sBeta[j]);
-                if (TRACE && p.tr_T && s == 0 && i < Lc) p.tr_T[((tok0 + i) * p.Hv + hv) * CH + j] = t;
+            store_colmajor(sXt + wave * 16 * TS, x4, lane);
+        }
+        __syncthreads();
+        if (wave < 4) {
+            // T_2J = -T_22 X_2J ; T_3J = -(T_32 X_2J + T_33 X_3J)
+            const int I = 2 + (wave >> 1), J = wave & 1;
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            if (I == 2) {
+                t = mm16(sA32 + 32 * S68 + 32, S68, sXt + J * 16 * TS, TS, t, lane);
+            } else {
+                t = mm16(sA32 + 48 * S68 + 32, S68, sXt + J * 16 * TS, TS, t, lane);
+                t = mm16(sA32 + 48 * S68 + 48, S68, sXt + (2 + J) * 16 * TS, TS, t, lane);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = -t[e];
+            store_rowmajor(sA32 + (16 * I) * S68 + 16 * J, S68, t, lane);     // A_IJ is no longer read
+        }
+        __syncthreads();
+        // T diag(beta) as the fp16 MFMA operand; row i, columns 8*(tid%8) ...
+        {
+            const int i = tid >> 3, j0 = 8 * (tid & 7);
+            const f32x4 t0 = *reinterpret_cast<const f32x4*>(sA32 + i * S68 + j0);
+            const f32x4 t1 = *reinterpret_cast<const f32x4*>(sA32 + i * S68 + j0 + 4);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + j0);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + j0 + 4);
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[e] = (_Float16)(t0[e] * b0[e]);
+                h[4 + e] = (_Float16)(t1[e] * b1[e]);
+            }
+            *reinterpret_cast<half8*>(smem + L::T16 + (i * S72 + j0) * 2) = h;
+            if (TRACE && p.tr_T && s == 0 && i < Lc) {
+                float* dst = p.tr_T + ((tok0 + i) * p.Hv + hv) * CH + j0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { dst[e] = t0[e]; dst[4 + e] = t1[e]; }
             }
         }
         __syncthreads();
