@@ -91,7 +91,8 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (h0 && !same_shape(h0, ss, 4)) return KDA_ERR_SHAPE;
     if (hT && !same_shape(hT, ss, 4)) return KDA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
-    if (Hv > (int64_t(1) << 20) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
+    // Per-block byte offsets of the kernel's buffer loads are 32-bit.
+    if (Hv > (int64_t(1) << 16) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
     const int S = kda_dv_slices(N, Hv);
     if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
 

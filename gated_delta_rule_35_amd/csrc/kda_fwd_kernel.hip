@@ -10,7 +10,8 @@
 //   a1  gate cumsum         G = chunk-local inclusive cumsum of g (fp32)
 //   a2  intra               Aqk = scale (q e^{G_i - G_j} k^T), j <= i
 //                           Akk = beta_i (k e^{G_i - G_j} k^T), j < i      (MFMA)
-//   a3  FP32 inversion      T = (I + Akk)^{-1}, blocked forward substitution
+//   a3  FP32 inversion      T = (I + Akk)^{-1}: diagonal 16x16 blocks by forward
+//                           substitution, the rest on fp32 MFMA
 //   a4  W/U recompute       W = T (beta k e^G), U = T (beta v)             (MFMA)
 //   a5  delta-H scan        v_new = U - W h;
 //                           h <- Diag(e^{G_last}) h + (k e^{G_last - G})^T v_new
@@ -18,6 +19,8 @@
 //
 // The state slice h (128 x DV, fp32) lives in MFMA accumulator registers for
 // the whole sequence; HBM sees q, k, v, g, beta once and o once, plus the states.
+// The next chunk's inputs are loaded into registers while the current chunk
+// computes.
 //
 // MFMA operands are fp16 (bf16 inputs convert exactly when in range; the
 // rounding of derived operands to fp16 keeps the result within tolerance where
@@ -40,6 +43,8 @@ namespace kda {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -56,77 +61,72 @@ constexpr int TS = 20;       // fp32 columns of a 16x16 column-major block (+4 p
 
 template <int DV>
 struct Lds {
-    // Region R1, phase A view (intra operands, fp16):
-    static constexpr int Aq = 0;                         // [64][136] q * F
-    static constexpr int Ak = Aq + 64 * S136 * 2;        // [64][136] k * F
-    static constexpr int Bd = Ak + 64 * S136 * 2;        // [64][136] k * e^{G_b - G_j}
-    static constexpr int Bo = Bd + 64 * S136 * 2;        // [96][136] k * e^{G_{b_I} - G_j}, 6 pairs
-    static constexpr int R1_A_END = Bo + 96 * S136 * 2;
-    // Region R1, phase B view:
+    // Region R1, prep view (written before the intra MFMAs):
+    static constexpr int Aq = 0;                         // [64][136] q * F         (intra, rows i)
+    static constexpr int Ak = Aq + 64 * S136 * 2;        // [64][136] k * F         (intra, rows i)
+    static constexpr int Bd = Ak + 64 * S136 * 2;        // [64][136] k * e^{G_b - G_j} (diagonal, rows j)
+    static constexpr int Bo = Bd + 64 * S136 * 2;        // [96][136] k * e^{G_{b_I} - G_j}, 6 block pairs
+    static constexpr int PREP_END = Bo + 96 * S136 * 2;
+    // Region R1, later view (overlaps Aq..Bo once the intra MFMAs are done):
     static constexpr int A32 = 0;                        // [64][68] fp32 Akk, then T
     static constexpr int Aqk = A32 + 64 * S68 * 4;       // [64][72] fp16
     static constexpr int T16 = Aqk + 64 * S72 * 2;       // [64][72] fp16 T diag(beta)
     static constexpr int W = T16 + 64 * S72 * 2;         // [64][136] fp16, -W
     // fp32 inversion scratch inside W's slot, column-major 16x16 blocks (stride TS):
     static constexpr int TtD = W;                        // 4 diagonal T blocks
-    static constexpr int Yt = TtD + 4 * 16 * TS * 4;     // 2 products A_IJ T_JJ
-    static constexpr int T1t = Yt + 2 * 16 * TS * 4;     // T_10, T_32
+    static constexpr int T1t = TtD + 4 * 16 * TS * 4;    // T_10, T_32 (and their A T products)
     static constexpr int Xt = T1t + 2 * 16 * TS * 4;     // 4 blocks of the 32x32 step
     static constexpr int VnT = W + 64 * S136 * 2;        // [DV][72] fp16, v_new^T
     static constexpr int Qg = VnT + DV * S72 * 2;        // [64][136] fp16, scale q e^G
-    static constexpr int KgT = Qg + 64 * S136 * 2;       // [128][72] fp16, (k e^G)^T
-    static constexpr int KhT = KgT + 128 * S72 * 2;      // [128][72] fp16, (k e^{G_last-G})^T
-    static constexpr int R1_B_END = KhT + 128 * S72 * 2;
-    static constexpr int R1_END = R1_A_END > R1_B_END ? R1_A_END : R1_B_END;
-    // Persistent / small regions.
-    static constexpr int Vt = R1_END;                    // [DV][72] fp16, v^T
+    static constexpr int LATE_END = Qg + 64 * S136 * 2;
+    // Transposed operands, written with the prep view and live until the state update:
+    static constexpr int KgT = (PREP_END > LATE_END ? PREP_END : LATE_END);  // [128][72] (k e^G)^T
+    static constexpr int KhT = KgT + 128 * S72 * 2;      // [128][72] fp16, (k e^{G_last - G})^T
+    static constexpr int Vt = KhT + 128 * S72 * 2;       // [DV][72] fp16, v^T
     static constexpr int HT = Vt + DV * S72 * 2;         // [DV][136] fp16, h^T
-    static constexpr int Blk = HT + DV * S136 * 2;       // 3 x [4][128] fp32: g_b, Q_b, tot
-    static constexpr int Scal = Blk + 3 * 4 * 128 * 4;   // Eb[4], Khs[4], InvR[4], Lam[6], Gam[1] x 128
-    static constexpr int Beta = Scal + 19 * 128 * 4;     // [64] fp32
-    static constexpr int Flag = Beta + 64 * 4;           // int: some chunk block decays past the guard
-    static constexpr int BYTES = Flag + 16;
+    static constexpr int Xch = HT + DV * S136 * 2;       // 3 x [4][128] fp32 half-block sums
+    static constexpr int Gam = Xch + 3 * 4 * 128 * 4;    // [128] fp32 e^{G_last}
+    static constexpr int Beta = Gam + 128 * 4;           // [64] fp32
+    static constexpr int Flag = Beta + 64 * 4;           // int: some block decays past the guard
+    static constexpr int Ost = Flag + 16;                // [64][DV+8] bf16 output of the previous chunk
+    static constexpr int BYTES = Ost + 64 * (DV + 8) * 2;
     static_assert(Xt + 4 * 16 * TS * 4 <= VnT, "inversion scratch overflows W slot");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Row (16-lane) shifts through DPP; lanes whose source lies outside the row read 0.
-__device__ __forceinline__ float row_shr(float x, int n) {
-    int v = __float_as_int(x);
-    int r;
-    switch (n) {
-        case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true); break;
-        case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true); break;
-        case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true); break;
-        default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true); break;
-    }
-    return __int_as_float(r);
-}
-__device__ __forceinline__ float row_shl(float x, int n) {
-    int v = __float_as_int(x);
-    int r;
-    switch (n) {
-        case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x101, 0xf, 0xf, true); break;
-        case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x102, 0xf, 0xf, true); break;
-        case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, true); break;
-        default: r = __builtin_amdgcn_update_dpp(0, v, 0x108, 0xf, 0xf, true); break;
-    }
-    return __int_as_float(r);
-}
 
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
+// 2^x on the hardware exp2 (v_exp_f32); arguments here are sums of g log2(e) <= 0.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ half8 lds_h8(const char* smem, int byte_off) {
     return *reinterpret_cast<const half8*>(smem + byte_off);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): stride 0, 32-bit dwords
+// (word 3 = 0x00020000 for gfx9-family raw buffers).  Loads past `bytes` read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Two fp32 values as one 32-bit word of two bf16 (v_cvt_pk_bf16_f32, round to
+// nearest even under the default rounding mode).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2v));
+}
+
+// Two fp32 values as one 32-bit word of two fp16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    half2v h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // C += A B for 16x16 fp32 blocks on v_mfma_f32_16x16x4f32.  A is row-major (row
@@ -136,9 +136,12 @@ __device__ __forceinline__ half8 lds_h8(const char* smem, int byte_off) {
 __device__ __forceinline__ f32x4 mm16(const float* A, int sa, const float* Bt, int sb, f32x4 c, int lane) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(A + (lane & 15) * sa + 4 * (lane >> 4));
     const f32x4 b = *reinterpret_cast<const f32x4*>(Bt + (lane & 15) * sb + 4 * (lane >> 4));
-#pragma unroll
-    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
-    return c;
+    f32x4 c1 = {0.f, 0.f, 0.f, 0.f};   // second accumulation chain: half the dependent latency
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c1, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c1, 0, 0, 0);
+    return c + c1;
 }
 __device__ __forceinline__ void store_colmajor(float* Ct, f32x4 c, int lane) {
     *reinterpret_cast<f32x4*>(Ct + (lane & 15) * TS + 4 * (lane >> 4)) = c;
@@ -146,6 +149,58 @@ __device__ __forceinline__ void store_colmajor(float* Ct, f32x4 c, int lane) {
 __device__ __forceinline__ void store_rowmajor(float* C, int sc, f32x4 c, int lane) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) C[(4 * (lane >> 4) + e) * sc + (lane & 15)] = c[e];
+}
+// Block (I, J) of T, in the C layout of mm16, scaled by beta of its columns into
+// the fp16 operand T16 (row stride 72).
+__device__ __forceinline__ void store_t16(_Float16* T16, f32x4 t, int I, int J, const float* beta, int lane) {
+    const int j = 16 * J + (lane & 15);
+    const float bj = beta[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T16[(16 * I + 4 * (lane >> 4) + e) * 72 + j] = (_Float16)(t[e] * bj);
+}
+// Trace dump of block (I, J) of T (rows past the chunk's length are skipped).
+__device__ __forceinline__ void trace_tblock(float* dst, int64_t tok0, int Lc, int Hv, int hv, f32x4 t, int I, int J,
+                                             int lane) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = 16 * I + 4 * (lane >> 4) + e;
+        if (i < Lc) dst[((tok0 + i) * Hv + hv) * 64 + 16 * J + (lane & 15)] = t[e];
+    }
+}
+
+// Work-group barrier for LDS hand-offs only.  The waves of a work-group share
+// data through LDS alone (global memory is only read, or written once per
+// element), so the barrier waits for this wave's LDS operations and not for its
+// outstanding global loads: the prefetch of the next chunk stays in flight
+// across barriers.  The asm is also a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Per-(block, channel) exponents, in log2 units, for the column block IB given
+// the four block sums tot: off = sum_{K < IB} tot_K (ascending), tail =
+// sum_{K > IB} tot_K (descending), lamarg[d] = sum_{IB < K < I2} tot_K + g_{b_I2}
+// for I2 = IB + 1 + d (0 where I2 > 3).
+template <int IB>
+__device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2 (&gI)[4], f32x2& off, f32x2& tail,
+                                              f32x2 (&lamarg)[3]) {
+    off = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < IB; ++K) off += tot[K];
+    tail = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int K = 3; K > IB; --K) tail += tot[K];
+    f32x2 acc = {0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int I2 = IB + 1 + d;
+        if (I2 < 4) {
+            lamarg[d] = acc + gI[I2 < 4 ? I2 : 3];
+            acc += tot[I2 < 4 ? I2 : 3];
+        } else {
+            lamarg[d] = f32x2{-1000.f, -1000.f};   // unused; exp2 gives 0
+        }
+    }
 }
 
 // Index of an off-diagonal 16x16 block pair (I > J) in 0..5.
@@ -158,6 +213,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
     constexpr int NU = 2 * (DV / 32);   // 32x32 tiles of a 64 x DV matrix
     constexpr int NH = 4 * (DV / 32);   // 32x32 tiles of the 128 x DV state
     constexpr int HPW = (NH + 7) / 8;   // state tiles per wave
+    constexpr int VPT = (CH * DV / 8 + NTHREADS - 1) / NTHREADS;   // 16-byte pieces of v per thread
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
     const int tid_o = threadIdx.x;
@@ -237,66 +293,99 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         }
     }
 
-    float* sBlkGb = reinterpret_cast<float*>(smem + L::Blk);
-    float* sBlkQb = sBlkGb + 512;
-    float* sBlkTot = sBlkQb + 512;
-    float* sEb = reinterpret_cast<float*>(smem + L::Scal);
-    float* sKhs = sEb + 512;
-    float* sInvR = sKhs + 512;
-    float* sLam = sInvR + 512;
-    float* sGam = sLam + 768;
+    float* sXa = reinterpret_cast<float*>(smem + L::Xch);   // [4][128] sum of rows b+1..b+7
+    float* sXb = sXa + 512;                                  // [4][128] sum of rows b+8..b+15
+    float* sXg = sXb + 512;                                  // [4][128] g at row b
+    float* sGam = reinterpret_cast<float*>(smem + L::Gam);
     float* sBeta = reinterpret_cast<float*>(smem + L::Beta);
     int* sFlag = reinterpret_cast<int*>(smem + L::Flag);
     float* sA32 = reinterpret_cast<float*>(smem + L::A32);
 
-    // Prefetch registers: one chunk's inputs in the a1 thread layout (row = lane,
-    // channels 16*wave ..), loaded one chunk ahead of their use.
-    constexpr int VPT = (CH * DV / 8 + NTHREADS - 1) / NTHREADS;   // 16-byte pieces of v per thread
-    float pf_g[16];
+    // Prefetch registers: one chunk's inputs in the prep layout (lane = channel
+    // pair, wave = 8-row half block), loaded one chunk ahead of their use.  Every
+    // load instruction of a wave reads one contiguous row segment (q, k: 256 B;
+    // g: 512 B).
+    float pf_g[8][2];
     uint32_t pf_q[8], pf_k[8];
     uint4 pf_v[VPT];
-    float pf_b = 0.f;
-    auto prefetch = [&](int64_t cstart, int tid_, int lane_, int wave_) {
+    uint32_t pf_b = 0;   // raw beta bits; converted when used
+    // Loads use raw buffer instructions: a wave-uniform 128-bit descriptor per
+    // row block (scalar base and byte range) and 32-bit per-lane offsets.  Rows
+    // past the sequence end fall outside the descriptor's range, and the hardware
+    // returns zeros for them.
+    // The next chunk's loads are split into groups issued at several points of
+    // the current chunk, each right after the last use of the registers it
+    // refills, so that the CU's load path works in the background instead of
+    // stalling every wave at one point.
+    auto pf_rows = [&](int64_t cstart, int wave_) {
+        const int Ln = (int)((len - cstart) < CH ? (len - cstart) : CH);
+        const int row0 = 8 * wave_;
+        return Ln - row0 < 0 ? 0 : (Ln - row0 > 8 ? 8 : Ln - row0);
+    };
+    auto prefetch_g = [&](int64_t cstart, int lane_, int wave_, int r0, int r1) {
+        const int64_t t0 = bos + cstart;
+        const int nrows = pf_rows(cstart, wave_);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + (t0 + 8 * wave_) * v_tok + (int64_t)hv * DK,
+                                                    nrows ? ((nrows - 1) * v_tok + DK) * 4 : 0);
+#pragma unroll
+        for (int rr = r0; rr < r1; ++rr) {
+            // The whole offset goes in the VGPR operand: only that part is range-checked.
+            const i32x2 g2 = __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * lane_ + (int)(rr * v_tok * 4), 0, 0);
+            pf_g[rr][0] = __int_as_float(g2[0]);
+            pf_g[rr][1] = __int_as_float(g2[1]);
+        }
+    };
+    auto prefetch_qk = [&](int64_t cstart, int lane_, int wave_, int r0, int r1) {
+        const int64_t t0 = bos + cstart;
+        const int nrows = pf_rows(cstart, wave_);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (t0 + 8 * wave_) * qk_tok + (int64_t)hq * DK,
+                                                    nrows ? ((nrows - 1) * qk_tok + DK) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (t0 + 8 * wave_) * qk_tok + (int64_t)hq * DK,
+                                                    nrows ? ((nrows - 1) * qk_tok + DK) * 2 : 0);
+#pragma unroll
+        for (int rr = r0; rr < r1; ++rr) {
+            pf_q[rr] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane_ + (int)(rr * qk_tok * 2), 0, 0);
+            pf_k[rr] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane_ + (int)(rr * qk_tok * 2), 0, 0);
+        }
+    };
+    auto prefetch_vb = [&](int64_t cstart, int tid_) {
         const int Ln = (int)((len - cstart) < CH ? (len - cstart) : CH);
         const int64_t t0 = bos + cstart;
-        if (lane_ < Ln) {
-            const int64_t tok = t0 + lane_;
-            const float4* gp = reinterpret_cast<const float4*>(p.g + tok * v_tok + (int64_t)hv * DK + 16 * wave_);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 t4 = gp[i];
-                pf_g[4 * i] = t4.x; pf_g[4 * i + 1] = t4.y; pf_g[4 * i + 2] = t4.z; pf_g[4 * i + 3] = t4.w;
-            }
-            const uint4* qp = reinterpret_cast<const uint4*>(p.q + tok * qk_tok + (int64_t)hq * DK + 16 * wave_);
-            const uint4* kp = reinterpret_cast<const uint4*>(p.k + tok * qk_tok + (int64_t)hq * DK + 16 * wave_);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint4 a = qp[i], b = kp[i];
-                pf_q[4 * i] = a.x; pf_q[4 * i + 1] = a.y; pf_q[4 * i + 2] = a.z; pf_q[4 * i + 3] = a.w;
-                pf_k[4 * i] = b.x; pf_k[4 * i + 1] = b.y; pf_k[4 * i + 2] = b.z; pf_k[4 * i + 3] = b.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) pf_g[i] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { pf_q[i] = 0; pf_k[i] = 0; }
-        }
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + t0 * v_tok + (int64_t)hv * DK + dv0,
+                                                    Ln ? ((Ln - 1) * v_tok + DV) * 2 : 0);
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int it = tid_ + NTHREADS * u;
             const int j = it / (DV / 8), c8 = it % (DV / 8);
             pf_v[u] = make_uint4(0, 0, 0, 0);
-            if (it < CH * DV / 8 && j < Ln)
-                pf_v[u] = *reinterpret_cast<const uint4*>(p.v + (t0 + j) * v_tok + (int64_t)hv * DK + dv0 + 8 * c8);
+            if (it < CH * DV / 8) {
+                const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)((j * v_tok + 8 * c8) * 2), 0, 0);
+                pf_v[u] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+            }
         }
         if (tid_ < CH) {
-            float b = 0.f;
-            if (tid_ < Ln) {
-                const int64_t idx = (t0 + tid_) * p.Hv + hv;
-                b = p.beta_f32 ? reinterpret_cast<const float*>(p.beta)[idx]
-                               : bf2f(reinterpret_cast<const uint16_t*>(p.beta)[idx]);
+            const int esz = p.beta_f32 ? 4 : 2;
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(reinterpret_cast<const char*>(p.beta) + (t0 * p.Hv + hv) * esz, Ln ? ((Ln - 1) * p.Hv + 1) * esz : 0);
+            pf_b = p.beta_f32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, tid_ * p.Hv * 4, 0, 0)
+                              : (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, tid_ * p.Hv * 2, 0, 0);
+        }
+    };
+    auto prefetch = [&](int64_t cstart, int tid_, int lane_, int wave_) {
+        prefetch_g(cstart, lane_, wave_, 0, 8);
+        prefetch_qk(cstart, lane_, wave_, 0, 8);
+        prefetch_vb(cstart, tid_);
+    };
+    // Output rows staged in Ost: 16-byte pieces, whole row segments per lane group.
+    auto store_output = [&](int64_t t0, int rows, int tid_) {
+#pragma unroll
+        for (int u = 0; u < (CH * DV / 8 + NTHREADS - 1) / NTHREADS; ++u) {
+            const int it = tid_ + NTHREADS * u;
+            const int i = it / (DV / 8), c8 = it % (DV / 8);
+            if (it < CH * DV / 8 && i < rows) {
+                const uint4 w = *reinterpret_cast<const uint4*>(smem + L::Ost + (i * (DV + 8) + 8 * c8) * 2);
+                *reinterpret_cast<uint4*>(p.o + (t0 + i) * v_tok + (int64_t)hv * DK + dv0 + 8 * c8) = w;
             }
-            pf_b = b;
         }
     };
     if (len > 0) prefetch(0, tid, lane, wave);
@@ -328,67 +417,44 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             }
         }
 
-        // ================= a1: gate cumsum (inputs were prefetched) =================
-        // Thread layout for this phase: row r = lane (token within the chunk),
-        // channel group cg = wave (channels 16cg .. 16cg+15).
-        const int r = lane, cg = wave;
-        const bool rvalid = r < Lc;
-        float gv[16];
-        uint32_t qw[8], kw[8];   // 16 bf16 values each, two per word
-#pragma unroll
-        for (int i = 0; i < 16; ++i) gv[i] = pf_g[i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { qw[i] = pf_q[i]; kw[i] = pf_k[i]; }
-        const float beta_r = pf_b;
-        uint4 vcur[VPT];
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) vcur[i] = pf_v[i];
-        // Start the next chunk's loads now; they land while this chunk computes.
-        if (c0 + CH < len) prefetch(c0 + CH, tid, lane, wave);
+        // ================= a1: gate cumsum and decay factors =================
+        // Prep layout: lane cp = channel pair (channels 2cp, 2cp + 1), wave hb =
+        // half block (rows 8hb .. 8hb+7), block Ib = hb / 2, half hh = hb % 2.
+        const int cp = lane, hb = wave, Ib = hb >> 1, hh = hb & 1;
+        // The prefetched registers are consumed in place: g right here, v and beta
+        // below, q and k up to the output operand; the next prefetch refills them
+        // after their last use.
+        uint32_t (&qw)[8] = pf_q;
+        uint32_t (&kw)[8] = pf_k;
 
-        auto qf = [&](int ch) { return __uint_as_float((ch & 1) ? (qw[ch >> 1] & 0xffff0000u) : (qw[ch >> 1] << 16)); };
-        auto kf = [&](int ch) { return __uint_as_float((ch & 1) ? (kw[ch >> 1] & 0xffff0000u) : (kw[ch >> 1] << 16)); };
-        // Within each 16-row block: P_r = sum_{b < r' <= r} g (so exp(P) = e^{G_r - G_b}),
-        // Q_r = sum_{r < r' <= e} g (so exp(Q) = e^{G_e - G_r}).
-        // F = exp(P) and R = exp(Q) are the factors the intra operands need.
-        float Fv[16], Rv[16];
-        float Pt[TRACE ? 16 : 1];
-        const bool first_row = (r & 15) == 0;
-        float qb_first[16];
+        // Local sums inside the half block, per channel e, in log2 units (g log2 e):
+        //   lp[rr] = sum over rows (hh == 0 ? 1 : 0) .. rr   (prefix; the block's first
+        //            row b is excluded because factors are anchored there)
+        //   ls[rr] = sum over rows rr+1 .. 7                  (exclusive suffix)
+        constexpr float LOG2E = 1.4426950408889634f;
+        float lp[8][2], ls[8][2], gb2[2];
 #pragma unroll
-        for (int ch = 0; ch < 16; ++ch) {
-            float x = first_row ? 0.f : gv[ch];
-            x += row_shr(x, 1);
-            x += row_shr(x, 2);
-            x += row_shr(x, 4);
-            x += row_shr(x, 8);
-            if constexpr (TRACE) Pt[ch] = x;
-            Fv[ch] = fexp(x);
-            float y = row_shl(gv[ch], 1);
-            y += row_shl(y, 1);
-            y += row_shl(y, 2);
-            y += row_shl(y, 4);
-            y += row_shl(y, 8);
-            Rv[ch] = fexp(y);
-            qb_first[ch] = y;
+        for (int e = 0; e < 2; ++e) {
+            float g2[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) g2[rr] = pf_g[rr][e] * LOG2E;
+            gb2[e] = g2[0];
+            float acc = hh ? g2[0] : 0.f;
+            lp[0][e] = acc;
+#pragma unroll
+            for (int rr = 1; rr < 8; ++rr) { acc += g2[rr]; lp[rr][e] = acc; }
+            float sacc = 0.f;
+            ls[7][e] = 0.f;
+#pragma unroll
+            for (int rr = 6; rr >= 0; --rr) { sacc += g2[rr + 1]; ls[rr][e] = sacc; }
         }
-        if (first_row) {
-            const int I = r >> 4;
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                f32x4 a, b, t;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = gv[4 * c4 + e];
-                    b[e] = qb_first[4 * c4 + e];
-                    t[e] = a[e] + b[e];
-                }
-                *reinterpret_cast<f32x4*>(sBlkGb + I * 128 + 16 * cg + 4 * c4) = a;
-                *reinterpret_cast<f32x4*>(sBlkQb + I * 128 + 16 * cg + 4 * c4) = b;
-                *reinterpret_cast<f32x4*>(sBlkTot + I * 128 + 16 * cg + 4 * c4) = t;
-            }
+        if (hh == 0) {
+            *reinterpret_cast<f32x2*>(sXa + Ib * 128 + 2 * cp) = f32x2{lp[7][0], lp[7][1]};
+            *reinterpret_cast<f32x2*>(sXg + Ib * 128 + 2 * cp) = f32x2{gb2[0], gb2[1]};
+        } else {
+            *reinterpret_cast<f32x2*>(sXb + Ib * 128 + 2 * cp) = f32x2{lp[7][0], lp[7][1]};
         }
-        if (tid < CH) sBeta[tid] = beta_r;
+        if (tid < CH) sBeta[tid] = __uint_as_float(p.beta_f32 ? pf_b : pf_b << 16);
         if (tid == 0) *sFlag = 0;
         // v tile (64 tokens x DV channels of this slice), stored transposed as fp16.
 #pragma unroll
@@ -396,96 +462,126 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             const int it = tid + NTHREADS * u;
             if (it < CH * DV / 8) {
                 const int j = it / (DV / 8), c8 = it % (DV / 8);
-                const uint32_t ww[4] = {vcur[u].x, vcur[u].y, vcur[u].z, vcur[u].w};
+                const uint32_t ww[4] = {pf_v[u].x, pf_v[u].y, pf_v[u].z, pf_v[u].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint16_t bits = (uint16_t)((ww[e >> 1] >> (16 * (e & 1))) & 0xffff);
-                    reinterpret_cast<_Float16*>(smem + L::Vt)[(8 * c8 + e) * S72 + j] = (_Float16)bf2f(bits);
+                    const float f = (e & 1) ? bf_hi(ww[e >> 1]) : bf_lo(ww[e >> 1]);
+                    reinterpret_cast<_Float16*>(smem + L::Vt)[(8 * c8 + e) * S72 + j] = (_Float16)f;
                 }
             }
         }
-        __syncthreads();
-
-        // Per (block I, channel c) factors.  Thread layout: I = tid / 128, c = tid % 128.
-        {
-            const int I = tid >> 7, c = tid & 127;
-            float tot[4];
-#pragma unroll
-            for (int K = 0; K < 4; ++K) tot[K] = sBlkTot[K * 128 + c];
-            const float gb = sBlkGb[I * 128 + c], qb = sBlkQb[I * 128 + c];
-            float off = 0.f;
-            for (int K = 0; K < I; ++K) off += tot[K];
-            float tail = 0.f;
-            for (int K = 3; K > I; --K) tail += tot[K];
-            sEb[I * 128 + c] = fexp(off + gb);            // e^{G_{b_I}}
-            sKhs[I * 128 + c] = fexp(tail);               // e^{G_last - G_{e_I}}
-            sInvR[I * 128 + c] = fexp(-qb);               // e^{G_{b_I} - G_{e_I}}
-            float acc = gb;                               // e^{G_{b_I} - G_{e_J}}, J = I-1, I-2, ...
-            for (int J = I - 1; J >= 0; --J) {
-                sLam[pair_index(I, J) * 128 + c] = fexp(acc);
-                acc += tot[J];
-            }
-            if (I == 0) sGam[c] = fexp(((tot[0] + tot[1]) + tot[2]) + tot[3]);
-            if (-qb > GUARD_DECAY) *sFlag = 1;
+        // g, v and beta of this chunk are consumed: next chunk's g rows 0..3, v, beta.
+        const bool has_next = c0 + CH < len;
+        if (has_next) {
+            prefetch_g(c0 + CH, lane, wave, 0, 4);
+            prefetch_vb(c0 + CH, tid);
         }
-        __syncthreads();
-        const bool guard = *sFlag != 0;   // block-uniform
+        lds_barrier();
 
-        // Intra operands (thread layout: row r, channel group cg).  All LDS reads first.
+        // Block sums of both channels; then the factors of every row of this half block:
+        //   F = e^{G_r - G_b}  (<= 1),  R = e^{G_e - G_r}  (<= 1)
+        // and the per-(block, channel) scalars.
+        float F[8][2], R[8][2];
+        float eb[2], khs[2], invr[2], lam[3][2];
+        int guard_local = 0;
         {
-            const int I = r >> 4;
-            float invR[16];
+            // Block sums in log2 units; Ib and hh are wave-uniform, so every LDS
+            // address below is uniform per wave except for the channel.
+            const f32x2 xa = *reinterpret_cast<const f32x2*>(sXa + Ib * 128 + 2 * cp);
+            const f32x2 xb = *reinterpret_cast<const f32x2*>(sXb + Ib * 128 + 2 * cp);
+            const f32x2 xg = *reinterpret_cast<const f32x2*>(sXg + Ib * 128 + 2 * cp);
+            f32x2 tot[4], gI[4];
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const f32x4 t = *reinterpret_cast<const f32x4*>(sInvR + I * 128 + 16 * cg + 4 * c4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) invR[4 * c4 + e] = t[e];
+            for (int K = 0; K < 4; ++K) {
+                const f32x2 a = *reinterpret_cast<const f32x2*>(sXa + K * 128 + 2 * cp);
+                const f32x2 b = *reinterpret_cast<const f32x2*>(sXb + K * 128 + 2 * cp);
+                gI[K] = *reinterpret_cast<const f32x2*>(sXg + K * 128 + 2 * cp);
+                tot[K] = (gI[K] + a) + b;
             }
-            half8 aq[2], ak[2], bd[2];
-#pragma unroll
-            for (int ch = 0; ch < 16; ++ch) {
-                const float qx = qf(ch), kx = kf(ch);
-                aq[ch >> 3][ch & 7] = (_Float16)(qx * Fv[ch]);
-                ak[ch >> 3][ch & 7] = (_Float16)(kx * Fv[ch]);
-                bd[ch >> 3][ch & 7] = (_Float16)(kx * Rv[ch] * invR[ch]);
+            // off = sum of the blocks before Ib, tail = sum of the blocks after Ib,
+            // lamarg[d] = exponent of e^{G_{b_I2} - G_{e_Ib}} for I2 = Ib + 1 + d.
+            // Ib is wave-uniform: one branch per wave, no per-lane selects.
+            f32x2 off, tail, lamarg[3];
+            switch (Ib) {
+                case 0: block_scalars<0>(tot, gI, off, tail, lamarg); break;
+                case 1: block_scalars<1>(tot, gI, off, tail, lamarg); break;
+                case 2: block_scalars<2>(tot, gI, off, tail, lamarg); break;
+                default: block_scalars<3>(tot, gI, off, tail, lamarg); break;
             }
-            const int off = (r * S136 + 16 * cg) * 2;
-            *reinterpret_cast<half8*>(smem + L::Aq + off) = aq[0];
-            *reinterpret_cast<half8*>(smem + L::Aq + off + 16) = aq[1];
-            *reinterpret_cast<half8*>(smem + L::Ak + off) = ak[0];
-            *reinterpret_cast<half8*>(smem + L::Ak + off + 16) = ak[1];
-            *reinterpret_cast<half8*>(smem + L::Bd + off) = bd[0];
-            *reinterpret_cast<half8*>(smem + L::Bd + off + 16) = bd[1];
-            for (int I2 = I + 1; I2 < 4; ++I2) {
-                const int pi = pair_index(I2, I);
-                float lam[16];
+            const f32x2 all = ((tot[0] + tot[1]) + tot[2]) + tot[3];
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const f32x4 t = *reinterpret_cast<const f32x4*>(sLam + pi * 128 + 16 * cg + 4 * c4);
+            for (int e = 0; e < 2; ++e) {
+                const float pre = hh ? xa[e] : 0.f;   // rows b+1..b+7 precede the second half
+                const float suf = hh ? 0.f : xb[e];   // rows b+8..b+15 follow the first half
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) lam[4 * c4 + e] = t[e];
+                for (int rr = 0; rr < 8; ++rr) {
+                    F[rr][e] = fexp2(pre + lp[rr][e]);
+                    R[rr][e] = fexp2(suf + ls[rr][e]);
                 }
-                half8 bo[2];
+                const float qb = xa[e] + xb[e];       // (G_e - G_b) log2 e of this block
+                eb[e] = fexp2(off[e] + xg[e]);        // e^{G_b}
+                khs[e] = fexp2(tail[e]);              // e^{G_last - G_e}
+                invr[e] = fexp2(-qb);                 // e^{G_b - G_e}
+                if (-qb > GUARD_DECAY * LOG2E) guard_local = 1;
+                if constexpr (TRACE) {
+                    if (p.tr_G && s == 0) {
 #pragma unroll
-                for (int ch = 0; ch < 16; ++ch) bo[ch >> 3][ch & 7] = (_Float16)(kf(ch) * Rv[ch] * lam[ch]);
-                const int o2 = ((16 * pi + (r & 15)) * S136 + 16 * cg) * 2;
-                *reinterpret_cast<half8*>(smem + L::Bo + o2) = bo[0];
-                *reinterpret_cast<half8*>(smem + L::Bo + o2 + 16) = bo[1];
-            }
-            if constexpr (TRACE) {
-                if (p.tr_G && s == 0 && rvalid) {
-                    float* dst = p.tr_G + ((tok0 + r) * p.Hv + hv) * DK + 16 * cg;
-#pragma unroll
-                    for (int ch = 0; ch < 16; ++ch) {
-                        const int c = 16 * cg + ch;
-                        float offv = 0.f;
-                        for (int K = 0; K < I; ++K) offv += sBlkTot[K * 128 + c];
-                        dst[ch] = offv + sBlkGb[I * 128 + c] + Pt[ch];
+                        for (int rr = 0; rr < 8; ++rr) {
+                            const int row = 8 * hb + rr;
+                            if (row < Lc)
+                                p.tr_G[((tok0 + row) * p.Hv + hv) * DK + 2 * cp + e] =
+                                    (off[e] + xg[e] + pre + lp[rr][e]) * 0.6931471805599453f;
+                        }
                     }
                 }
             }
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                lam[d][0] = fexp2(lamarg[d][0]);
+                lam[d][1] = fexp2(lamarg[d][1]);
+            }
+            if (Ib == 0 && hh == 0)
+                *reinterpret_cast<f32x2*>(sGam + 2 * cp) = f32x2{fexp2(all[0]), fexp2(all[1])};
         }
-        __syncthreads();
+        if (guard_local) *sFlag = 1;
+        // Intra operands (rows of this half block, two channels per 32-bit word).
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int row = 8 * hb + rr;
+            const float q0 = bf_lo(qw[rr]), q1 = bf_hi(qw[rr]);
+            const float k0 = bf_lo(kw[rr]), k1 = bf_hi(kw[rr]);
+            const int o = (row * S136 + 2 * cp) * 2;
+            *reinterpret_cast<uint32_t*>(smem + L::Aq + o) = pack_h2(q0 * F[rr][0], q1 * F[rr][1]);
+            *reinterpret_cast<uint32_t*>(smem + L::Ak + o) = pack_h2(k0 * F[rr][0], k1 * F[rr][1]);
+            const float kr0 = k0 * R[rr][0], kr1 = k1 * R[rr][1];
+            *reinterpret_cast<uint32_t*>(smem + L::Bd + o) = pack_h2(kr0 * invr[0], kr1 * invr[1]);
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                const int I2 = Ib + 1 + d;
+                if (I2 < 4) {
+                    const int o2 = ((16 * pair_index(I2, Ib) + (row & 15)) * S136 + 2 * cp) * 2;
+                    *reinterpret_cast<uint32_t*>(smem + L::Bo + o2) = pack_h2(kr0 * lam[d][0], kr1 * lam[d][1]);
+                }
+            }
+        }
+        // Transposed operands: (k e^G)^T for W and (k e^{G_last - G})^T for the state
+        // update; eight consecutive rows of one channel are one 16-byte store.
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            half8 kg, kh;
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const float kx = e ? bf_hi(kw[rr]) : bf_lo(kw[rr]);
+                kg[rr] = (_Float16)(kx * F[rr][e] * eb[e]);
+                kh[rr] = (_Float16)(kx * R[rr][e] * khs[e]);
+            }
+            const int c = 2 * cp + e;
+            *reinterpret_cast<half8*>(smem + L::KgT + (c * S72 + 8 * hb) * 2) = kg;
+            *reinterpret_cast<half8*>(smem + L::KhT + (c * S72 + 8 * hb) * 2) = kh;
+        }
+        if (has_next) prefetch_g(c0 + CH, lane, wave, 4, 8);
+        lds_barrier();
+        const bool guard = *sFlag != 0;   // block-uniform
 
         // ================= a2: intra-chunk Aqk / Akk on MFMA =================
         // 20 jobs of 16x16 output tiles: (matrix, I, J) with J <= I.  Each tile is
@@ -516,19 +612,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 iacc[u] = acc;
             }
         }
-        // LDS reads for the derived operands below, issued before the barrier.
-        float ebv[16], khs[16];
-        {
-            const int I = r >> 4;
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(sEb + I * 128 + 16 * cg + 4 * c4);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(sKhs + I * 128 + 16 * cg + 4 * c4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { ebv[4 * c4 + e] = a[e]; khs[4 * c4 + e] = b[e]; }
-            }
-        }
-        __syncthreads();
+        lds_barrier();
         // Store the lower tiles (masked, scaled), zero the upper ones.
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
@@ -557,7 +641,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         }
         {
             // Upper 16x16 tiles (I < J) of Akk (fp32) and Aqk (fp16) are zero.
-            const int tile = tid >> 6, w64 = tid & 63;   // 8 slots, 6 used
+            const int tile = wave, w64 = lane;   // 8 slots, 6 used
             if (tile < 6) {
                 const int I = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
                 const int J = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
@@ -575,7 +659,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         }
         if (guard) {
             // Exact fp32 diagonal blocks for strongly decaying chunks.
-            __syncthreads();
+            lds_barrier();
             for (int idx = tid; idx < 4 * 256; idx += NTHREADS) {
                 const int B = idx >> 8, m = (idx >> 4) & 15, nn = idx & 15;
                 if (nn > m) continue;
@@ -588,8 +672,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                     for (int c = 0; c < DK; ++c) {
                         float dsum = 0.f;
                         for (int rr = j + 1; rr <= i; ++rr) dsum += p.g[(tok0 + rr) * v_tok + (int64_t)hv * DK + c];
-                        const float e = fexp(dsum);
-                        const float kjv = bf2f(kj[c]) * e;
+                        const float ex = fexp(dsum);
+                        const float kjv = bf2f(kj[c]) * ex;
                         sq += bf2f(qi[c]) * kjv;
                         sk += bf2f(ki[c]) * kjv;
                     }
@@ -599,22 +683,21 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 if (TRACE && p.tr_Aqk && s == 0 && i < Lc) p.tr_Aqk[((tok0 + i) * p.Hv + hv) * CH + j] = p.scale * sq;
             }
         }
-        // Derived operands for W, the output and the state update (row r, channels 16cg..).
-        {
-            half8 qg[2];
+        // scale q e^G for the output (rows of this half block, prep layout).
 #pragma unroll
-            for (int ch = 0; ch < 16; ++ch) {
-                const int c = 16 * cg + ch;
-                const float kx = kf(ch);
-                qg[ch >> 3][ch & 7] = (_Float16)(p.scale * qf(ch) * Fv[ch] * ebv[ch]);
-                reinterpret_cast<_Float16*>(smem + L::KgT)[c * S72 + r] = (_Float16)(kx * Fv[ch] * ebv[ch]);
-                reinterpret_cast<_Float16*>(smem + L::KhT)[c * S72 + r] = (_Float16)(kx * Rv[ch] * khs[ch]);
-            }
-            const int off = (r * S136 + 16 * cg) * 2;
-            *reinterpret_cast<half8*>(smem + L::Qg + off) = qg[0];
-            *reinterpret_cast<half8*>(smem + L::Qg + off + 16) = qg[1];
+        for (int rr = 0; rr < 8; ++rr) {
+            const int row = 8 * hb + rr;
+            const int o = (row * S136 + 2 * cp) * 2;
+            *reinterpret_cast<uint32_t*>(smem + L::Qg + o) =
+                pack_h2(p.scale * bf_lo(qw[rr]) * F[rr][0] * eb[0], p.scale * bf_hi(qw[rr]) * F[rr][1] * eb[1]);
         }
-        __syncthreads();
+        // The previous chunk's output, staged in Ost, goes out now: after this
+        // chunk's prefetched registers have been consumed and before the next
+        // prefetch is issued.  Global stores share the vmcnt counter with loads, so
+        // this order keeps every wait for prefetched data clear of pending stores.
+        if (c0 > 0) store_output(tok0 - CH, CH, tid);
+        if (has_next) prefetch_qk(c0 + CH, lane, wave, 0, 4);
+        lds_barrier();
         if (TRACE && p.tr_Akk && s == 0) {
             for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
                 const int i = idx >> 6, j = idx & 63;
@@ -623,15 +706,21 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
         }
 
         // ================= a3: T = (I + Akk)^{-1} in fp32 =================
-        // Diagonal 16x16 blocks: wave 0, lane = (block, column); forward substitution.
-        // Results go back row-major into the diagonal blocks of A32 and column-major
-        // into the TtD scratch (the B-operand layout of the fp32 MFMA products below).
+        // Three barrier-separated steps.  T diag(beta), the fp16 MFMA operand T16,
+        // is written by whichever wave produces each block.
+        //  1. waves 0 / 1: diagonal blocks (0,1) / (2,3) by forward substitution
+        //     (lane = (block, column)), then the pair T_10 / T_32 =
+        //     -T_II A_I,I-1 T_I-1,I-1 on fp32 MFMA; waves 2..7 zero T16's upper blocks.
+        //  2. waves 0..3: X_IJ = sum_{K=J}^{1} A_IK T_KJ  (I in {2,3}, J in {0,1}).
+        //  3. waves 0..3: T_2J = -T_22 X_2J, T_3J = -(T_32 X_2J + T_33 X_3J).
+        // Diagonal T blocks go back row-major into A32 (as MFMA A operands) and
+        // column-major into TtD (as B operands).
         float* sTtD = reinterpret_cast<float*>(smem + L::TtD);
-        float* sYt = reinterpret_cast<float*>(smem + L::Yt);
         float* sT1t = reinterpret_cast<float*>(smem + L::T1t);
         float* sXt = reinterpret_cast<float*>(smem + L::Xt);
-        if (wave == 0) {
-            const int B = lane >> 4, j = lane & 15;
+        _Float16* sT16 = reinterpret_cast<_Float16*>(smem + L::T16);
+        if (wave < 2) {
+            const int B = 2 * wave + ((lane >> 4) & 1), j = lane & 15;   // lanes 32..63 repeat 0..31
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
@@ -640,36 +729,60 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
 #pragma unroll
                 for (int i = kk + 1; i < 16; ++i) x[i] -= sA32[(16 * B + i) * S68 + 16 * B + kk] * x[kk];
             }
-            // Diagonal blocks are read only by this wave; write back after all reads.
+            // The diagonal blocks of A are read only by this wave; write back after all reads.
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane < 32) {
+                const float bj = sBeta[16 * B + j];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sA32[(16 * B + i) * S68 + 16 * B + j] = x[i];
+                for (int i = 0; i < 16; ++i) {
+                    sA32[(16 * B + i) * S68 + 16 * B + j] = x[i];
+                    sT16[(16 * B + i) * S72 + 16 * B + j] = (_Float16)(x[i] * bj);
+                    if (TRACE && p.tr_T && s == 0 && 16 * B + i < Lc)
+                        p.tr_T[((tok0 + 16 * B + i) * p.Hv + hv) * CH + 16 * B + j] = x[i];
+                }
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                f32x4 v4 = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
-                *reinterpret_cast<f32x4*>(sTtD + (B * 16 + j) * TS + 4 * i4) = v4;
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    f32x4 v4 = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+                    *reinterpret_cast<f32x4*>(sTtD + (B * 16 + j) * TS + 4 * i4) = v4;
+                }
             }
-        }
-        __syncthreads();
-        // Off-diagonal blocks on fp32 MFMA (16x16x4): T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
-        // by doubling: first (1,0) and (3,2), then the lower-left 32x32 block.
-        // mm16 multiplies a row-major A block by a column-major B block.
-        if (wave < 2) {
-            // wave 0: pair (1,0); wave 1: pair (3,2)
-            const int I = wave == 0 ? 1 : 3, J = I - 1;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // pair (I, I-1) with I = 2 wave + 1: T_I,I-1 = -T_II (A_I,I-1 T_I-1,I-1)
+            const int I = 2 * wave + 1, J = I - 1;
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
             y = mm16(sA32 + (16 * I) * S68 + 16 * J, S68, sTtD + J * 16 * TS, TS, y, lane);
-            store_colmajor(sYt + wave * 16 * TS, y, lane);
+            store_colmajor(sT1t + wave * 16 * TS, y, lane);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mm16(sA32 + (16 * I) * S68 + 16 * I, S68, sYt + wave * 16 * TS, TS, t, lane);
+            t = mm16(sA32 + (16 * I) * S68 + 16 * I, S68, sT1t + wave * 16 * TS, TS, t, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] = -t[e];
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             store_rowmajor(sA32 + (16 * I) * S68 + 16 * J, S68, t, lane);   // replaces A_IJ, no longer read
             store_colmajor(sT1t + wave * 16 * TS, t, lane);
+            store_t16(sT16, t, I, J, sBeta, lane);
+            if (TRACE && p.tr_T && s == 0) trace_tblock(p.tr_T, tok0, Lc, p.Hv, hv, t, I, J, lane);
+        } else {
+            // zero upper blocks (I < J) of T16: six 16x16 blocks, 8 columns per item
+            for (int it = tid - 128; it < 6 * 32; it += NTHREADS - 128) {
+                const int tile = it >> 5, w32 = it & 31;
+                const int I = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+                const int J = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+                const int m = w32 >> 1, h = w32 & 1;
+                half8 z;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
+                *reinterpret_cast<half8*>(smem + L::T16 + ((16 * I + m) * S72 + 16 * J + 8 * h) * 2) = z;
+                if (TRACE && p.tr_T && s == 0 && 16 * I + m < Lc) {
+                    float* dst = p.tr_T + ((tok0 + 16 * I + m) * p.Hv + hv) * CH + 16 * J + 8 * h;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dst[e] = 0.f;
+                }
+            }
         }
-        __syncthreads();
+        lds_barrier();
+        // Next chunk's q, k rows 4..7 (waves 0 and 1 load theirs after the diagonal work).
+        if (has_next) prefetch_qk(c0 + CH, lane, wave, 4, 8);
         if (wave < 4) {
             // X_IJ = sum_{K=J}^{1} A_IK T_KJ for I in {2,3}, J in {0,1}; wave = 2 (I-2) + J
             const int I = 2 + (wave >> 1), J = wave & 1;
@@ -682,7 +795,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             }
             store_colmajor(sXt + wave * 16 * TS, x4, lane);
         }
-        __syncthreads();
+        lds_barrier();
         if (wave < 4) {
             // T_2J = -T_22 X_2J ; T_3J = -(T_32 X_2J + T_33 X_3J)
             const int I = 2 + (wave >> 1), J = wave & 1;
@@ -695,30 +808,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] = -t[e];
-            store_rowmajor(sA32 + (16 * I) * S68 + 16 * J, S68, t, lane);     // A_IJ is no longer read
+            store_t16(sT16, t, I, J, sBeta, lane);
+            if (TRACE && p.tr_T && s == 0) trace_tblock(p.tr_T, tok0, Lc, p.Hv, hv, t, I, J, lane);
         }
-        __syncthreads();
-        // T diag(beta) as the fp16 MFMA operand; row i, columns 8*(tid%8) ...
-        {
-            const int i = tid >> 3, j0 = 8 * (tid & 7);
-            const f32x4 t0 = *reinterpret_cast<const f32x4*>(sA32 + i * S68 + j0);
-            const f32x4 t1 = *reinterpret_cast<const f32x4*>(sA32 + i * S68 + j0 + 4);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + j0);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + j0 + 4);
-            half8 h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[e] = (_Float16)(t0[e] * b0[e]);
-                h[4 + e] = (_Float16)(t1[e] * b1[e]);
-            }
-            *reinterpret_cast<half8*>(smem + L::T16 + (i * S72 + j0) * 2) = h;
-            if (TRACE && p.tr_T && s == 0 && i < Lc) {
-                float* dst = p.tr_T + ((tok0 + i) * p.Hv + hv) * CH + j0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { dst[e] = t0[e]; dst[4 + e] = t1[e]; }
-            }
-        }
-        __syncthreads();
+        lds_barrier();
 
         // ================= a4: W^T = (k e^G)^T (T diag beta)^T, U = T diag(beta) v =================
         {
@@ -769,18 +862,26 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= a5 (first half): v_new = U - W h =================
         if (wave < NU) {
-            f32x16 acc = uacc;
+            // Two independent accumulation chains (even / odd k steps) halve the
+            // dependent MFMA latency; they are summed once at the end.
+            f32x16 acc = uacc, acc1;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
+            for (int e = 0; e < 16; ++e) acc1[e] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 8; kk += 2) {
                 const int ko = 16 * kk + 8 * (lane >> 5);
-                const half8 a = lds_h8(smem, L::W + ((32 * tu_it + (lane & 31)) * S136 + ko) * 2);
-                const half8 b = lds_h8(smem, L::HT + ((32 * tu_dt + (lane & 31)) * S136 + ko) * 2);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+                const half8 a0 = lds_h8(smem, L::W + ((32 * tu_it + (lane & 31)) * S136 + ko) * 2);
+                const half8 b0 = lds_h8(smem, L::HT + ((32 * tu_dt + (lane & 31)) * S136 + ko) * 2);
+                const half8 a1 = lds_h8(smem, L::W + ((32 * tu_it + (lane & 31)) * S136 + ko + 16) * 2);
+                const half8 b1 = lds_h8(smem, L::HT + ((32 * tu_dt + (lane & 31)) * S136 + ko + 16) * 2);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc1, 0, 0, 0);
             }
+            acc += acc1;
             const int d = 32 * tu_dt + (lane & 31);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -796,41 +897,47 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= a6: o^T = h^T (scale q e^G)^T + v_new^T Aqk^T =================
+        // Results go to the output staging tile Ost; they are written to HBM during
+        // the next chunk (or after the loop).
         {
             const int wo = 7 - wave;
             if (wo < NU) {
                 const int it = wo / (DV / 32), dt = wo % (DV / 32);
-                f32x16 acc;
+                f32x16 acc, acc1;   // two accumulation chains, summed at the end
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+                for (int e = 0; e < 16; ++e) { acc[e] = 0.f; acc1[e] = 0.f; }
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
+                for (int kk = 0; kk < 8; kk += 2) {
                     const int ko = 16 * kk + 8 * (lane >> 5);
-                    const half8 a = lds_h8(smem, L::HT + ((32 * dt + (lane & 31)) * S136 + ko) * 2);
-                    const half8 b = lds_h8(smem, L::Qg + ((32 * it + (lane & 31)) * S136 + ko) * 2);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+                    const half8 a0 = lds_h8(smem, L::HT + ((32 * dt + (lane & 31)) * S136 + ko) * 2);
+                    const half8 b0 = lds_h8(smem, L::Qg + ((32 * it + (lane & 31)) * S136 + ko) * 2);
+                    const half8 a1 = lds_h8(smem, L::HT + ((32 * dt + (lane & 31)) * S136 + ko + 16) * 2);
+                    const half8 b1 = lds_h8(smem, L::Qg + ((32 * it + (lane & 31)) * S136 + ko + 16) * 2);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc1, 0, 0, 0);
                 }
                 const int kmax = it == 0 ? 2 : 4;
-                for (int kk = 0; kk < kmax; ++kk) {
+                for (int kk = 0; kk < kmax; kk += 2) {
                     const int ko = 16 * kk + 8 * (lane >> 5);
-                    const half8 a = lds_h8(smem, L::VnT + ((32 * dt + (lane & 31)) * S72 + ko) * 2);
-                    const half8 b = lds_h8(smem, L::Aqk + ((32 * it + (lane & 31)) * S72 + ko) * 2);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+                    const half8 a0 = lds_h8(smem, L::VnT + ((32 * dt + (lane & 31)) * S72 + ko) * 2);
+                    const half8 b0 = lds_h8(smem, L::Aqk + ((32 * it + (lane & 31)) * S72 + ko) * 2);
+                    const half8 a1 = lds_h8(smem, L::VnT + ((32 * dt + (lane & 31)) * S72 + ko + 16) * 2);
+                    const half8 b1 = lds_h8(smem, L::Aqk + ((32 * it + (lane & 31)) * S72 + ko + 16) * 2);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc1, 0, 0, 0);
                 }
+                acc += acc1;
                 const int i = 32 * it + (lane & 31);
-                if (i < Lc) {
-                    uint16_t* dst = p.o + (tok0 + i) * v_tok + (int64_t)hv * DK + dv0 + 32 * dt;
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int d = 8 * q4 + 4 * (lane >> 5);
-                        uint2 w;
-                        w.x = (uint32_t)f2bf(acc[4 * q4]) | ((uint32_t)f2bf(acc[4 * q4 + 1]) << 16);
-                        w.y = (uint32_t)f2bf(acc[4 * q4 + 2]) | ((uint32_t)f2bf(acc[4 * q4 + 3]) << 16);
-                        *reinterpret_cast<uint2*>(dst + d) = w;
-                    }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * dt + 8 * q4 + 4 * (lane >> 5);
+                    uint2 w;
+                    w.x = pack_bf2(acc[4 * q4], acc[4 * q4 + 1]);
+                    w.y = pack_bf2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+                    *reinterpret_cast<uint2*>(smem + L::Ost + (i * (DV + 8) + d) * 2) = w;
                 }
             }
         }
@@ -841,9 +948,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
             if (th < NH) {
                 const int ct = th / (DV / 32), dt = th % (DV / 32);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int c = 32 * ct + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    hacc[u][e] *= sGam[c];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + 32 * ct + 8 * q4 + 4 * (lane >> 5));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hacc[u][4 * q4 + e] *= gm[e];
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -854,7 +962,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int u = 0; u < HPW; ++u) {
             const int th = wave + 8 * u;
@@ -871,8 +979,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(const KdaParams p)
                 }
             }
         }
-        // The next chunk's first LDS writes (sBlk, sBeta, Vt) do not alias HT, and
-        // its first barrier orders these stores before any read of HT.
+        // The next chunk writes Xch, Beta, Flag and Vt before its first barrier; none
+        // of them aliases HT.  Ost is read (and then rewritten) only after later barriers.
+    }
+
+    // ---- output of the last chunk (staged in Ost before the loop's last barrier) ----
+    if (len > 0) {
+        const int64_t last = (len - 1) / CH * CH;
+        store_output(bos + last, (int)(len - last), tid);
     }
 
     // ---- final state ----
