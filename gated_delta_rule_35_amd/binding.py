@@ -1,9 +1,12 @@
 """ctypes binding of libkda.so (argument marshalling only).
 
 Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_trace,
-kda_status_string, kda_dv_slices.  Tensors are passed as kda_tensor_t
-descriptors built from torch tensors (data pointer, dtype, shape, strides); the
-stream is torch's current HIP stream unless one is given.
+kda_fwd_workspace_size, kda_status_string, kda_dv_slices.  Tensors are passed
+as kda_tensor_t descriptors built from torch tensors (data pointer, dtype,
+shape, strides); the stream is torch's current HIP stream unless one is given.
+The workspace is a uint8 device tensor from torch's caching allocator unless
+the caller passes one (or `workspace=False`, which lets the library allocate
+it in stream order).
 """
 import ctypes
 import os
@@ -17,8 +20,8 @@ _lib = None
 KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
-                "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP"]
-EXPORTED = ["kda_fwd", "kda_fwd_trace", "kda_status_string", "kda_dv_slices"]
+                "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
+EXPORTED = ["kda_fwd", "kda_fwd_trace", "kda_fwd_workspace_size", "kda_status_string", "kda_dv_slices"]
 
 
 class KdaTensor(ctypes.Structure):
@@ -52,15 +55,18 @@ def load_library(path=None):
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(p)
     tp = ctypes.POINTER(KdaTensor)
-    lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p]
+    lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p, ctypes.c_int64,
+                            ctypes.c_void_p]
     lib.kda_fwd.restype = ctypes.c_int
-    lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp,
-                                  ctypes.POINTER(KdaTrace), ctypes.c_void_p]
+    lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_dv_slices.argtypes = [ctypes.c_int64, ctypes.c_int64]
     lib.kda_dv_slices.restype = ctypes.c_int32
+    lib.kda_fwd_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.kda_fwd_workspace_size.restype = ctypes.c_int64
     if path is None:
         _lib = lib
     return lib
@@ -105,7 +111,34 @@ def kda_dv_slices(num_sequences, num_value_heads):
     return int(load_library().kda_dv_slices(num_sequences, num_value_heads))
 
 
-def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace):
+def kda_fwd_workspace_size(total_tokens, num_sequences, num_value_heads):
+    return int(load_library().kda_fwd_workspace_size(total_tokens, num_sequences, num_value_heads))
+
+
+def _workspace(workspace, q, v, cu_seqlens, stream):
+    """(tensor, pointer, size) of the workspace argument: a given uint8 tensor,
+    NULL for workspace=False (the library allocates in stream order), else a
+    fresh tensor of the size the library asks for.  A fresh tensor is marked as
+    used on an explicitly given stream, so the caching allocator does not hand
+    it out again before that stream's work on it is done."""
+    if workspace is False:
+        return None, None, 0
+    if workspace is None:
+        if q.dim() != 4 or v.dim() != 4:
+            return None, None, 0   # the C library rejects the shapes
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            return None, None, 0   # a raw stream handle: let the library allocate on it
+        n = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        size = kda_fwd_workspace_size(q.shape[0] * q.shape[1], max(n, 0), v.shape[2])
+        if size <= 0:
+            return None, None, 0
+        workspace = torch.empty(size, dtype=torch.uint8, device=v.device)
+        if stream is not None:
+            workspace.record_stream(stream)
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace):
     lib = load_library()
     tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
     for t in tensors:
@@ -113,8 +146,9 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
             raise ValueError("kda_fwd needs every tensor on the GPU")
     descs = [describe(t) for t in tensors]
     s = _stream_handle(stream, tensors)
+    _ws, ws_ptr, ws_size = _workspace(workspace, q, v, cu_seqlens, stream)
     args = [_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]), float(scale),
-            _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8])]
+            _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8]), ws_ptr, ws_size]
     if trace is None:
         _check(lib, lib.kda_fwd(*args, s))
     else:
@@ -123,23 +157,26 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
 
 
 def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
-            stream=None):
+            stream=None, workspace=None):
     """KDA forward.  Returns (out, final_state); allocates them when not given
-    (final_state is allocated only when `final_state=True` is passed)."""
+    (final_state is allocated only when `final_state=True` is passed).
+    `workspace`: a uint8 device tensor of at least kda_fwd_workspace_size() bytes,
+    None (allocated here from torch's caching allocator) or False (the library
+    allocates it in stream order)."""
     if out is None:
         out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     if final_state is True:
         n = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
         final_state = torch.empty((n, v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=v.device)
-    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace)
     return out, final_state
 
 
 def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state=None, out=None,
-                  final_state=None, stream=None):
+                  final_state=None, stream=None, workspace=None):
     """kda_fwd that also fills the fp32 intermediate dumps in `trace`, a dict with
     any of the keys G, Aqk, Akk, T, W, U, v_new, h (see include/kda.h)."""
     if out is None:
         out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
-    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace)
     return out, final_state

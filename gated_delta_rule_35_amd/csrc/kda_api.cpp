@@ -18,7 +18,7 @@
 namespace {
 
 constexpr int64_t kHeadDim = 128;
-constexpr int64_t kMaxBlocks = int64_t(1) << 22;  // 512 threads each: grid stays below 2^31 work-items
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;  // 512 threads each: a grid stays below 2^31 work-items
 
 int64_t numel(const kda_tensor_t* t) {
     int64_t n = 1;
@@ -58,7 +58,8 @@ bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
 
 kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                  const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
-                 const kda_tensor_t* out, const kda_tensor_t* hT, const kda_trace_t* trace, void* stream) {
+                 const kda_tensor_t* out, const kda_tensor_t* hT, void* workspace, int64_t workspace_size,
+                 const kda_trace_t* trace, void* stream) {
     kda_status_t st;
     if ((st = check_tensor(q, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
     if ((st = check_tensor(k, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
@@ -95,6 +96,11 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (Hv > (int64_t(1) << 16) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
     const int S = kda_dv_slices(N, Hv);
     if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const int64_t nslots = (B * T + 63) / 64 + N;
+    if (nslots * Hv > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const int64_t ws_need = kda::workspace_bytes(B * T, N, Hv);
+    if (workspace && (workspace_size < ws_need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+        return KDA_ERR_WORKSPACE;
 
     kda::KdaParams p{};
     p.q = static_cast<const uint16_t*>(q->data);
@@ -122,11 +128,21 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
         p.tr_vnew = trace->v_new;
         p.tr_h = trace->h;
     }
+    p.nslots = nslots;
     if (N == 0 || (T == 0 && !hT)) return KDA_OK;  // nothing to compute or write
-    const hipError_t e = kda::launch_kda_fwd(p, S, trace != nullptr, static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    // Without a caller workspace the record array is allocated and released in
+    // stream order around the two launches.
+    void* ws = workspace;
+    if (!ws && T > 0 && hipMallocAsync(&ws, (size_t)ws_need, hs) != hipSuccess) return KDA_ERR_HIP;
+    p.ws = static_cast<char*>(ws);
+    hipError_t e = hipSuccess;
+    if (T > 0) e = kda::launch_kda_intra(p, trace != nullptr, hs);
+    if (e == hipSuccess) e = kda::launch_kda_scan(p, S, trace != nullptr, hs);
+    if (!workspace && ws && hipFreeAsync(ws, hs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     if (e != hipSuccess) return KDA_ERR_HIP;
     if (std::getenv("KDA_DEBUG_SYNC")) {
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+        if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERR_HIP;
         if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
     }
     return KDA_OK;
@@ -142,20 +158,27 @@ int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads) {
     return num_sequences * num_value_heads >= 128 ? 2 : 4;
 }
 
+int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads) {
+    if (total_tokens < 0 || num_sequences < 0 || num_value_heads < 0) return -1;
+    return kda::workspace_bytes(total_tokens, num_sequences, num_value_heads);
+}
+
 kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                      const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
                      const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
-                     void* stream) {
-    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, nullptr, stream);
+                     void* workspace, int64_t workspace_size, void* stream) {
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
+               nullptr, stream);
 }
 
 kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                            const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                            const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
-                           const kda_tensor_t* out, const kda_tensor_t* final_state, const kda_trace_t* trace,
-                           void* stream) {
+                           const kda_tensor_t* out, const kda_tensor_t* final_state, void* workspace,
+                           int64_t workspace_size, const kda_trace_t* trace, void* stream) {
     if (!trace) return KDA_ERR_NULL;
-    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, trace, stream);
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
+               trace, stream);
 }
 
 const char* kda_status_string(kda_status_t s) {
@@ -168,6 +191,7 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported configuration";
         case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scale must be finite and positive";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_fwd_workspace_size or misaligned";
     }
     return "KDA: unknown status";
 }

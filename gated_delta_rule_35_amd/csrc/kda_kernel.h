@@ -15,6 +15,8 @@ struct KdaParams {
     const float* h0;       // [N, Hv, 128, 128] or nullptr
     uint16_t* o;           // [tokens, Hv, 128] bf16 bits
     float* hT;             // [N, Hv, 128, 128] or nullptr
+    char* ws;              // [nslots, Hv] records of the intra kernel's results
+    int64_t nslots;        // ceil(total tokens / 64) + N
     int64_t T;             // tokens per sequence (fixed length) or total tokens (packed)
     int32_t N, Hq, Hv;
     int32_t beta_f32;
@@ -30,7 +32,13 @@ struct KdaParams {
     float* tr_h;
 };
 
-// Enqueues the fused forward kernel: N * Hv * dv_slices work-groups on `stream`.
-hipError_t launch_kda_fwd(const KdaParams& p, int dv_slices, bool trace, hipStream_t stream);
+// Workspace bytes for the given sizes (20 fp16 16x16 tiles per chunk slot and value head).
+int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
+
+// Intra-chunk kernel: one work-group per (chunk slot, value head), nslots * Hv in all.
+hipError_t launch_kda_intra(const KdaParams& p, bool trace, hipStream_t stream);
+
+// Scan kernel: N * Hv * dv_slices work-groups, each walking one sequence's chunks.
+hipError_t launch_kda_scan(const KdaParams& p, int dv_slices, bool trace, hipStream_t stream);
 
 }  // namespace kda

@@ -12,13 +12,19 @@
  *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
  *     o_t = scale * S_t^T q_t
  *
- * evaluated chunk by chunk (chunk length 64) in one fused HIP kernel.
+ * evaluated chunk by chunk (chunk length 64) by two HIP kernels: an
+ * intra-chunk kernel that runs every chunk at once (gate cumsum, the Aqk and
+ * Akk products, the fp32 inversion of I + Akk) and a scan kernel that walks
+ * each sequence's chunks in order (W/U recompute, state update, output).  The
+ * intra kernel hands its results to the scan kernel through a device
+ * workspace of kda_fwd_workspace_size() bytes (10 KiB per 64-token chunk slot
+ * and value head).
  *
  * Tensors are described by kda_tensor_t: a device pointer, a dtype, a rank
  * and per-dimension sizes and strides counted in elements.  All tensors must
  * be dense row-major (contiguous) and their data 16-byte aligned (beta and
- * cu_seqlens: aligned to their element size).  The caller owns all memory;
- * the library keeps no pointer after a call returns and allocates nothing.
+ * cu_seqlens: aligned to their element size).  The caller owns all memory it
+ * passes; the library keeps no pointer after a call returns.
  *
  * Shapes (B batch rows, T tokens per row, Hq query/key heads, Hv value heads,
  * head dimension 128):
@@ -67,8 +73,16 @@ typedef enum {
     KDA_ERR_LAYOUT = 4,      /* non-contiguous strides or misaligned data */
     KDA_ERR_UNSUPPORTED = 5, /* head dim != 128, Hv % Hq != 0, B != 1 with cu_seqlens, grid too large */
     KDA_ERR_VALUE = 6,       /* scale not finite or not > 0 */
-    KDA_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+    KDA_ERR_HIP = 7,         /* the HIP runtime reported an error at launch or allocation */
+    KDA_ERR_WORKSPACE = 8    /* workspace smaller than kda_fwd_workspace_size() or not 16-byte aligned */
 } kda_status_t;
+
+/*
+ * kda_fwd_workspace_size -- bytes of device workspace kda_fwd needs for a call
+ * with `total_tokens` = B * T tokens, N sequences and Hv value heads:
+ * (ceil(total_tokens / 64) + N) * Hv * 10240.  Returns -1 for a negative size.
+ */
+int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads);
 
 /*
  * kda_fwd -- the KDA forward pass over a batch.
@@ -81,6 +95,11 @@ typedef enum {
  * element has exactly one writer and a fixed reduction order).
  * initial_state may alias final_state (each state tile is read before it is
  * written, by the same work-group).
+ * workspace: device memory of at least kda_fwd_workspace_size() bytes,
+ * 16-byte aligned, owned by the caller and not used by anything else until the
+ * call's work on `stream` has finished; its contents need no initialisation.
+ * With workspace == NULL the library allocates it with hipMallocAsync on
+ * `stream` and releases it with hipFreeAsync after the two launches.
  * cu_seqlens must be non-decreasing with cu_seqlens[0] = 0 and
  * cu_seqlens[N] <= T.  That is a precondition the host cannot check without a
  * device read; the kernel clamps every sequence to [0, T) so that malformed
@@ -93,7 +112,8 @@ typedef enum {
 kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                      const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                      const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
-                     const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
+                     const kda_tensor_t* out, const kda_tensor_t* final_state,
+                     void* workspace, int64_t workspace_size, void* stream);
 
 /*
  * Optional fp32 dumps of the chunked method's intermediates, for stage-by-stage
@@ -123,20 +143,21 @@ typedef struct {
 
 /*
  * kda_fwd_trace -- kda_fwd plus the dumps above (a test and debugging entry; the
- * same kernel with the extra stores compiled in).  Same arguments, checks and
+ * same kernels with the extra stores compiled in).  Same arguments, checks and
  * results as kda_fwd; `trace` may not be NULL.
  */
 kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                            const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                            const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
                            const kda_tensor_t* out, const kda_tensor_t* final_state,
+                           void* workspace, int64_t workspace_size,
                            const kda_trace_t* trace, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status_t status);
 
-/* Number of dv slices (work-groups per sequence and value head) that kda_fwd
- * launches for N sequences and Hv value heads: 2 or 4. */
+/* Number of dv slices (scan work-groups per sequence and value head) that
+ * kda_fwd launches for N sequences and Hv value heads: 2 or 4. */
 int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads);
 
 #ifdef __cplusplus

@@ -56,10 +56,10 @@ def good(B=1, T_=64, Hq=2, Hv=2, beta_dtype=binding.KDA_F32):
                 out=T([B, T_, Hv, 128]))
 
 
-def call(lib, a, scale=0.088, cu=None, h0=None, hT=None):
+def call(lib, a, scale=0.088, cu=None, h0=None, hT=None, ws=None, ws_size=0):
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
     return lib.kda_fwd(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")),
-                       scale, r(cu), r(h0), r(a.get("out")), r(hT), None)
+                       scale, r(cu), r(h0), r(a.get("out")), r(hT), ws, ws_size, None)
 
 
 def expect(lib, a, name, **kw):
@@ -161,5 +161,26 @@ def test_trace_requires_descriptor(lib):
     a = good()
     r = ctypes.byref
     st = lib.kda_fwd_trace(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["beta"]), 0.1, None, None,
-                           r(a["out"]), None, None, None)
+                           r(a["out"]), None, None, 0, None, None)
     assert binding.STATUS_NAMES[st] == "KDA_ERR_NULL"
+
+
+def test_workspace_size(lib):
+    # one 10 KiB record per (64-token slot, value head); N extra slots for the
+    # partial chunks sequences may start mid-slot
+    assert lib.kda_fwd_workspace_size(2 * 8192, 2, 64) == (256 + 2) * 64 * 10240
+    assert lib.kda_fwd_workspace_size(16384, 14, 64) == (256 + 14) * 64 * 10240
+    assert lib.kda_fwd_workspace_size(1, 1, 1) == 2 * 10240
+    assert lib.kda_fwd_workspace_size(0, 0, 64) == 0
+    assert lib.kda_fwd_workspace_size(-1, 1, 1) == -1
+
+
+def test_workspace_checked_before_launch(lib):
+    a = good(B=2, T_=100, Hv=4)
+    need = lib.kda_fwd_workspace_size(200, 2, 4)
+    expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
+    expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE + 8, ws_size=need)
+    # the workspace is checked after the tensors
+    b = good(B=2, T_=100, Hv=4)
+    b["q"] = T([2, 100, 2, 64])
+    expect(lib, b, "KDA_ERR_UNSUPPORTED", ws=FAKE, ws_size=0)

@@ -244,6 +244,38 @@ def test_two_streams_match_serial_runs():
         assert torch.equal(ob[1].view(torch.int32), rb[1].view(torch.int32))
 
 
+def test_workspace_choices_are_bitwise_identical():
+    """Library-allocated (stream-ordered), caller-provided oversized and a reused
+    dirty workspace all give the same bits."""
+    from gated_delta_rule_35_amd import kda_fwd_workspace_size
+    _say("workspace variants B=2 H=8 T=333")
+    x = make_inputs(2, 333, 4, 8, torch.float32, h0=True, seed=91)
+    d = to_device(x)
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o2, h2 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True,
+                     workspace=False)
+    size = kda_fwd_workspace_size(2 * 333, 2, 8)
+    ws = torch.full((size + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
+    o3, h3 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    for o, h in ((o2, h2), (o3, h3)):
+        assert torch.equal(o.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(h.view(torch.int32), h1.view(torch.int32))
+
+
+def test_many_sequences_random_lengths():
+    """37 packed sequences with lengths 0..200 (several empty, several exact
+    multiples of 64): the chunk-slot search and the per-sequence scans."""
+    g = torch.Generator().manual_seed(101)
+    lens = torch.randint(0, 201, (37,), generator=g).tolist()
+    lens[3], lens[10], lens[20], lens[21] = 0, 64, 128, 0
+    cu = cu_from_lengths(lens)
+    _say(f"37 sequences, total {int(cu[-1])} tokens, H=3")
+    x = make_inputs(1, int(cu[-1]), 3, 3, torch.float32, h0=True, N=len(lens), seed=102)
+    check_against_oracle(x, cu, label="37 sequences")
+
+
 # ---- the named workloads at their full sizes, checked on sampled heads ----
 
 FULL = [
