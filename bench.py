@@ -3,17 +3,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one kda_fwd call over the whole batch of the workload (default: B=2,
-H=64, T=8192, dk=dv=128, chunk 64, fp32 beta, initial state ~ 0.1 N(0,1)), with
-all inputs and outputs already resident in HBM.  The K timed steps are bracketed
-by device synchronisation; every launch is also bracketed by HIP events on the
-stream it runs on, which gives the kernel's average duration for the roofline.
+A step is one KDA forward over the whole batch of the workload (default: B=2,
+H=64, T=8192, dk=dv=128, chunk 64, fp32 beta, initial state ~ 0.1 N(0,1)) with
+all inputs, outputs and the workspace already resident in HBM: the two kernels
+of kda_fwd, launched through its two stage entry points (kda_fwd_intra, then
+kda_fwd_scan, which together are exactly kda_fwd) so that HIP events on the
+launch stream bracket each kernel.  The K timed steps are bracketed by device
+synchronisation; value = tokens / wall time per step.
 
-Roofline (HBM-bound kernel): algorithmic bytes per launch = q, k, v, g, beta read
-once, o written once, the initial state read (if any) and the final state
-written; achieved = bytes / average launch duration, against 8 TB/s.  The MFMA
-side uses the algorithmic flop count of the chunked method (4,512,416 MAC per
-full 64-token chunk and value head).
+Roofline (HBM-bound): the forward's algorithmic bytes (q, k, v, g, beta read
+once, o written once, the initial state read if given, the final state
+written) divided by the summed average durations of the two kernels, against
+8 TB/s.  Each kernel is also reported against its own algorithmic bytes (what
+it must move in this design: the intra kernel reads q, k, g, beta and writes
+one 10 KiB record per chunk and value head; the scan kernel reads q, k, g, v
+and the records and writes o and the states).  The MFMA side uses the
+algorithmic flop count of the chunked method (4,512,416 MAC per full 64-token
+chunk and value head).
 
 cpu_baseline: the fp64 CPU oracle (token recurrence, OpenMP over sequence x head)
 timed on a bounded sample of the same workload, scaled to tokens/s of the full
@@ -33,7 +39,14 @@ METRIC = "KDA fwd tokens/s (B=2,H=64,d=128,T=8192); ms/call; % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 MAC_PER_CHUNK_HEAD = 4_512_416
-KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_35_amd", "csrc", "kda_fwd_kernel.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_35_amd", "csrc", f)
+                  for f in ("kda_intra.hip", "kda_scan.hip", "kda_device.h", "kda_kernel.h")]
+RECORD_BYTES = 10240   # workspace record per (chunk, value head)
+# The pages' own time for this exact workload ("cuLA PR #131: SM100/SM103 KDA
+# forward to pure CuTeDSL", Performance table, fp32 beta, T=8192, B=2, H=64,
+# CuTeDSL column), measured on NVIDIA SM100/SM103: context, not the target.
+PAGES_MS = {"mha_b2_h64_t8192": 0.8564}
+KERNELS = ("kda_intra_kernel", "kda_scan_kernel")
 
 
 def log(msg):
@@ -50,13 +63,27 @@ def chunk_heads(lengths, Hv, C=64):
     return sum((L + C - 1) // C for L in lengths) * Hv
 
 
+def kernel_bytes(n_tok, n_ch, N, Hq, Hv, beta_bytes, has_h0, d=128):
+    """Algorithmic bytes of each kernel (n_ch = chunk-heads)."""
+    qk = n_tok * Hq * d * 2 * 2
+    g = n_tok * Hv * d * 4
+    v = o = n_tok * Hv * d * 2
+    b = n_tok * Hv * beta_bytes
+    states = N * Hv * d * d * 4 * (2 if has_h0 else 1)
+    rec = n_ch * RECORD_BYTES
+    return {"kda_intra_kernel": qk + g + b + rec, "kda_scan_kernel": qk + g + v + rec + o + states}
+
+
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def load_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+    """HBM bytes per launch of each kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_kda_fwd_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -93,7 +120,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from gated_delta_rule_35_amd import kda_fwd, kda_dv_slices
+    from gated_delta_rule_35_amd import kda_fwd_intra, kda_fwd_scan, kda_fwd_workspace_size, kda_dv_slices
     from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
@@ -108,44 +135,67 @@ def main():
     cu_d = cu.to(dev) if cu is not None else None
     out = torch.empty_like(d["v"])
     hT = torch.empty((N, w.Hv, 128, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda_fwd_workspace_size(B * T, N, w.Hv), dtype=torch.uint8, device=dev)
     scale = w.scale
+    stream = torch.cuda.current_stream(dev)
 
-    def step():
-        kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
-                out=out, final_state=hT)
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kda_fwd_intra(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
+                      out=out, final_state=hT)
+        if ev:
+            ev[1].record(stream)
+        kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
+                     out=out, final_state=hT)
+        if ev:
+            ev[2].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
+        step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    intra_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    scan_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    t_intra = sum(intra_ms) / len(intra_ms) / 1e3
+    t_scan = sum(scan_ms) / len(scan_ms) / 1e3
+    t_kern = t_intra + t_scan
     ms_per_step = wall / args.steps * 1e3
     tokens_per_s = n_tok / (ms_per_step / 1e3)
-    log(f"{ms_per_step:.4f} ms/step (wall), kernel avg {avg_launch_s * 1e3:.4f} ms, "
-        f"min {min(launch_ms):.4f} ms, {tokens_per_s / 1e6:.2f} M tokens/s")
+    log(f"{ms_per_step:.4f} ms/step (wall); intra kernel avg {t_intra * 1e3:.4f} ms (min {min(intra_ms):.4f}), "
+        f"scan kernel avg {t_scan * 1e3:.4f} ms (min {min(scan_ms):.4f}); {tokens_per_s / 1e6:.2f} M tokens/s")
 
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
-    flops = 2 * MAC_PER_CHUNK_HEAD * chunk_heads(lengths, w.Hv)
-    achieved_gbs = nbytes / avg_launch_s / 1e9
+    n_ch = chunk_heads(lengths, w.Hv)
+    flops = 2 * MAC_PER_CHUNK_HEAD * n_ch
+    kbytes = kernel_bytes(n_tok, n_ch, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
     traffic = load_traffic(w.name)
+    kt = {"kda_intra_kernel": t_intra, "kda_scan_kernel": t_scan}
+    kernels = {}
+    for name in KERNELS:
+        a = kbytes[name] / kt[name] / 1e9
+        kernels[name] = {"ms_avg": round(kt[name] * 1e3, 5), "algorithmic_bytes": kbytes[name],
+                         "achieved": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
+                         "traffic": traffic.get(name) if traffic else None}
+    achieved_gbs = nbytes / t_kern / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    mfma = {"achieved": round(flops / avg_launch_s / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(flops / avg_launch_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": sum(traffic[k] for k in KERNELS) if traffic else None,
+                "scope": "whole forward: algorithmic bytes of the forward over the summed average durations of "
+                         "kda_intra_kernel and kda_scan_kernel",
+                "kernels": kernels}
+    mfma = {"achieved": round(flops / t_kern / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / t_kern / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "algorithmic_flop_per_launch": flops}
 
     cpu = None
@@ -178,7 +228,10 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": (round(tokens_per_s / (n_tok / (PAGES_MS[w.name] / 1e3)), 4) if w.name in PAGES_MS else None),
+        "vs_baseline_ref": (f"pages' CuTeDSL forward {PAGES_MS[w.name]} ms for this workload on NVIDIA SM100/SM103 "
+                            f"({n_tok / (PAGES_MS[w.name] / 1e3):.0f} tokens/s); another machine, context only"
+                            if w.name in PAGES_MS else None),
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "N_sequences": N, "tokens": n_tok, "Hq": w.Hq, "Hv": w.Hv,
@@ -186,9 +239,8 @@ def main():
                    "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0),
                    "dv_slices": kda_dv_slices(N, w.Hv), "mfma_operands": "f16", "accumulate": "f32",
                    "io": "bf16 q/k/v/o, f32 g/state"},
-        "kernel_ms_avg": round(avg_launch_s * 1e3, 5),
-        "kernel_ms_min": round(min(launch_ms), 5),
-        "algorithmic_bytes_per_launch": nbytes,
+        "kernel_ms_avg": round(t_kern * 1e3, 5),
+        "algorithmic_bytes_per_step": nbytes,
         "roofline": roofline,
         "mfma": mfma,
         "cpu_baseline": cpu,

@@ -21,7 +21,8 @@ KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
-EXPORTED = ["kda_fwd", "kda_fwd_trace", "kda_fwd_workspace_size", "kda_status_string", "kda_dv_slices"]
+EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_workspace_size",
+            "kda_status_string", "kda_dv_slices"]
 
 
 class KdaTensor(ctypes.Structure):
@@ -58,6 +59,9 @@ def load_library(path=None):
     lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p, ctypes.c_int64,
                             ctypes.c_void_p]
     lib.kda_fwd.restype = ctypes.c_int
+    for name in ("kda_fwd_intra", "kda_fwd_scan"):
+        getattr(lib, name).argtypes = lib.kda_fwd.argtypes
+        getattr(lib, name).restype = ctypes.c_int
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
@@ -138,7 +142,8 @@ def _workspace(workspace, q, v, cu_seqlens, stream):
     return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace):
+def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace,
+          entry="kda_fwd"):
     lib = load_library()
     tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
     for t in tensors:
@@ -150,7 +155,7 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
     args = [_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]), float(scale),
             _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8]), ws_ptr, ws_size]
     if trace is None:
-        _check(lib, lib.kda_fwd(*args, s))
+        _check(lib, getattr(lib, entry)(*args, s))
     else:
         tr = KdaTrace(**{n: (t.data_ptr() if t is not None else None) for n, t in trace.items()})
         _check(lib, lib.kda_fwd_trace(*args, ctypes.byref(tr), s))
@@ -170,6 +175,22 @@ def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=No
         final_state = torch.empty((n, v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=v.device)
     _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace)
     return out, final_state
+
+
+def kda_fwd_intra(q, k, v, g, beta, scale, workspace, cu_seqlens=None, initial_state=None, out=None,
+                  final_state=None, stream=None):
+    """First kernel of kda_fwd: fills `workspace` (a uint8 device tensor of at
+    least kda_fwd_workspace_size() bytes)."""
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace,
+          "kda_fwd_intra")
+
+
+def kda_fwd_scan(q, k, v, g, beta, scale, workspace, cu_seqlens=None, initial_state=None, out=None,
+                 final_state=None, stream=None):
+    """Second kernel of kda_fwd: reads `workspace` (filled by kda_fwd_intra with
+    the same arguments) and writes `out` and `final_state`."""
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace,
+          "kda_fwd_scan")
 
 
 def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state=None, out=None,

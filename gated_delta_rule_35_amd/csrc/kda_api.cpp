@@ -18,6 +18,7 @@
 namespace {
 
 constexpr int64_t kHeadDim = 128;
+constexpr int kIntra = 1, kScan = 2, kBoth = 3;   // which kernels a call launches
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;  // 512 threads each: a grid stays below 2^31 work-items
 
 int64_t numel(const kda_tensor_t* t) {
@@ -59,7 +60,7 @@ bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
 kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                  const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
                  const kda_tensor_t* out, const kda_tensor_t* hT, void* workspace, int64_t workspace_size,
-                 const kda_trace_t* trace, void* stream) {
+                 const kda_trace_t* trace, int stages, void* stream) {
     kda_status_t st;
     if ((st = check_tensor(q, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
     if ((st = check_tensor(k, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
@@ -101,6 +102,7 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     const int64_t ws_need = kda::workspace_bytes(B * T, N, Hv);
     if (workspace && (workspace_size < ws_need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
         return KDA_ERR_WORKSPACE;
+    if (!workspace && stages != kBoth) return KDA_ERR_WORKSPACE;   // a lone stage needs the caller's workspace
 
     kda::KdaParams p{};
     p.q = static_cast<const uint16_t*>(q->data);
@@ -137,8 +139,8 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (!ws && T > 0 && hipMallocAsync(&ws, (size_t)ws_need, hs) != hipSuccess) return KDA_ERR_HIP;
     p.ws = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
-    if (T > 0) e = kda::launch_kda_intra(p, trace != nullptr, hs);
-    if (e == hipSuccess) e = kda::launch_kda_scan(p, S, trace != nullptr, hs);
+    if (T > 0 && (stages & kIntra)) e = kda::launch_kda_intra(p, trace != nullptr, hs);
+    if (e == hipSuccess && (stages & kScan)) e = kda::launch_kda_scan(p, S, trace != nullptr, hs);
     if (!workspace && ws && hipFreeAsync(ws, hs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     if (e != hipSuccess) return KDA_ERR_HIP;
     if (std::getenv("KDA_DEBUG_SYNC")) {
@@ -168,7 +170,25 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
                      const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
                      void* workspace, int64_t workspace_size, void* stream) {
     return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
-               nullptr, stream);
+               nullptr, kBoth, stream);
+}
+
+kda_status_t kda_fwd_intra(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state, void* workspace,
+                           int64_t workspace_size, void* stream) {
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
+               nullptr, kIntra, stream);
+}
+
+kda_status_t kda_fwd_scan(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                          const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                          const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                          const kda_tensor_t* out, const kda_tensor_t* final_state, void* workspace,
+                          int64_t workspace_size, void* stream) {
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
+               nullptr, kScan, stream);
 }
 
 kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
@@ -178,7 +198,7 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
                            int64_t workspace_size, const kda_trace_t* trace, void* stream) {
     if (!trace) return KDA_ERR_NULL;
     return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
-               trace, stream);
+               trace, kBoth, stream);
 }
 
 const char* kda_status_string(kda_status_t s) {

@@ -14,7 +14,7 @@
 //
 // Each work-group writes one workspace record: the lower 16x16 tiles of Aqk and
 // of T diag(beta), in fp16 (the precision in which the scan kernel's MFMAs
-// consume them).  Two work-groups share a CU, so one's loads and inversion
+// consume them), staged in LDS and stored with 16-byte writes at the end.  Two work-groups share a CU, so one's loads and inversion
 // latency overlap the other's factor and MFMA work.
 //
 // Per-channel decay inside MFMA products.  exp(G_i - G_j) is factored through
@@ -51,7 +51,8 @@ struct IntraLds {
     static constexpr int TtD = T16 + 64 * S72 * 2;         // 4 diagonal T blocks, column-major
     static constexpr int T1t = TtD + 4 * 16 * TS * 4;      // T_10, T_32 (and their A T products)
     static constexpr int Xt = T1t + 2 * 16 * TS * 4;       // 4 blocks of the 32x32 step
-    static constexpr int LATE_END = Xt + 4 * 16 * TS * 4;
+    static constexpr int Aqk16 = Xt + 4 * 16 * TS * 4;     // [64][72] fp16 Aqk
+    static constexpr int LATE_END = Aqk16 + 64 * S72 * 2;
     static constexpr int Xch = PREP_END;                   // 3 x [4][128] fp32 half-block sums
     static constexpr int Beta = Xch + 3 * 4 * 128 * 4;     // [64] fp32
     static constexpr int Flag = Beta + 64 * 4;             // int: some block decays past the guard
@@ -147,14 +148,19 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
 
     // slot -> (sequence, chunk): the first slot of sequence n, floor(bos_n / 64) + n,
     // does not decrease with n; take the last sequence whose first slot is <= slot.
-    int lo = 0, hi = p.N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        int64_t b, l;
-        seq_bounds(p, mid, b, l);
-        if (chunk_slot(b, mid, 0) <= slot) lo = mid; else hi = mid - 1;
+    int n;
+    if (!p.cu && p.T % CH == 0) {
+        n = (int)(slot / (p.T / CH + 1));   // sequence n has slots n (T/64 + 1) .. + T/64 - 1
+    } else {
+        int lo = 0, hi = p.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            int64_t b, l;
+            seq_bounds(p, mid, b, l);
+            if (chunk_slot(b, mid, 0) <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
     }
-    const int n = lo;
     int64_t bos, len;
     seq_bounds(p, n, bos, len);
     const int64_t cidx = slot - chunk_slot(bos, n, 0);
@@ -350,31 +356,38 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
         }
     }
     lds_barrier();   // A32 overlaps the operand arrays
-    // Aqk tiles go straight to the workspace (the diagonal ones are rewritten
-    // exactly below for a guarded chunk); Akk tiles go to A32.
+    // Aqk tiles go to the fp16 staging tile Aqk16 (the diagonal ones are rewritten
+    // exactly below for a guarded chunk); Akk tiles go to A32.  Only diagonal
+    // tiles need the causal masks (I and J are uniform per wave).
+    _Float16* sAqk16 = reinterpret_cast<_Float16*>(smem + L::Aqk16);
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         if (jobM[u] >= 0) {
             const int I = jobI[u], J = jobJ[u];
             const int i = 16 * I + (lane & 15);
             const int j0 = 16 * J + 4 * (lane >> 4);
+            f32x4 v4 = iacc[u];
             if (jobM[u] == 0) {
-                if (!(guard && I == J)) {
-                    half4 h4;
+                v4 *= p.scale;
+                if (I == J) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h4[e] = (_Float16)((j0 + e <= i) ? p.scale * iacc[u][e] : 0.f);
-                    *reinterpret_cast<half4*>(rec + tri_index(I, J) * WS_TILE_BYTES + ((lane & 15) * 16 + 4 * (lane >> 4)) * 2) = h4;
+                    for (int e = 0; e < 4; ++e) v4[e] = (j0 + e <= i) ? v4[e] : 0.f;
                 }
+                half4 h4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h4[e] = (_Float16)v4[e];
+                *reinterpret_cast<half4*>(sAqk16 + i * S72 + j0) = h4;
                 if (TRACE && p.tr_Aqk && i < Lc) {
                     float* dst = p.tr_Aqk + ((tok0 + i) * p.Hv + hv) * CH + j0;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[e] = (j0 + e <= i) ? p.scale * iacc[u][e] : 0.f;
+                    for (int e = 0; e < 4; ++e) dst[e] = v4[e];
                 }
             } else {
-                const float bi = sBeta[i];
-                f32x4 v4;
+                v4 *= sBeta[i];
+                if (I == J) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = (j0 + e < i) ? bi * iacc[u][e] : 0.f;
+                    for (int e = 0; e < 4; ++e) v4[e] = (j0 + e < i) ? v4[e] : 0.f;
+                }
                 *reinterpret_cast<f32x4*>(smem + L::A32 + (i * S68 + j0) * 4) = v4;
             }
         }
@@ -416,7 +429,7 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
                     sk += bf2f(ki[c]) * kjv;
                 }
             }
-            reinterpret_cast<_Float16*>(rec + tri_index(B, B) * WS_TILE_BYTES)[m * 16 + nn] = (_Float16)(p.scale * sq);
+            sAqk16[i * S72 + j] = (_Float16)(p.scale * sq);
             if (nn <= m) sA32[i * S68 + j] = (nn < m) ? sBeta[i] * sk : 0.f;
             if (TRACE && p.tr_Aqk && nn <= m && i < Lc) p.tr_Aqk[((tok0 + i) * p.Hv + hv) * CH + j] = p.scale * sq;
         }
@@ -530,13 +543,20 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     }
     lds_barrier();
 
-    // T diag(beta): the 10 lower tiles to the workspace, 16 bytes per thread.
-    if (tid < 10 * 32) {
-        const int t = tid >> 5, r = (tid >> 1) & 15, h = tid & 1;
-        const int I = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-        const int J = t - I * (I + 1) / 2;
-        const uint4 w = *reinterpret_cast<const uint4*>(smem + L::T16 + ((16 * I + r) * S72 + 16 * J + 8 * h) * 2);
-        *reinterpret_cast<uint4*>(rec + (10 + t) * WS_TILE_BYTES + (r * 16 + 8 * h) * 2) = w;
+    // The workspace record: the 10 lower tiles of Aqk, then those of T diag(beta),
+    // in 16-byte pieces (640 in all).
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = tid + NTHREADS * u;
+        if (it < WS_RECORD_BYTES / 16) {
+            const int t = it >> 5, r = (it >> 1) & 15, h = it & 1;
+            const int tt = t % 10;
+            const int I = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+            const int J = tt - I * (I + 1) / 2;
+            const uint4 w = *reinterpret_cast<const uint4*>(smem + (t < 10 ? L::Aqk16 : L::T16) +
+                                                            ((16 * I + r) * S72 + 16 * J + 8 * h) * 2);
+            *reinterpret_cast<uint4*>(rec + it * 16) = w;
+        }
     }
 }
 

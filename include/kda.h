@@ -116,6 +116,27 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
                      void* workspace, int64_t workspace_size, void* stream);
 
 /*
+ * kda_fwd_intra, kda_fwd_scan -- the two kernels of kda_fwd as separate calls,
+ * for callers that schedule them apart (e.g. the next batch's intra kernel on
+ * another stream) or time them one by one.  kda_fwd_intra fills the workspace
+ * (gate cumsum, Aqk, Akk, the inversion); kda_fwd_scan reads it and writes out
+ * and final_state.  Both take kda_fwd's arguments and checks; the workspace is
+ * required (NULL gives KDA_ERR_WORKSPACE).  kda_fwd_intra followed by
+ * kda_fwd_scan with the same arguments, in stream order, gives exactly
+ * kda_fwd's results.
+ */
+kda_status_t kda_fwd_intra(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state,
+                           void* workspace, int64_t workspace_size, void* stream);
+kda_status_t kda_fwd_scan(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                          const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                          const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                          const kda_tensor_t* out, const kda_tensor_t* final_state,
+                          void* workspace, int64_t workspace_size, void* stream);
+
+/*
  * Optional fp32 dumps of the chunked method's intermediates, for stage-by-stage
  * checks of kda_fwd_trace.  Any pointer may be NULL.  Ttot = B * T.
  *   G     [Ttot, Hv, 128]  chunk-local inclusive cumsum of g

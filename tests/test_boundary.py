@@ -180,6 +180,12 @@ def test_workspace_checked_before_launch(lib):
     need = lib.kda_fwd_workspace_size(200, 2, 4)
     expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
     expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE + 8, ws_size=need)
+    # a lone stage needs the caller's workspace
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    for entry in (lib.kda_fwd_intra, lib.kda_fwd_scan):
+        st = entry(r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["beta"]), 0.088, None, None, r(a["out"]), None,
+                   None, 0, None)
+        assert binding.STATUS_NAMES[st] == "KDA_ERR_WORKSPACE"
     # the workspace is checked after the tensors
     b = good(B=2, T_=100, Hv=4)
     b["q"] = T([2, 100, 2, 64])

@@ -264,6 +264,28 @@ def test_workspace_choices_are_bitwise_identical():
         assert torch.equal(h.view(torch.int32), h1.view(torch.int32))
 
 
+def test_stage_calls_equal_kda_fwd_bitwise():
+    """kda_fwd_intra then kda_fwd_scan (the calls bench.py times) = kda_fwd."""
+    from gated_delta_rule_35_amd import kda_fwd_intra, kda_fwd_scan, kda_fwd_workspace_size
+    lens = [300, 0, 64, 129]
+    cu = cu_from_lengths(lens).cuda()
+    _say(f"stage calls vs kda_fwd, lengths={lens}, H=8")
+    x = make_inputs(1, 493, 4, 8, torch.float32, h0=True, N=4, seed=95)
+    d = to_device(x)
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu, initial_state=d["h0"],
+                     final_state=True)
+    ws = torch.empty(kda_fwd_workspace_size(493, 4, 8), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    h2 = torch.empty_like(h1)
+    kda_fwd_intra(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, ws, cu_seqlens=cu, initial_state=d["h0"],
+                  out=o2, final_state=h2)
+    kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, ws, cu_seqlens=cu, initial_state=d["h0"],
+                 out=o2, final_state=h2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
+
+
 def test_many_sequences_random_lengths():
     """37 packed sequences with lengths 0..200 (several empty, several exact
     multiples of 64): the chunk-slot search and the per-sequence scans."""
