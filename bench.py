@@ -16,8 +16,8 @@ once, o written once, the initial state read if given, the final state
 written) divided by the summed average durations of the two kernels, against
 8 TB/s.  Each kernel is also reported against its own algorithmic bytes (what
 it must move in this design: the intra kernel reads q, k, g, beta and writes
-one 10 KiB record per chunk and value head; the scan kernel reads q, k, g, v
-and the records and writes o and the states).  The MFMA side uses the
+one 59,904-byte record per chunk and value head; the scan kernel reads v and
+the records and writes o and the states).  The MFMA side uses the
 algorithmic flop count of the chunked method (4,512,416 MAC per full 64-token
 chunk and value head).
 
@@ -41,7 +41,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 MAC_PER_CHUNK_HEAD = 4_512_416
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_35_amd", "csrc", f)
                   for f in ("kda_intra.hip", "kda_scan.hip", "kda_device.h", "kda_kernel.h")]
-RECORD_BYTES = 10240   # workspace record per (chunk, value head)
+RECORD_BYTES = 61952   # workspace record per (chunk, value head)
 # The pages' own time for this exact workload ("cuLA PR #131: SM100/SM103 KDA
 # forward to pure CuTeDSL", Performance table, fp32 beta, T=8192, B=2, H=64,
 # CuTeDSL column), measured on NVIDIA SM100/SM103: context, not the target.
@@ -71,7 +71,7 @@ def kernel_bytes(n_tok, n_ch, N, Hq, Hv, beta_bytes, has_h0, d=128):
     b = n_tok * Hv * beta_bytes
     states = N * Hv * d * d * 4 * (2 if has_h0 else 1)
     rec = n_ch * RECORD_BYTES
-    return {"kda_intra_kernel": qk + g + b + rec, "kda_scan_kernel": qk + g + v + rec + o + states}
+    return {"kda_intra_kernel": qk + g + b + rec, "kda_scan_kernel": v + rec + o + states}
 
 
 def kernel_sha():

@@ -95,7 +95,7 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
     // Per-block byte offsets of the kernel's buffer loads are 32-bit.
     if (Hv > (int64_t(1) << 16) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
-    const int S = kda_dv_slices(N, Hv);
+    const int S = kda::scan_slices();
     if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
     const int64_t nslots = (B * T + 63) / 64 + N;
     if (nslots * Hv > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
@@ -140,7 +140,7 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     p.ws = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
     if (T > 0 && (stages & kIntra)) e = kda::launch_kda_intra(p, trace != nullptr, hs);
-    if (e == hipSuccess && (stages & kScan)) e = kda::launch_kda_scan(p, S, trace != nullptr, hs);
+    if (e == hipSuccess && (stages & kScan)) e = kda::launch_kda_scan(p, trace != nullptr, hs);
     if (!workspace && ws && hipFreeAsync(ws, hs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     if (e != hipSuccess) return KDA_ERR_HIP;
     if (std::getenv("KDA_DEBUG_SYNC")) {
@@ -155,9 +155,9 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
 extern "C" {
 
 int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads) {
-    // Two 64-wide dv slices per head fill the 256 CUs once N * Hv >= 128; below
-    // that, four 32-wide slices.
-    return num_sequences * num_value_heads >= 128 ? 2 : 4;
+    (void)num_sequences;
+    (void)num_value_heads;
+    return kda::scan_slices();   // 64-wide dv slices
 }
 
 int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads) {

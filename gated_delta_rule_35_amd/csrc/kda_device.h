@@ -87,11 +87,31 @@ __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 
 // Index of an off-diagonal 16x16 block pair (I > J) in 0..5.
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// Workspace record of one (chunk, value head): 20 fp16 tiles of 16x16, row-major
-// inside a tile: tiles 0..9 hold the lower tiles of Aqk, tiles 10..19 those of
-// T diag(beta), both in tri_index order.
-constexpr int WS_TILE_BYTES = 16 * 16 * 2;
-constexpr int WS_TILES = 20;
-constexpr int WS_RECORD_BYTES = WS_TILES * WS_TILE_BYTES;
+// Workspace record of one (chunk, value head): everything the scan kernel needs
+// of the chunk besides v, in the precision its MFMAs consume (fp16).  Apart from
+// e^{G_last}, it is a list of 1 KB operand fragments of v_mfma_f32_32x32x16_f16:
+// 64 lanes x 16 bytes, loaded by the scan kernel's waves straight into registers.
+// Fragment (m, kk) of a matrix X holds in lane l the eight elements
+// X[32 m + l % 32][16 kk + 8 (l / 32) + s], s = 0 .. 7, unless stated otherwise.
+//   WS_AQK  Aqk (scale included), the six lower fragments (m, kk): m = 0, kk < 2
+//           and m = 1, kk < 4; index frag_lt(m, kk)
+//   WS_T    T diag(beta), the same six, with the columns of each 16-wide k step
+//           taken in the order in which a 32x32 MFMA accumulator tile holds its
+//           rows: lane l holds columns 16 kk + 8 (s / 4) + 4 (l / 32) + s % 4
+//   WS_QG   scale q e^G (64 x 128), fragments (m, kk), m < 2, kk < 8; index 8 m + kk
+//   WS_KG   -(k e^G), likewise
+//   WS_KH   (k e^{G_last - G})^T (128 x 64), fragments (m, kk), m < 4, kk < 4;
+//           index 4 m + kk
+//   WS_GAM  e^{G_last}, [128] fp32
+constexpr int WS_FRAG = 64 * 16;
+__host__ __device__ constexpr int frag_lt(int m, int kk) { return m == 0 ? kk : 2 + kk; }
+constexpr int WS_AQK = 0;
+constexpr int WS_T = WS_AQK + 6 * WS_FRAG;
+constexpr int WS_QG = WS_T + 6 * WS_FRAG;
+constexpr int WS_KG = WS_QG + 16 * WS_FRAG;
+constexpr int WS_KH = WS_KG + 16 * WS_FRAG;
+constexpr int WS_GAM = WS_KH + 16 * WS_FRAG;
+constexpr int WS_RECORD_BYTES = WS_GAM + 128 * 4;
+static_assert(WS_RECORD_BYTES == 61952, "record size");
 
 }  // namespace kda

@@ -12,9 +12,12 @@
 //   a3  FP32 inversion   T = (I + Akk)^{-1}: diagonal 16x16 blocks by forward
 //                        substitution, the rest on fp32 MFMA
 //
-// Each work-group writes one workspace record: the lower 16x16 tiles of Aqk and
-// of T diag(beta), in fp16 (the precision in which the scan kernel's MFMAs
-// consume them), staged in LDS and stored with 16-byte writes at the end.  Two work-groups share a CU, so one's loads and inversion
+// Each work-group writes one workspace record, in fp16 (the precision in which
+// the scan kernel's MFMAs consume it): the lower 16x16 tiles of Aqk and of
+// T diag(beta) (staged in LDS, stored as 16-byte pieces at the end), and the
+// decayed operands scale q e^G, (k e^G)^T, (k e^{G_last - G})^T with e^{G_last}
+// (stored from registers as soon as the factors exist).  The scan kernel then
+// needs nothing of q, k and g.  Two work-groups share a CU, so one's loads and inversion
 // latency overlap the other's factor and MFMA work.
 //
 // Per-channel decay inside MFMA products.  exp(G_i - G_j) is factored through
@@ -106,14 +109,18 @@ __device__ __forceinline__ void trace_tblock(float* dst, int64_t tok0, int Lc, i
 }
 
 // Per-(block, channel) exponents, in log2 units, for the column block IB given
-// the four block sums tot: off = sum_{K < IB} tot_K, lamarg[d] =
-// sum_{IB < K < I2} tot_K + g_{b_I2} for I2 = IB + 1 + d (unused where I2 > 3).
+// the four block sums tot: off = sum_{K < IB} tot_K, tail = sum_{K > IB} tot_K,
+// lamarg[d] = sum_{IB < K < I2} tot_K + g_{b_I2} for I2 = IB + 1 + d (unused
+// where I2 > 3).
 template <int IB>
-__device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2 (&gI)[4], f32x2& off,
+__device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2 (&gI)[4], f32x2& off, f32x2& tail,
                                               f32x2 (&lamarg)[3]) {
     off = f32x2{0.f, 0.f};
 #pragma unroll
     for (int K = 0; K < IB; ++K) off += tot[K];
+    tail = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int K = 3; K > IB; --K) tail += tot[K];
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
@@ -124,6 +131,31 @@ __device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2
         } else {
             lamarg[d] = f32x2{-1000.f, -1000.f};   // unused; exp2 gives 0
         }
+    }
+}
+
+// 4x4 transpose of 32-bit words across each quad of lanes: on entry quad lane j
+// holds x[0..3]; on exit it holds x[p] = (x[j] of quad lane p).  A per-lane
+// rotation, three fixed quad permutations (DPP) and the inverse rotation.
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int j) {
+    const bool o1 = (j & 1) != 0, o2 = (j & 2) != 0;
+    uint32_t t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {   // t[k] = x[(k + j) % 4]
+        const uint32_t u = o1 ? x[(k + 1) & 3] : x[k];
+        const uint32_t w = o1 ? x[(k + 3) & 3] : x[(k + 2) & 3];
+        t[k] = o2 ? w : u;
+    }
+    // t[k] <- t[k] of quad lane (j - k) % 4; DPP quad_perm selectors [3,0,1,2],
+    // [2,3,0,1], [1,2,3,0].
+    t[1] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[1], 0x93, 0xf, 0xf, false);
+    t[2] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[2], 0x4e, 0xf, 0xf, false);
+    t[3] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[3], 0x39, 0xf, 0xf, false);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {   // x[p] = t[(j - p) % 4]
+        const uint32_t u = o1 ? t[(1 - p) & 3] : t[(0 - p) & 3];
+        const uint32_t w = o1 ? t[(3 - p) & 3] : t[(2 - p) & 3];
+        x[p] = o2 ? w : u;
     }
 }
 
@@ -249,9 +281,10 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
 
     // Factors of every row of this half block:
     //   F = e^{G_r - G_b}  (<= 1),  R = e^{G_e - G_r}  (<= 1)   (b, e: first, last row)
-    // and the per-(block, channel) scalars invr = e^{G_b - G_e}, lam[d] = e^{G_{b_I2} - G_e}.
+    // and the per-(block, channel) scalars invr = e^{G_b - G_e}, lam[d] = e^{G_{b_I2} - G_e},
+    // eb = e^{G_b}, khs = e^{G_last - G_e}.
     float F[8][2], R[8][2];
-    float invr[2], lam[3][2];
+    float invr[2], lam[3][2], eb[2], khs[2];
     int guard_local = 0;
     {
         const f32x2 xa = *reinterpret_cast<const f32x2*>(sXa + Ib * 128 + 2 * cp);
@@ -265,12 +298,17 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
             tot[K] = (gI[K] + a) + b;
         }
         // Ib is wave-uniform: one branch per wave, no per-lane selects.
-        f32x2 off, lamarg[3];
+        f32x2 off, tail, lamarg[3];
         switch (Ib) {
-            case 0: block_scalars<0>(tot, gI, off, lamarg); break;
-            case 1: block_scalars<1>(tot, gI, off, lamarg); break;
-            case 2: block_scalars<2>(tot, gI, off, lamarg); break;
-            default: block_scalars<3>(tot, gI, off, lamarg); break;
+            case 0: block_scalars<0>(tot, gI, off, tail, lamarg); break;
+            case 1: block_scalars<1>(tot, gI, off, tail, lamarg); break;
+            case 2: block_scalars<2>(tot, gI, off, tail, lamarg); break;
+            default: block_scalars<3>(tot, gI, off, tail, lamarg); break;
+        }
+        if (Ib == 0 && hh == 0) {
+            // e^{G_last} of the two channels
+            const f32x2 all = ((tot[0] + tot[1]) + tot[2]) + tot[3];
+            *reinterpret_cast<f32x2*>(rec + WS_GAM + 8 * cp) = f32x2{fexp2(all[0]), fexp2(all[1])};
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -283,6 +321,8 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
             }
             const float qb = xa[e] + xb[e];       // (G_e - G_b) log2 e of this block
             invr[e] = fexp2(-qb);                 // e^{G_b - G_e}
+            eb[e] = fexp2(off[e] + gI[Ib][e]);    // e^{G_b}
+            khs[e] = fexp2(tail[e]);              // e^{G_last - G_e}
             if (-qb > GUARD_DECAY * LOG2E) guard_local = 1;
             if constexpr (TRACE) {
                 if (p.tr_G) {
@@ -320,6 +360,45 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
                 const int o2 = swz(16 * pair_index(I2, Ib) + (row & 15), 2 * cp);
                 *reinterpret_cast<uint32_t*>(smem + L::Bo + o2) = pack_h2(kr0 * lam[d][0], kr1 * lam[d][1]);
             }
+        }
+    }
+    // The scan kernel's operands of this chunk, straight to the record.  scale q e^G
+    // and -(k e^G) go out as 16-byte row pieces of 8 channels, gathered from the
+    // four lanes of a quad; (k e^{G_last - G})^T per channel as its eight rows.
+    {
+        const float sq0 = p.scale * eb[0], sq1 = p.scale * eb[1];
+        uint32_t qg[8], kg[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const float k0 = bf_lo(kw[rr]), k1 = bf_hi(kw[rr]);
+            qg[rr] = pack_h2(bf_lo(qw[rr]) * F[rr][0] * sq0, bf_hi(qw[rr]) * F[rr][1] * sq1);
+            kg[rr] = pack_h2(-(k0 * F[rr][0] * eb[0]), -(k1 * F[rr][1] * eb[1]));
+        }
+        const int qa = cp >> 2, qj = cp & 3;   // quad: channels 8 qa .. 8 qa + 7
+#pragma unroll
+        for (int b4 = 0; b4 < 2; ++b4) {
+            uint32_t xq[4] = {qg[4 * b4], qg[4 * b4 + 1], qg[4 * b4 + 2], qg[4 * b4 + 3]};
+            uint32_t xk[4] = {kg[4 * b4], kg[4 * b4 + 1], kg[4 * b4 + 2], kg[4 * b4 + 3]};
+            quad_transpose(xq, qj);
+            quad_transpose(xk, qj);
+            // row 8 hb + 4 b4 + qj, channels 8 qa ..: fragment (row / 32, qa / 2), lane row % 32 + 32 (qa % 2)
+            const int row = 8 * hb + 4 * b4 + qj;
+            const int fo = ((row >> 5) * 8 + (qa >> 1)) * WS_FRAG + ((row & 31) + 32 * (qa & 1)) * 16;
+            *reinterpret_cast<uint4*>(rec + WS_QG + fo) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+            *reinterpret_cast<uint4*>(rec + WS_KG + fo) = make_uint4(xk[0], xk[1], xk[2], xk[3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            half8 kh;
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const float kx = e ? bf_hi(kw[rr]) : bf_lo(kw[rr]);
+                kh[rr] = (_Float16)(kx * R[rr][e] * khs[e]);
+            }
+            // channel c, rows 8 hb ..: fragment (c / 32, hb / 2), lane c % 32 + 32 (hb % 2)
+            const int c = 2 * cp + e;
+            const int fo = ((c >> 5) * 4 + (hb >> 1)) * WS_FRAG + ((c & 31) + 32 * (hb & 1)) * 16;
+            *reinterpret_cast<half8*>(rec + WS_KH + fo) = kh;
         }
     }
     lds_barrier();
@@ -442,6 +521,15 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
         }
     }
 
+    // The fragments include the upper 16x16 tiles (0,1) and (2,3) of Aqk and T:
+    // zero them in the staging tiles (waves 2..7 are idle in the first inversion step).
+    if (tid >= 128 && tid < 128 + 4 * 32) {
+        const int it = tid - 128, w = it >> 5, r = (it >> 1) & 15, h = it & 1;
+        const int blk = w & 1;   // tile (0,1) or (2,3)
+        *reinterpret_cast<uint4*>(smem + ((w >> 1) ? L::T16 : L::Aqk16) +
+                                  ((32 * blk + r) * S72 + 32 * blk + 16 + 8 * h) * 2) = make_uint4(0, 0, 0, 0);
+    }
+
     // ================= a3: T = (I + Akk)^{-1} in fp32 =================
     // Three barrier-separated steps.  T diag(beta) goes into T16 (fp16), written
     // by whichever wave produces each block.
@@ -543,18 +631,23 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     }
     lds_barrier();
 
-    // The workspace record: the 10 lower tiles of Aqk, then those of T diag(beta),
-    // in 16-byte pieces (640 in all).
+    // The record's Aqk and T diag(beta) fragments (six each, 768 16-byte pieces;
+    // the T columns in accumulator row order, two 8-byte runs per piece).
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int it = tid + NTHREADS * u;
-        if (it < WS_RECORD_BYTES / 16) {
-            const int t = it >> 5, r = (it >> 1) & 15, h = it & 1;
-            const int tt = t % 10;
-            const int I = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-            const int J = tt - I * (I + 1) / 2;
-            const uint4 w = *reinterpret_cast<const uint4*>(smem + (t < 10 ? L::Aqk16 : L::T16) +
-                                                            ((16 * I + r) * S72 + 16 * J + 8 * h) * 2);
+        if (it < 12 * 64) {
+            const int f = it >> 6, l = it & 63, ff = f % 6;
+            const int m = ff < 2 ? 0 : 1, kk = ff < 2 ? ff : ff - 2;
+            const int rowo = (32 * m + (l & 31)) * S72 + 16 * kk;
+            uint4 w;
+            if (f < 6) {
+                w = *reinterpret_cast<const uint4*>(smem + L::Aqk16 + (rowo + 8 * (l >> 5)) * 2);
+            } else {
+                const uint2 lo = *reinterpret_cast<const uint2*>(smem + L::T16 + (rowo + 4 * (l >> 5)) * 2);
+                const uint2 hi = *reinterpret_cast<const uint2*>(smem + L::T16 + (rowo + 8 + 4 * (l >> 5)) * 2);
+                w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
             *reinterpret_cast<uint4*>(rec + it * 16) = w;
         }
     }

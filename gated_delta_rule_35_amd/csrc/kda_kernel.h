@@ -32,13 +32,15 @@ struct KdaParams {
     float* tr_h;
 };
 
-// Workspace bytes for the given sizes (20 fp16 16x16 tiles per chunk slot and value head).
+// Workspace bytes for the given sizes (one record per chunk slot and value head).
 int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
 
 // Intra-chunk kernel: one work-group per (chunk slot, value head), nslots * Hv in all.
 hipError_t launch_kda_intra(const KdaParams& p, bool trace, hipStream_t stream);
 
-// Scan kernel: N * Hv * dv_slices work-groups, each walking one sequence's chunks.
-hipError_t launch_kda_scan(const KdaParams& p, int dv_slices, bool trace, hipStream_t stream);
+// Scan kernel: N * Hv * scan_slices() work-groups, each walking one sequence's chunks
+// for one slice of the value head's dv columns.
+int scan_slices();
+hipError_t launch_kda_scan(const KdaParams& p, bool trace, hipStream_t stream);
 
 }  // namespace kda

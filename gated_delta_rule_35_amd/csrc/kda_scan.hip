@@ -1,117 +1,128 @@
 // State-dependent stages of the KDA chunked forward for gfx950 (MI355X, CDNA4).
 //
-// One work-group of 512 threads (8 wave64s) owns one (sequence, value head,
-// dv slice) and walks that sequence's chunks of 64 tokens in order.  Per chunk
-// it runs the stages that depend on the recurrent state ("cuLA PR #131:
+// One work-group of four wave64s owns one (sequence, value head, 64-wide dv
+// slice) and walks that sequence's chunks of 64 tokens in order.  Per chunk it
+// runs the stages that depend on the recurrent state ("cuLA PR #131:
 // SM100/SM103 KDA forward to pure CuTeDSL", Summary: recompute W/U; "cuLA
 // REPO_LAYOUT.md", ops/: chunk delta-H and forward output):
 //
-//   a1  gate cumsum     G = chunk-local inclusive cumsum of g (fp32)
-//   a4  W/U recompute   W = T (beta k e^G), U = T (beta v)                 (MFMA)
-//   a5  delta-H scan    v_new = U - W h;
-//                       h <- Diag(e^{G_last}) h + (k e^{G_last - G})^T v_new
-//   a6  output          o = (scale q e^G) h + Aqk v_new                     (MFMA)
+//   a4+a5  v_new = U - W h  with  W = T diag(beta) (k e^G),  U = T diag(beta) v,
+//          evaluated as  v_new = T diag(beta) (v - (k e^G) h)
+//          h <- Diag(e^{G_last}) h + (k e^{G_last - G})^T v_new
+//   a6     o = (scale q e^G) h + Aqk v_new
 //
-// Aqk and T diag(beta) come from the intra kernel's workspace record of the
-// chunk.  The state slice h (128 x DV, fp32) lives in MFMA accumulator
-// registers for the whole sequence.  MFMA operands are fp16, accumulation is
-// fp32; o is rounded to bf16 once.
+// Everything state-independent comes from the intra kernel's workspace record of
+// the chunk, stored as MFMA operand fragments.  The work-group copies each record
+// once into LDS by DMA (buffer loads that write LDS directly), two chunks ahead,
+// double-buffered; every wave then reads its fragments from there.  v comes the
+// same way, one chunk ahead.  The kernel reads only v and the records from
+// memory, and writes o and the final state; its loops hold no loads into
+// registers, so every wait for memory is an explicit, counted one.
 //
-// Software pipeline.  The gate cumsum and the decay factors of a chunk
-// (q e^G, k e^G, k e^{G_last - G}: the kernel's main vector-ALU load) do not
-// depend on the state, so they are computed one chunk ahead, inside the
-// previous chunk's MFMA phases, and held in registers until their chunk
-// starts.  q, k and g are loaded two chunks ahead into two register sets used
-// in turn (the chunk loop is unrolled by two), one third per phase; v and the
-// workspace record one chunk ahead.  Per chunk, four barrier-separated phases:
-//   C  stage this chunk's operands in LDS; store the previous chunk's output;
-//      load the next chunk's v and workspace record
-//   D  W^T and U on MFMA                 | gate sums of the next chunk; g of chunk + 2
-//   E  v_new on MFMA                     | factors of the next chunk, rows 0-3; q of chunk + 2
-//   F  o and the state update on MFMA    | factors of the next chunk, rows 4-7; k of chunk + 2
-// and the fp16 copy of the new state for the next chunk's MFMAs.
+// Roles.  Two wave pairs, each owning 32 dv columns.  A pair's state h (128 x 32,
+// fp32) is split by rows between its two waves, which keep their 32 x 32 tiles
+// in MFMA accumulators for the whole sequence; only fp16 copies of h and v_new
+// cross between them, through LDS.  Per chunk:
+//   chain wave:   Z = v - (k e^G) h  (MFMA, accumulators start from v);
+//                 v_new = T diag(beta) Z, its B operand taken straight from Z's
+//                 accumulator registers (the record's T columns are in
+//                 accumulator row order); v_new^T -> LDS
+//   output wave:  o^T = h^T (scale q e^G)^T, the state-only part of o
+//   barrier; the record DMA of chunk + 2 into the buffer just read
+//   both:         own state rows h <- e^{G_last} h + Khat^T v_new; fp16 h^T -> LDS
+//   barrier
+//   output wave:  o^T += v_new^T Aqk^T; o stored (bf16) straight from the
+//                 accumulators, four channels per lane store
+// All products run on v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulate).
 #include "kda_device.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int S136 = 136;    // fp16 rows of 128 (+8 pad)
-constexpr int S72 = 72;      // fp16 rows of 64 (+8 pad)
+constexpr int SCAN_THREADS = 256;   // four waves: two (chain, output) pairs
+constexpr int DVW = 32;             // dv columns per pair
+constexpr int PAIRS = 2;
+constexpr int SLICES = DK / (DVW * PAIRS);                   // work-groups per (sequence, head)
+constexpr int REC_PIECES = (WS_RECORD_BYTES + WS_FRAG - 1) / WS_FRAG;   // 1 KB DMA pieces of a record
+constexpr int REC_LDS = REC_PIECES * WS_FRAG;
+constexpr int S136 = 136;           // fp16 rows of 128 (+8 pad)
+constexpr int S72 = 72;             // 16-bit rows of 64 (+8 pad)
 
-template <int DV>
 struct ScanLds {
-    static constexpr int Qg = 0;                          // [64][136] fp16, q e^G
-    static constexpr int KgT = Qg + 64 * S136 * 2;         // [128][72] fp16, (k e^G)^T
-    static constexpr int KhT = KgT + 128 * S72 * 2;        // [128][72] fp16, (k e^{G_last - G})^T
-    static constexpr int Vt = KhT + 128 * S72 * 2;         // [DV][72] fp16, v^T
-    static constexpr int T16 = Vt + DV * S72 * 2;          // [64][72] fp16, T diag(beta)
-    static constexpr int Aqk = T16 + 64 * S72 * 2;         // [64][72] fp16
-    static constexpr int W = Aqk + 64 * S72 * 2;           // [64][136] fp16, -W
-    static constexpr int VnT = W + 64 * S136 * 2;          // [DV][72] fp16, v_new^T
-    static constexpr int HT = VnT + DV * S72 * 2;          // [DV][136] fp16, h^T
-    static constexpr int Ost = HT + DV * S136 * 2;         // [64][DV+8] bf16 output of the previous chunk
-    static constexpr int Xs = Ost + 64 * (DV + 8) * 2;     // [8][128] fp32 sums of g over each wave's 8 rows
-    static constexpr int Gam = Xs + 8 * 128 * 4;           // [128] fp32 e^{G_last}
-    static constexpr int BYTES = Gam + 128 * 4;
+    static constexpr int Rec = 0;                          // [2][REC_LDS] records of two chunks
+    static constexpr int Pair = 2 * REC_LDS;               // then, per pair:
+    static constexpr int HT = 0;                           //   [32][136] fp16 h^T (dv column x key)
+    static constexpr int VnT = HT + DVW * S136 * 2;        //   [32][72] fp16 v_new^T (dv column x token)
+    static constexpr int Vs = VnT + DVW * S72 * 2;         //   [64][32] bf16 v of the next chunk (DMA)
+    static constexpr int PAIR_BYTES = Vs + CH * DVW * 2;
+    static constexpr int BYTES = Pair + PAIRS * PAIR_BYTES;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// One chunk's q, k and g in the factor layout: lane = channel pair (channels
-// 2 lane, 2 lane + 1), wave = rows 8 wave .. 8 wave + 7.
-struct InRegs {
-    float g[8][2];
-    uint32_t q[8], k[8];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Decay factors of one chunk in the same layout, as fp16: q e^G for rows rr
-// (two channels per word), and per channel the eight rows of k e^G and
-// k e^{G_last - G}.
-struct FacRegs {
-    uint32_t qg[8];
-    half8 kg[2], kh[2];
-    f32x2 gam;   // e^{G_last} of the two channels
-};
+__device__ __forceinline__ f32x16 mfma32(half8 a, half8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Accumulator registers 8j .. 8j+7 of a 32x32 tile as an fp16 B operand: rows
+// 16 j + 8 (s / 4) + 4 (lane / 32) + s % 4 of the tile, the column order of the
+// record's T fragments.
+__device__ __forceinline__ half8 acc_to_b(const f32x16& a, int j) {
+    half8 h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) h[s] = (_Float16)a[8 * j + s];
+    return h;
+}
+
+// fp16 element (row i, column j) of the record's T diag(beta) fragments (zero
+// above the 32x32 diagonal blocks); trace dumps only.
+__device__ __forceinline__ float rec_t(const char* rec, int i, int j) {
+    const int m = i >> 5, kk = j >> 4, jj = j & 15;
+    if (m == 0 && kk >= 2) return 0.f;
+    const int hh = (jj >> 2) & 1, s = ((jj >> 3) << 2) | (jj & 3);
+    const int off = WS_T + frag_lt(m, kk) * WS_FRAG + ((i & 31) + 32 * hh) * 16 + 2 * s;
+    return (float)*reinterpret_cast<const _Float16*>(rec + off);
+}
+// fp16 element (row i, channel c) of the record's -(k e^G) fragments.
+__device__ __forceinline__ float rec_kg(const char* rec, int i, int c) {
+    const int off = WS_KG + ((i >> 5) * 8 + (c >> 4)) * WS_FRAG + ((i & 31) + 32 * ((c >> 3) & 1)) * 16 + 2 * (c & 7);
+    return (float)*reinterpret_cast<const _Float16*>(rec + off);
+}
 
 }  // namespace
 
-template <int DV, bool TRACE>
-__global__ void __launch_bounds__(NTHREADS, 1) kda_scan_kernel(const KdaParams p) {
-    using L = ScanLds<DV>;
-    constexpr int S = DK / DV;          // dv slices
-    constexpr int NU = 2 * (DV / 32);   // 32x32 tiles of a 64 x DV matrix
-    constexpr int NH = 4 * (DV / 32);   // 32x32 tiles of the 128 x DV state (at most one per wave)
-    static_assert(NH <= 8, "one state tile per wave");
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+template <bool TRACE>
+__global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaParams p) {
+    using L = ScanLds;
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int pr = wave >> 1, role = wave & 1;   // pair; role 0: chain, 1: output
+    const int hl = lane >> 5, cl = lane & 31;
+    char* const ps = smem + L::Pair + pr * L::PAIR_BYTES;   // this pair's LDS
 
-    // tid and lane are re-made opaque at the top of every chunk (see `chunk`), so
-    // the compiler recomputes the LDS addresses derived from them per chunk
-    // instead of hoisting hundreds of them out of the loop into registers.
-    int tid = threadIdx.x;
-    int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform, kept in an SGPR
-
-    // Work-group -> (sequence, value head, slice).  Slices of one head go to the
-    // same XCD (work-groups are dealt to the 8 XCDs round robin), so their
-    // duplicate q/k/g reads meet in that XCD's L2.
+    // Work-group -> (sequence, value head, slice).  The slices of one head go to
+    // the same XCD (work-groups are dealt to the 8 XCDs round robin), so their
+    // duplicate record reads meet in that XCD's L2.
     const int npairs = p.N * p.Hv;
     int pair, s;
     if ((npairs & 7) == 0) {
         const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
-        pair = (loc / S) * 8 + x;
-        s = loc % S;
+        pair = (loc / SLICES) * 8 + x;
+        s = loc % SLICES;
     } else {
-        pair = blockIdx.x / S;
-        s = blockIdx.x % S;
+        pair = blockIdx.x / SLICES;
+        s = blockIdx.x % SLICES;
     }
-    const int n = pair / p.Hv, hv = pair % p.Hv, hq = hv / (p.Hv / p.Hq);
+    const int n = pair / p.Hv, hv = pair % p.Hv;
     int64_t bos, len;
     seq_bounds(p, n, bos, len);
     const int64_t nch = (len + CH - 1) / CH;
-    const int64_t qk_tok = (int64_t)p.Hq * DK;   // token stride of q, k
-    const int64_t v_tok = (int64_t)p.Hv * DK;    // token stride of v, g, o
-    const int dv0 = s * DV;
-    const int64_t slot0 = chunk_slot(bos, n, 0);
+    const int64_t v_tok = (int64_t)p.Hv * DK;   // token stride of v, o
+    const int dv0 = (PAIRS * s + pr) * DVW;     // this pair's dv columns
+    const int64_t slot0 = chunk_slot(bos, n, 0);   // record slot of chunk c: slot0 + c
 
     int64_t trace_chunk = 0;   // index of this sequence's first chunk in the h dump
     if (TRACE && p.tr_h) {
@@ -126,486 +137,331 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_scan_kernel(const KdaParams p
         }
     }
 
-    // State tile of this wave: rows c = 32 ct .., columns d = 32 dt .. of h (128 x DV).
-    const bool has_h = wave < NH;
-    const int h_ct = wave / (DV / 32), h_dt = wave % (DV / 32);
-    f32x16 hacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) hacc[r] = 0.f;
-    if (has_h && p.h0) {
-        const float* src = p.h0 + ((int64_t)n * p.Hv + hv) * DK * DK + dv0 + 32 * h_dt + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) hacc[r] = src[(int64_t)(32 * h_ct + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * DK];
-    }
-    // fp16 copy of h^T in LDS (the B / A operand of the state's MFMAs).
-    auto write_ht = [&]() {
-        if (has_h) {
-            const int d = 32 * h_dt + (lane & 31);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                half4 h4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h4[e] = (_Float16)hacc[4 * q4 + e];
-                *reinterpret_cast<half4*>(smem + L::HT + (d * S136 + 32 * h_ct + 8 * q4 + 4 * (lane >> 5)) * 2) = h4;
-            }
-        }
-    };
-    write_ht();
-    // Upper 16x16 tiles of T16 and Aqk are zero (the MFMAs read some of them);
-    // the chunk loop writes only the lower tiles.
-    for (int it = tid; it < 2 * 6 * 32; it += NTHREADS) {
-        const int mtx = it / 192, tile = (it / 32) % 6, w32 = it & 31;
-        const int I = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-        const int J = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-        const int m = w32 >> 1, h = w32 & 1;
-        *reinterpret_cast<uint4*>(smem + (mtx ? L::Aqk : L::T16) + ((16 * I + m) * S72 + 16 * J + 8 * h) * 2) =
-            make_uint4(0, 0, 0, 0);
-    }
-
-    // Loop-invariant per-lane offsets, computed once from threadIdx.x (the
-    // opaque tid below would make the compiler recompute them every chunk).
-    // Workspace record pieces: 16 bytes each, tid and tid + 512 (< 640).
-    int ws_dst[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int it = (int)threadIdx.x + NTHREADS * u;
-        const int t = it >> 5, r = (it >> 1) & 15, h = it & 1;
-        const int tt = t % 10;
-        const int I = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-        const int J = tt - I * (I + 1) / 2;
-        ws_dst[u] = (t < 10 ? L::Aqk : L::T16) + ((16 * I + r) * S72 + 16 * J + 8 * h) * 2;
-    }
-    // Output pieces: row i, 8 channels c8 of the slice.
-    constexpr int OPT = (CH * DV / 8 + NTHREADS - 1) / NTHREADS;
-    int o_row[OPT], o_lds[OPT], o_glb[OPT];
-#pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-        const int it = (int)threadIdx.x + NTHREADS * u;
-        const int i = it / (DV / 8), c8 = it % (DV / 8);
-        o_row[u] = it < CH * DV / 8 ? i : CH;   // CH: no piece
-        o_lds[u] = L::Ost + (i * (DV + 8) + 8 * c8) * 2;
-        o_glb[u] = (int)((i * v_tok + 8 * c8) * 2);
-    }
-
-    float* sXs = reinterpret_cast<float*>(smem + L::Xs);
-    float* sGam = reinterpret_cast<float*>(smem + L::Gam);
-
-    // ---- loads ----
-    // Raw buffer loads: a wave-uniform descriptor (scalar base and byte range) and
-    // per-lane 32-bit offsets.  Rows past the sequence end, and whole chunks past
-    // it, fall outside the range and read as zero without touching memory, so the
-    // loads of later chunks need no branches.
     auto chunk_rows = [&](int64_t c) -> int {   // valid rows of chunk c (0 past the end)
         const int64_t r = len - c * CH;
         return r <= 0 ? 0 : (r >= CH ? CH : (int)r);
     };
-    // part 0: g rows, 1: q rows, 2: k rows.
-    auto load_inputs = [&](InRegs& in, int64_t c, int part) {
-        const int Lc = chunk_rows(c);
-        const int nr = Lc - 8 * wave < 0 ? 0 : (Lc - 8 * wave > 8 ? 8 : Lc - 8 * wave);
-        const int64_t t0 = bos + c * CH + 8 * wave;
-        if (part == 0) {
-            const __amdgpu_buffer_rsrc_t rg =
-                make_rsrc(p.g + t0 * v_tok + (int64_t)hv * DK, nr ? ((nr - 1) * v_tok + DK) * 4 : 0);
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                const i32x2 g2 = __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * lane + (int)(rr * v_tok * 4), 0, 0);
-                in.g[rr][0] = __int_as_float(g2[0]);
-                in.g[rr][1] = __int_as_float(g2[1]);
-            }
-        } else {
-            const uint16_t* base = part == 1 ? p.q : p.k;
-            const __amdgpu_buffer_rsrc_t r =
-                make_rsrc(base + t0 * qk_tok + (int64_t)hq * DK, nr ? ((nr - 1) * qk_tok + DK) * 2 : 0);
-            uint32_t* dst = part == 1 ? in.q : in.k;
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr)
-                dst[rr] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, 4 * lane + (int)(rr * qk_tok * 2), 0, 0);
-        }
-    };
-    // v: thread (jp, cg) = (tid % 32, tid / 32) holds tokens 2 jp and 2 jp + 1 of
-    // channels 4 cg .. 4 cg + 3.
-    uint2 pf_v[2];
-    uint4 pf_w[2];
-    auto load_v_ws = [&](int64_t c) {
-        const int v_jp = tid & 31, v_cg = tid >> 5;
-        const bool v_act = v_cg < DV / 4;
-        const int v_off = (int)((2 * v_jp * v_tok + 4 * v_cg) * 2);
-        const int Lc = chunk_rows(c);
-        const int64_t t0 = bos + c * CH;
-        const __amdgpu_buffer_rsrc_t rv =
-            make_rsrc(p.v + t0 * v_tok + (int64_t)hv * DK + dv0, Lc ? ((Lc - 1) * v_tok + DV) * 2 : 0);
-        pf_v[0] = make_uint2(0, 0);
-        pf_v[1] = make_uint2(0, 0);
-        if (v_act) {
-            const i32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0);
-            const i32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rv, v_off + (int)(v_tok * 2), 0, 0);
-            pf_v[0] = make_uint2((uint32_t)a[0], (uint32_t)a[1]);
-            pf_v[1] = make_uint2((uint32_t)b[0], (uint32_t)b[1]);
-        }
-        const __amdgpu_buffer_rsrc_t rw =
-            make_rsrc(p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES, Lc ? WS_RECORD_BYTES : 0);
-        const i32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * tid, 0, 0);
-        pf_w[0] = make_uint4((uint32_t)w0[0], (uint32_t)w0[1], (uint32_t)w0[2], (uint32_t)w0[3]);
-        pf_w[1] = make_uint4(0, 0, 0, 0);
-        if (tid < WS_RECORD_BYTES / 16 - NTHREADS) {
-            const i32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * (tid + NTHREADS), 0, 0);
-            pf_w[1] = make_uint4((uint32_t)w1[0], (uint32_t)w1[1], (uint32_t)w1[2], (uint32_t)w1[3]);
-        }
-    };
-    static_assert(WS_RECORD_BYTES / 16 > NTHREADS && WS_RECORD_BYTES / 16 <= 2 * NTHREADS, "two pieces per thread");
 
-    // ---- decay factors (state independent) ----
-    // Per token and channel E = e^{g} = 2^{g log2 e}; the factors are running
-    // products of E (one exponential per element instead of two):
-    //   e^{G_r}          = e^{G at the end of the earlier waves' rows} * prod_{s <= r} E_s
-    //   e^{G_last - G_r} = e^{G_last - G at the end of this wave's rows} * prod_{r < s <= 7} E_s
-    // The cross-wave parts come from the waves' sums of g log2 e, exchanged in Xs.
-    float ex[8][2];
-    auto gate_sums = [&](const InRegs& in) {
-        f32x2 tot = {0.f, 0.f};
+    // ---- record DMA ----
+    // Chunk c's record into LDS buffer b: 1 KB pieces, piece i by wave i % 4, lane l's
+    // 16 bytes to byte 16 l of the piece.  Past the record's end, and for chunks past
+    // the sequence end, the range check makes the DMA write zeros.  The loads are
+    // issued as inline assembly (M0 = LDS address) so that the compiler, which cannot
+    // tell them apart from the fragment reads of the other buffer, adds no waits;
+    // their completion is awaited explicitly before the barrier that publishes them.
+    constexpr int DMA_PER_WAVE = (REC_PIECES + 3) / 4;
+    const uint32_t lds_rec = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem + L::Rec);
+    auto dma_record = [&](int64_t c, int b) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES,
+                                                   chunk_rows(c) ? WS_RECORD_BYTES : 0);
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float x = in.g[rr][e] * LOG2E;
-                tot[e] += x;
-                ex[rr][e] = fexp2(x);
+        for (int u = 0; u < DMA_PER_WAVE; ++u) {
+            const int i = wave + 4 * u;
+            if (i < REC_PIECES) {
+                const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + i * WS_FRAG);
+                const int voff = i * WS_FRAG + lane * 16;
+                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(r)
+                             : "memory");
             }
         }
-        *reinterpret_cast<f32x2*>(sXs + wave * 128 + 2 * lane) = tot;
     };
-    // Running products: pg = e^{G} of the last row done, ph = e^{G_last - G} of row 3
-    // (rows 0-3) or row 7 (rows 4-7).
-    f32x2 pg;
-    auto gate_offsets = [&](FacRegs& f) {
-        f32x2 x[8];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) x[w] = *reinterpret_cast<const f32x2*>(sXs + w * 128 + 2 * lane);
-        // prefix over the earlier waves; wave is uniform, so this is one scalar branch
-        f32x2 off = {0.f, 0.f}, mine;
-        switch (wave) {
-#define KDA_OFF_CASE(W)                                      \
-            case W:                                          \
-                _Pragma("unroll") for (int w = 0; w < W; ++w) off += x[w]; \
-                mine = x[W];                                 \
-                break;
-            KDA_OFF_CASE(0) KDA_OFF_CASE(1) KDA_OFF_CASE(2) KDA_OFF_CASE(3)
-            KDA_OFF_CASE(4) KDA_OFF_CASE(5) KDA_OFF_CASE(6)
-            default:
-#pragma unroll
-                for (int w = 0; w < 7; ++w) off += x[w];
-                mine = x[7];
-                break;
-#undef KDA_OFF_CASE
-        }
-        const f32x2 all = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-        pg = f32x2{fexp2(off[0]), fexp2(off[1])};
-        f.gam = f32x2{fexp2(all[0]), fexp2(all[1])};
-        return f32x2{fexp2(all[0] - off[0] - mine[0]), fexp2(all[1] - off[1] - mine[1])};   // e^{G_last - G_7}
-    };
-    // Rows r0 .. r0+3 of the factors: Qg = q e^G (scale is applied to the o
-    // accumulator), Kg = k e^G, Kh = k e^{G_last - G}.  ph enters as
-    // e^{G_last - G_{r0+3}}.
-    auto factors = [&](const InRegs& in, FacRegs& f, int r0, f32x2 ph) {
-        f32x2 eh[4];
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-            eh[j] = ph;
-            if (j > 0) ph *= f32x2{ex[r0 + j][0], ex[r0 + j][1]};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = r0 + j;
-            pg *= f32x2{ex[rr][0], ex[rr][1]};
-            const float q0 = bf_lo(in.q[rr]), q1 = bf_hi(in.q[rr]);
-            const float k0 = bf_lo(in.k[rr]), k1 = bf_hi(in.k[rr]);
-            f.qg[rr] = pack_h2(q0 * pg[0], q1 * pg[1]);
-            f.kg[0][rr] = (_Float16)(k0 * pg[0]);
-            f.kg[1][rr] = (_Float16)(k1 * pg[1]);
-            f.kh[0][rr] = (_Float16)(k0 * eh[j][0]);
-            f.kh[1][rr] = (_Float16)(k1 * eh[j][1]);
-        }
-    };
-    // e^{G_last - G_3} from e^{G_last - G_7}: times E of rows 4..7.
-    auto ph_rows03 = [&](f32x2 ph7) {
-#pragma unroll
-        for (int rr = 4; rr < 8; ++rr) ph7 *= f32x2{ex[rr][0], ex[rr][1]};
-        return ph7;
+    // DMA pieces this wave issues per chunk: the count of memory operations a
+    // wait must let stay in flight to cover one chunk's DMA.
+    const int dma_mine = (REC_PIECES - wave + 3) / 4;
+    auto frag = [&](int b, int off) -> half8 {
+        return *reinterpret_cast<const half8*>(smem + L::Rec + b * REC_LDS + off + lane * 16);
     };
 
-    // Output rows staged in Ost: 16-byte pieces, whole row segments per lane group.
-    auto store_output = [&](int64_t t0, int rows) {
-        char* base = reinterpret_cast<char*>(p.o + t0 * v_tok + (int64_t)hv * DK + dv0);
+    // State tiles of this wave: rows (keys) 32 t .. 32 t + 31, t = 2 role + tt, of the
+    // pair's slice h[:, dv0 .. dv0 + 31].  Accumulator register r of a tile holds key
+    // 32 t + 8 (r / 4) + 4 hl + r % 4, column cl.
+    f32x16 hacc[2];
 #pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-            if (o_row[u] < rows)
-                *reinterpret_cast<uint4*>(base + o_glb[u]) = *reinterpret_cast<const uint4*>(smem + o_lds[u]);
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[tt][r] = 0.f;
+        if (p.h0) {
+            const float* src = p.h0 + ((int64_t)n * p.Hv + hv) * DK * DK + dv0;
+            const int lo = cl + 4 * hl * DK;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) hacc[tt][r] = src[lo + (32 * (2 * role + tt) + 8 * (r >> 2) + (r & 3)) * DK];
         }
-    };
-
-    InRegs in0, in1;
-    FacRegs fac;
-    if (nch > 0) {
-        // Prologue: chunk 0's factors; chunk 1's q, k, g in flight.
-        for (int part = 0; part < 3; ++part) load_inputs(in0, 0, part);
-        load_v_ws(0);
-        for (int part = 0; part < 3; ++part) load_inputs(in1, 1, part);
-        gate_sums(in0);
-        lds_barrier();
-        const f32x2 ph7 = gate_offsets(fac);
-        factors(in0, fac, 0, ph_rows03(ph7));
-        factors(in0, fac, 4, ph7);
     }
+    // fp16 h^T in LDS: this wave's rows, four consecutive keys per 8-byte store.
+    auto write_ht = [&]() {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                half4 h4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h4[e] = (_Float16)hacc[tt][4 * q4 + e];
+                *reinterpret_cast<half4*>(ps + L::HT + (cl * S136 + 32 * (2 * role + tt) + 8 * q4 + 4 * hl) * 2) = h4;
+            }
+        }
+    };
+    // h as MFMA operand, k step kk (keys 16 kk + 8 hl + 0..7 of column cl): the B
+    // operand of (k e^G) h and, identically, the A operand of h^T (q e^G)^T.
+    half8 hf[8];
+    auto read_ht = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) hf[kk] = lds_h8(ps, L::HT + (cl * S136 + 16 * kk + 8 * hl) * 2);
+    };
 
-    // One chunk.  `fr` held this chunk's inputs (consumed: it receives chunk c + 2);
-    // `nx` holds chunk c + 1's, whose factors are computed here.
-    auto chunk = [&](int64_t c, InRegs& fr, InRegs& nx) __attribute__((always_inline)) {
-        asm volatile("" : "+v"(tid), "+v"(lane));
-        const int64_t tok0 = bos + c * CH;
+    // v of chunk c (the pair's 32 columns) into the pair's Vs by DMA (chain wave):
+    // four 1 KB pieces, lane l of piece u taking token 16 u + l / 4, channels
+    // 8 (l % 4) .. + 7, so Vs is row-major [token][32].  Rows past the sequence end
+    // fall outside the range and arrive as zeros.
+    const uint32_t lds_vs = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ps + L::Vs);
+    auto dma_v = [&](int64_t c) {
         const int Lc = chunk_rows(c);
-        const bool more = c + 1 < nch;
-
-        if (TRACE && p.tr_h && has_h) {
-            const int d = dv0 + 32 * h_dt + (lane & 31);
-            float* dst = p.tr_h + ((trace_chunk + c) * p.Hv + hv) * DK * DK;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (bos + c * CH) * v_tok + (int64_t)hv * DK + dv0,
+                                                    Lc ? ((Lc - 1) * v_tok + DVW) * 2 : 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dst[(int64_t)(32 * h_ct + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * DK + d] = hacc[r];
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_vs + u * WS_FRAG);
+            const int voff = (int)(((16 * u + (lane >> 2)) * v_tok + 8 * (lane & 3)) * 2);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(rv)
+                         : "memory");
         }
+    };
 
-        // ================= C: stage this chunk's operands =================
+    write_ht();
+    if (nch > 0) {
+        dma_record(0, 0);
+        dma_record(1, 1);
+        if (role == 0) dma_v(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();   // h^T, the first two records and the first chunk's v complete
+    read_ht();
+
+    auto trace_chunk_start = [&](int64_t c, int64_t tok0, int Lc) {
+        if (p.tr_h) {
+            float* dst = p.tr_h + ((trace_chunk + c) * p.Hv + hv) * DK * DK + dv0 + cl;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-            *reinterpret_cast<uint32_t*>(smem + L::Qg + ((8 * wave + rr) * S136 + 2 * lane) * 2) = fac.qg[rr];
+            for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            *reinterpret_cast<half8*>(smem + L::KgT + ((2 * lane + e) * S72 + 8 * wave) * 2) = fac.kg[e];
-            *reinterpret_cast<half8*>(smem + L::KhT + ((2 * lane + e) * S72 + 8 * wave) * 2) = fac.kh[e];
-        }
-        if (wave == 0) *reinterpret_cast<f32x2*>(sGam + 2 * lane) = fac.gam;
-        const int v_jp = tid & 31, v_cg = tid >> 5;
-        if (v_cg < DV / 4) {
-            // v^T: channel 4 cg + e, tokens 2 jp and 2 jp + 1 as one 32-bit word.
-            const uint32_t a[2] = {pf_v[0].x, pf_v[0].y}, b[2] = {pf_v[1].x, pf_v[1].y};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = (e & 1) ? bf_hi(a[e >> 1]) : bf_lo(a[e >> 1]);
-                const float x1 = (e & 1) ? bf_hi(b[e >> 1]) : bf_lo(b[e >> 1]);
-                *reinterpret_cast<uint32_t*>(smem + L::Vt + ((4 * v_cg + e) * S72 + 2 * v_jp) * 2) = pack_h2(x0, x1);
+                for (int r = 0; r < 16; ++r)
+                    dst[(int64_t)(32 * (2 * role + tt) + 8 * (r >> 2) + 4 * hl + (r & 3)) * DK] = hacc[tt][r];
             }
         }
-        // Aqk and T diag(beta): the 20 lower 16x16 tiles of the workspace record.
-        *reinterpret_cast<uint4*>(smem + ws_dst[0]) = pf_w[0];
-        if (tid < WS_RECORD_BYTES / 16 - NTHREADS) *reinterpret_cast<uint4*>(smem + ws_dst[1]) = pf_w[1];
-        // The previous chunk's output goes out after this chunk's v and workspace
-        // registers are consumed and before they are reloaded: global stores share
-        // the vmcnt counter with loads, so every wait for loaded data stays clear of
-        // pending stores.
-        if (c > 0) store_output(tok0 - CH, CH);
-        load_v_ws(c + 1);
-        lds_barrier();
-
-        // ================= D: W^T = (k e^G)^T (T diag beta)^T, U = T diag(beta) v =================
-        {
-            const int ct = wave >> 1, it = wave & 1;  // W^T tile: rows c (32ct..), cols i (32it..)
-            f32x16 acc;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 || it == 1) {              // T is lower triangular
-                    const int ko = 16 * kk + 8 * (lane >> 5);
-                    const half8 a = lds_h8(smem, L::KgT + ((32 * ct + (lane & 31)) * S72 + ko) * 2);
-                    const half8 b = lds_h8(smem, L::T16 + ((32 * it + (lane & 31)) * S72 + ko) * 2);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
-                }
+        // W = T diag(beta) (k e^G) and U = T diag(beta) v from the record's fp16
+        // values, element by element (the kernel itself never forms them).
+        const char* rec = p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES;
+        if (p.tr_W && s == 0 && pr == 0) {
+            for (int it = threadIdx.x & 127; it < CH * DK; it += 128) {
+                const int i = it / DK, ch = it % DK;
+                if (i >= Lc) continue;
+                float acc = 0.f;
+                for (int j = 0; j < CH; ++j) acc += rec_t(rec, i, j) * -rec_kg(rec, j, ch);
+                p.tr_W[((tok0 + i) * p.Hv + hv) * DK + ch] = acc;
             }
-            const int i = 32 * it + (lane & 31);
+        }
+        if (p.tr_U) {
+            for (int it = threadIdx.x & 127; it < CH * DVW; it += 128) {
+                const int i = it / DVW, d = it % DVW;
+                if (i >= Lc) continue;
+                float acc = 0.f;
+                for (int j = 0; j < Lc; ++j)
+                    acc += rec_t(rec, i, j) *
+                           (float)(_Float16)bf2f(p.v[(tok0 + j) * v_tok + (int64_t)hv * DK + dv0 + d]);
+                p.tr_U[((tok0 + i) * p.Hv + hv) * DK + dv0 + d] = acc;
+            }
+        }
+    };
+    // Decay of this wave's state rows by e^{G_last} (from the record in LDS).
+    auto decay_state = [&](int b) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int cc = 32 * ct + 8 * q4 + 4 * (lane >> 5);
-                half4 h4;
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(smem + L::Rec + b * REC_LDS + WS_GAM +
+                                                                 (32 * (2 * role + tt) + 8 * q4 + 4 * hl) * 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h4[e] = (_Float16)(-acc[4 * q4 + e]);
-                *reinterpret_cast<half4*>(smem + L::W + (i * S136 + cc) * 2) = h4;
-                if (TRACE && p.tr_W && s == 0 && i < Lc) {
-                    float* dst = p.tr_W + ((tok0 + i) * p.Hv + hv) * DK + cc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[e] = acc[4 * q4 + e];
-                }
+                for (int e = 0; e < 4; ++e) hacc[tt][4 * q4 + e] *= gm[e];
             }
         }
-        f32x16 uacc;
-        const int tu_it = wave / (DV / 32), tu_dt = wave % (DV / 32);
-        if (wave < NU) {
+    };
+    half8 fkh[8];   // Khat^T fragments of this wave's state rows: (tt, kk) at 4 tt + kk
+    half8 vf[4];    // v_new operand, k step kk: tokens 16 kk + 8 hl + 0..7 of column cl
+    // After the first barrier: the record DMA of chunk c + 2 into buffer b; the state
+    // update h <- e^{G_last} h + Khat^T v_new of this wave's rows (the output wave
+    // also stages the next chunk's v^T); the fp16 h^T copy; the second barrier.
+    auto update_state = [&](int64_t c, int b) {
+        dma_record(c + 2, b);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) uacc[e] = 0.f;
+        for (int kk = 0; kk < 4; ++kk) vf[kk] = lds_h8(ps, L::VnT + (cl * S72 + 16 * kk + 8 * hl) * 2);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 || tu_it == 1) {
-                    const int ko = 16 * kk + 8 * (lane >> 5);
-                    const half8 a = lds_h8(smem, L::T16 + ((32 * tu_it + (lane & 31)) * S72 + ko) * 2);
-                    const half8 b = lds_h8(smem, L::Vt + ((32 * tu_dt + (lane & 31)) * S72 + ko) * 2);
-                    uacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, uacc, 0, 0, 0);
-                }
-            }
-            if (TRACE && p.tr_U) {
-                const int d = dv0 + 32 * tu_dt + (lane & 31);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int i = 32 * tu_it + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (i < Lc) p.tr_U[((tok0 + i) * p.Hv + hv) * DK + d] = uacc[e];
-                }
-            }
+        for (int kk = 0; kk < 4; ++kk) {
+            hacc[0] = mfma32(fkh[kk], vf[kk], hacc[0]);
+            hacc[1] = mfma32(fkh[4 + kk], vf[kk], hacc[1]);
         }
-        if (more) gate_sums(nx);
-        load_inputs(fr, c + 2, 0);
-        lds_barrier();
-
-        // ================= E: v_new = U - W h;  (q e^G) h for o =================
-        if (wave < NU) {
-            // Two independent accumulation chains (even / odd k steps) halve the
-            // dependent MFMA latency; they are summed once at the end.
-            f32x16 acc = uacc, acc1;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc1[e] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 8; kk += 2) {
-                const int ko = 16 * kk + 8 * (lane >> 5);
-                const half8 a0 = lds_h8(smem, L::W + ((32 * tu_it + (lane & 31)) * S136 + ko) * 2);
-                const half8 b0 = lds_h8(smem, L::HT + ((32 * tu_dt + (lane & 31)) * S136 + ko) * 2);
-                const half8 a1 = lds_h8(smem, L::W + ((32 * tu_it + (lane & 31)) * S136 + ko + 16) * 2);
-                const half8 b1 = lds_h8(smem, L::HT + ((32 * tu_dt + (lane & 31)) * S136 + ko + 16) * 2);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc1, 0, 0, 0);
-            }
-            acc += acc1;
-            const int d = 32 * tu_dt + (lane & 31);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int i = 32 * tu_it + 8 * q4 + 4 * (lane >> 5);
-                half4 h4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h4[e] = (_Float16)acc[4 * q4 + e];
-                *reinterpret_cast<half4*>(smem + L::VnT + (d * S72 + i) * 2) = h4;
-                if (TRACE && p.tr_vnew) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (i + e < Lc) p.tr_vnew[((tok0 + i + e) * p.Hv + hv) * DK + dv0 + d] = acc[4 * q4 + e];
-                }
-            }
-        }
-        // o^T = h^T (q e^G)^T scale + v_new^T Aqk^T: the first term needs only the
-        // state entering the chunk, so waves 8 - NU .. 7 (idle in the v_new MFMAs)
-        // take it here; the second follows in F.
-        const int wo = 7 - wave;
-        const int o_it = wo / (DV / 32), o_dt = wo % (DV / 32);
-        f32x16 oacc;
-        if (wo < NU) {
-            f32x16 acc1;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) { oacc[e] = 0.f; acc1[e] = 0.f; }
-#pragma unroll
-            for (int kk = 0; kk < 8; kk += 2) {
-                const int ko = 16 * kk + 8 * (lane >> 5);
-                const half8 a0 = lds_h8(smem, L::HT + ((32 * o_dt + (lane & 31)) * S136 + ko) * 2);
-                const half8 b0 = lds_h8(smem, L::Qg + ((32 * o_it + (lane & 31)) * S136 + ko) * 2);
-                const half8 a1 = lds_h8(smem, L::HT + ((32 * o_dt + (lane & 31)) * S136 + ko + 16) * 2);
-                const half8 b1 = lds_h8(smem, L::Qg + ((32 * o_it + (lane & 31)) * S136 + ko + 16) * 2);
-                oacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, oacc, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc1, 0, 0, 0);
-            }
-            // scale here; Aqk already carries it
-            oacc = (oacc + acc1) * p.scale;
-        }
-        f32x2 ph7 = {0.f, 0.f};
-        if (more) {
-            ph7 = gate_offsets(fac);
-            factors(nx, fac, 0, ph_rows03(ph7));
-        }
-        load_inputs(fr, c + 2, 1);
-        lds_barrier();
-
-        // ================= F: o += v_new^T Aqk^T; state update =================
-        // o goes to the staging tile Ost and out to HBM during the next chunk.
-        if (wo < NU) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 || o_it == 1) {
-                    const int ko = 16 * kk + 8 * (lane >> 5);
-                    const half8 a = lds_h8(smem, L::VnT + ((32 * o_dt + (lane & 31)) * S72 + ko) * 2);
-                    const half8 b = lds_h8(smem, L::Aqk + ((32 * o_it + (lane & 31)) * S72 + ko) * 2);
-                    oacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, oacc, 0, 0, 0);
-                }
-            }
-            const int i = 32 * o_it + (lane & 31);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * o_dt + 8 * q4 + 4 * (lane >> 5);
-                uint2 w;
-                w.x = pack_bf2(oacc[4 * q4], oacc[4 * q4 + 1]);
-                w.y = pack_bf2(oacc[4 * q4 + 2], oacc[4 * q4 + 3]);
-                *reinterpret_cast<uint2*>(smem + L::Ost + (i * (DV + 8) + d) * 2) = w;
-            }
-        }
-        // h <- Diag(e^{G_last}) h + Khat^T v_new
-        if (has_h) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(sGam + 32 * h_ct + 8 * q4 + 4 * (lane >> 5));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hacc[4 * q4 + e] *= gm[e];
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int ko = 16 * kk + 8 * (lane >> 5);
-                const half8 a = lds_h8(smem, L::KhT + ((32 * h_ct + (lane & 31)) * S72 + ko) * 2);
-                const half8 b = lds_h8(smem, L::VnT + ((32 * h_dt + (lane & 31)) * S72 + ko) * 2);
-                hacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, hacc, 0, 0, 0);
-            }
-        }
-        if (more) factors(nx, fac, 4, ph7);
-        load_inputs(fr, c + 2, 2);
-        lds_barrier();
         write_ht();
-        // The next chunk's phase C writes Qg, KgT, KhT, Gam, Vt, Aqk and T16; every
-        // read of them in this chunk happened before the barrier above, and none
-        // aliases HT.  Ost is read (and then rewritten) only after later barriers.
+        // Chunk c + 1's record DMA (issued a chunk ago) must be complete before the
+        // barrier publishes it; this chunk's record DMA may stay in flight, and so may
+        // the chain wave's v DMA of chunk c + 1 (four operations, issued between them).
+        // (The output wave's o stores of the previous chunk, issued between them too,
+        // are not counted: it waits for those as well.)
+        if (role == 0) {
+            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
+        } else {
+            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+        }
+        lds_barrier();   // h^T and chunk c + 1's record complete; reads of v_new^T and the old h^T done
+        read_ht();
     };
 
-    for (int64_t c = 0; c < nch; c += 2) {
-        chunk(c, in0, in1);
-        if (c + 1 < nch) chunk(c + 1, in1, in0);
-    }
-
-    // ---- output of the last chunk (staged in Ost before the loop's last barrier) ----
-    if (nch > 0) {
-        const int64_t last = (nch - 1) * CH;
-        store_output(bos + last, (int)(len - last));
+    if (role == 0) {
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t tok0 = bos + c * CH;
+            const int Lc = chunk_rows(c);
+            const int b = (int)(c & 1);
+            if (TRACE) trace_chunk_start(c, tok0, Lc);
+            decay_state(b);
+            // Z = v - (k e^G) h: two token tiles, accumulators starting from v, read from
+            // Vs in the accumulator layout (token 32 m + 8 (r / 4) + 4 hl + r % 4,
+            // column cl).  v of this chunk has landed once only the record DMA issued
+            // after it is in flight; Vs is then free for the next chunk's v.
+            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+            f32x16 z[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    z[m][r] = bf2f(*reinterpret_cast<const uint16_t*>(ps + L::Vs + (tok * DVW + cl) * 2));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            dma_v(c + 1);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                z[0] = mfma32(frag(b, WS_KG + kk * WS_FRAG), hf[kk], z[0]);
+                z[1] = mfma32(frag(b, WS_KG + (8 + kk) * WS_FRAG), hf[kk], z[1]);
+            }
+            // v_new = T diag(beta) Z (T lower triangular by 32x32 blocks).
+            half8 ft[6];
+#pragma unroll
+            for (int f = 0; f < 6; ++f) ft[f] = frag(b, WS_T + f * WS_FRAG);
+            half8 zb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) zb[kk] = acc_to_b(z[kk >> 1], kk & 1);
+            f32x16 vn[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) vn[m][r] = 0.f;
+            }
+            vn[0] = mfma32(ft[frag_lt(0, 0)], zb[0], vn[0]);
+            vn[1] = mfma32(ft[frag_lt(1, 0)], zb[0], vn[1]);
+            vn[0] = mfma32(ft[frag_lt(0, 1)], zb[1], vn[0]);
+            vn[1] = mfma32(ft[frag_lt(1, 1)], zb[1], vn[1]);
+            vn[1] = mfma32(ft[frag_lt(1, 2)], zb[2], vn[1]);
+            vn[1] = mfma32(ft[frag_lt(1, 3)], zb[3], vn[1]);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) fkh[f] = frag(b, WS_KH + (8 * role + f) * WS_FRAG);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int i = 32 * m + 8 * q4 + 4 * hl;
+                    half4 h4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h4[e] = (_Float16)vn[m][4 * q4 + e];
+                    *reinterpret_cast<half4*>(ps + L::VnT + (cl * S72 + i) * 2) = h4;
+                    if (TRACE && p.tr_vnew) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (i + e < Lc) p.tr_vnew[((tok0 + i + e) * p.Hv + hv) * DK + dv0 + cl] = vn[m][4 * q4 + e];
+                    }
+                }
+            }
+            lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
+            update_state(c, b);
+        }
+    } else {
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t tok0 = bos + c * CH;
+            const int Lc = chunk_rows(c);
+            const int b = (int)(c & 1);
+            if (TRACE) trace_chunk_start(c, tok0, Lc);
+            decay_state(b);
+            // o^T = h^T (scale q e^G)^T: needs only the state entering the chunk.
+            f32x16 oacc[2];   // o^T tiles (dv column x token), token tiles 0 / 1
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[m][r] = 0.f;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                oacc[0] = mfma32(hf[kk], frag(b, WS_QG + kk * WS_FRAG), oacc[0]);
+                oacc[1] = mfma32(hf[kk], frag(b, WS_QG + (8 + kk) * WS_FRAG), oacc[1]);
+            }
+            half8 fq[6];   // Aqk fragments, read before the buffer is released
+#pragma unroll
+            for (int f = 0; f < 6; ++f) fq[f] = frag(b, WS_AQK + f * WS_FRAG);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) fkh[f] = frag(b, WS_KH + (8 * role + f) * WS_FRAG);
+            lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
+            update_state(c, b);
+            // o^T += v_new^T Aqk^T (Aqk lower triangular by 32x32 blocks)
+            oacc[0] = mfma32(vf[0], fq[frag_lt(0, 0)], oacc[0]);
+            oacc[1] = mfma32(vf[0], fq[frag_lt(1, 0)], oacc[1]);
+            oacc[0] = mfma32(vf[1], fq[frag_lt(0, 1)], oacc[0]);
+            oacc[1] = mfma32(vf[1], fq[frag_lt(1, 1)], oacc[1]);
+            oacc[1] = mfma32(vf[2], fq[frag_lt(1, 2)], oacc[1]);
+            oacc[1] = mfma32(vf[3], fq[frag_lt(1, 3)], oacc[1]);
+            // o^T tile m: register r holds channel 8 (r / 4) + 4 hl + r % 4, token 32 m + cl.
+            uint16_t* obase = p.o + tok0 * v_tok + (int64_t)hv * DK + dv0;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int i = 32 * m + cl;
+                if (i < Lc) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        uint2 w;
+                        w.x = pack_bf2(oacc[m][4 * q4], oacc[m][4 * q4 + 1]);
+                        w.y = pack_bf2(oacc[m][4 * q4 + 2], oacc[m][4 * q4 + 3]);
+                        *reinterpret_cast<uint2*>(obase + i * v_tok + 8 * q4 + 4 * hl) = w;
+                    }
+                }
+            }
+        }
     }
 
     // ---- final state ----
-    if (p.hT && has_h) {
-        const int d = 32 * h_dt + (lane & 31);
-        float* dst = p.hT + ((int64_t)n * p.Hv + hv) * DK * DK + dv0 + d;
+    if (p.hT) {
+        // The lane offset is recomputed here from an opaque copy of the lane index,
+        // so that it is not kept live (with the h0 addresses) through the chunk loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        float* dst = p.hT + ((int64_t)n * p.Hv + hv) * DK * DK + dv0;
+        const int lo = (ln & 31) + 4 * (ln >> 5) * DK;
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2)
-            dst[(int64_t)(32 * h_ct + 8 * (r2 >> 2) + 4 * (lane >> 5) + (r2 & 3)) * DK] = hacc[r2];
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[lo + (32 * (2 * role + tt) + 8 * (r >> 2) + (r & 3)) * DK] = hacc[tt][r];
+        }
     }
 }
 
-template <int DV, bool TRACE>
-static hipError_t launch_dv(const KdaParams& p, int nblocks, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_scan_kernel<DV, TRACE>), dim3(nblocks), dim3(NTHREADS), 0, stream, p);
+template <bool TRACE>
+static hipError_t launch(const KdaParams& p, int nblocks, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_scan_kernel<TRACE>), dim3(nblocks), dim3(SCAN_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_kda_scan(const KdaParams& p, int dv_slices, bool trace, hipStream_t stream) {
-    const int64_t nblocks = (int64_t)p.N * p.Hv * dv_slices;
+int scan_slices() { return SLICES; }
+
+hipError_t launch_kda_scan(const KdaParams& p, bool trace, hipStream_t stream) {
+    const int64_t nblocks = (int64_t)p.N * p.Hv * SLICES;
     if (nblocks == 0) return hipSuccess;
-    if (dv_slices == 2) return trace ? launch_dv<64, true>(p, (int)nblocks, stream) : launch_dv<64, false>(p, (int)nblocks, stream);
-    return trace ? launch_dv<32, true>(p, (int)nblocks, stream) : launch_dv<32, false>(p, (int)nblocks, stream);
+    return trace ? launch<true>(p, (int)nblocks, stream) : launch<false>(p, (int)nblocks, stream);
 }
 
 }  // namespace kda

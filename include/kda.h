@@ -17,8 +17,9 @@
  * Akk products, the fp32 inversion of I + Akk) and a scan kernel that walks
  * each sequence's chunks in order (W/U recompute, state update, output).  The
  * intra kernel hands its results to the scan kernel through a device
- * workspace of kda_fwd_workspace_size() bytes (10 KiB per 64-token chunk slot
- * and value head).
+ * workspace of kda_fwd_workspace_size() bytes (61,952 bytes per 64-token chunk
+ * slot and value head: Aqk, T diag(beta) and the decayed q and k operands in
+ * fp16, laid out as the scan kernel's MFMA operand fragments).
  *
  * Tensors are described by kda_tensor_t: a device pointer, a dtype, a rank
  * and per-dimension sizes and strides counted in elements.  All tensors must
@@ -80,7 +81,7 @@ typedef enum {
 /*
  * kda_fwd_workspace_size -- bytes of device workspace kda_fwd needs for a call
  * with `total_tokens` = B * T tokens, N sequences and Hv value heads:
- * (ceil(total_tokens / 64) + N) * Hv * 10240.  Returns -1 for a negative size.
+ * (ceil(total_tokens / 64) + N) * Hv * 61952.  Returns -1 for a negative size.
  */
 int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads);
 
@@ -178,7 +179,7 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
 const char* kda_status_string(kda_status_t status);
 
 /* Number of dv slices (scan work-groups per sequence and value head) that
- * kda_fwd launches for N sequences and Hv value heads: 2 or 4. */
+ * kda_fwd launches for N sequences and Hv value heads: 2 (64 dv columns each). */
 int32_t kda_dv_slices(int64_t num_sequences, int64_t num_value_heads);
 
 #ifdef __cplusplus

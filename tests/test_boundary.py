@@ -152,9 +152,9 @@ def test_status_strings(lib):
 
 
 def test_dv_slices(lib):
-    assert lib.kda_dv_slices(2, 64) == 2
-    assert lib.kda_dv_slices(1, 64) == 4
-    assert lib.kda_dv_slices(14, 64) == 2
+    # one scan work-group per 64-wide dv slice, whatever the sizes
+    for n, hv in ((2, 64), (1, 64), (14, 64), (1, 1)):
+        assert lib.kda_dv_slices(n, hv) == 2
 
 
 def test_trace_requires_descriptor(lib):
@@ -166,11 +166,15 @@ def test_trace_requires_descriptor(lib):
 
 
 def test_workspace_size(lib):
-    # one 10 KiB record per (64-token slot, value head); N extra slots for the
-    # partial chunks sequences may start mid-slot
-    assert lib.kda_fwd_workspace_size(2 * 8192, 2, 64) == (256 + 2) * 64 * 10240
-    assert lib.kda_fwd_workspace_size(16384, 14, 64) == (256 + 14) * 64 * 10240
-    assert lib.kda_fwd_workspace_size(1, 1, 1) == 2 * 10240
+    # one 61,952-byte record per (64-token slot, value head): 12 fp16 operand
+    # fragments of 64 lanes x 16 bytes (Aqk, T diag beta), three fp16 64x128
+    # operands, 128 fp32; N extra slots for the partial chunks of sequences that
+    # start mid-slot
+    rec = 12 * 64 * 16 + 3 * 64 * 128 * 2 + 128 * 4
+    assert rec == 61952
+    assert lib.kda_fwd_workspace_size(2 * 8192, 2, 64) == (256 + 2) * 64 * rec
+    assert lib.kda_fwd_workspace_size(16384, 14, 64) == (256 + 14) * 64 * rec
+    assert lib.kda_fwd_workspace_size(1, 1, 1) == 2 * rec
     assert lib.kda_fwd_workspace_size(0, 0, 64) == 0
     assert lib.kda_fwd_workspace_size(-1, 1, 1) == -1
 
