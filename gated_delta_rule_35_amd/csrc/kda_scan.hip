@@ -28,11 +28,12 @@
 //                 accumulator registers (the record's T columns are in
 //                 accumulator row order); v_new^T -> LDS
 //   output wave:  o^T = h^T (scale q e^G)^T, the state-only part of o
-//   barrier; the record DMA of chunk + 2 into the buffer just read
+//   barrier
 //   both:         own state rows h <- e^{G_last} h + Khat^T v_new; fp16 h^T -> LDS
 //   barrier
 //   output wave:  o^T += v_new^T Aqk^T; o stored (bf16) straight from the
-//                 accumulators, four channels per lane store
+//                 accumulators, four channels per lane store; the record DMA of
+//                 chunk + 2 into the buffer this chunk was read from
 // All products run on v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulate).
 #include "kda_device.h"
 
@@ -143,31 +144,45 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     };
 
     // ---- record DMA ----
-    // Chunk c's record into LDS buffer b: 1 KB pieces, piece i by wave i % 4, lane l's
-    // 16 bytes to byte 16 l of the piece.  Past the record's end, and for chunks past
-    // the sequence end, the range check makes the DMA write zeros.  The loads are
-    // issued as inline assembly (M0 = LDS address) so that the compiler, which cannot
-    // tell them apart from the fragment reads of the other buffer, adds no waits;
-    // their completion is awaited explicitly before the barrier that publishes them.
-    constexpr int DMA_PER_WAVE = (REC_PIECES + 3) / 4;
+    // Chunk c's record into LDS buffer b, by the two output waves (which have slack
+    // at the end of each chunk): 1 KB pieces, piece i by the output wave of pair
+    // i % 2, lane l's 16 bytes to byte 16 l of the piece.  The loads are issued as
+    // one block of inline assembly, stepping M0 (the LDS address) and the scalar
+    // offset, so that the compiler, which cannot tell them apart from the fragment
+    // reads of the other buffer, adds no waits; their completion is awaited
+    // explicitly before the barrier that publishes them.  A write of M0 is followed
+    // by one other instruction before the DMA that uses it.
+    //   Pieces 0 .. 59 lie inside the record, so the scalar offset may carry their
+    // position; piece 60 (the last 512 bytes) carries it in the per-lane offset, so
+    // that the range check drops its lanes 32 .. 63.  For chunks past the sequence
+    // end the range is empty and the DMA writes zeros.
+    static_assert(REC_PIECES == 61 && WS_RECORD_BYTES == 60 * WS_FRAG + 512, "record pieces");
     const uint32_t lds_rec = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem + L::Rec);
     auto dma_record = [&](int64_t c, int b) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES,
                                                    chunk_rows(c) ? WS_RECORD_BYTES : 0);
-#pragma unroll
-        for (int u = 0; u < DMA_PER_WAVE; ++u) {
-            const int i = wave + 4 * u;
-            if (i < REC_PIECES) {
-                const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + i * WS_FRAG);
-                const int voff = i * WS_FRAG + lane * 16;
-                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(r)
-                             : "memory");
-            }
+        uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + pr * WS_FRAG);
+        uint32_t soff = pr * WS_FRAG;
+        const int vlane = lane * 16;
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            ".rept 30\n\t"
+            "buffer_load_dwordx4 %2, %3, %1 offen lds\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_add_u32 %1, %1, 2048\n\t"
+            ".endr"
+            : "+s"(m0), "+s"(soff)
+            : "v"(vlane), "s"(r)
+            : "memory", "scc");
+        if (pr == 0) {   // piece 60
+            const uint32_t m60 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + 60 * WS_FRAG);
+            const int vlast = 60 * WS_FRAG + vlane;
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m60), "v"(vlast),
+                         "s"(r)
+                         : "memory");
         }
     };
-    // DMA pieces this wave issues per chunk: the count of memory operations a
-    // wait must let stay in flight to cover one chunk's DMA.
-    const int dma_mine = (REC_PIECES - wave + 3) / 4;
     auto frag = [&](int b, int off) -> half8 {
         return *reinterpret_cast<const half8*>(smem + L::Rec + b * REC_LDS + off + lane * 16);
     };
@@ -221,16 +236,20 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
         for (int u = 0; u < 4; ++u) {
             const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_vs + u * WS_FRAG);
             const int voff = (int)(((16 * u + (lane >> 2)) * v_tok + 8 * (lane & 3)) * 2);
-            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(rv)
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff),
+                         "s"(rv)
                          : "memory");
         }
     };
 
     write_ht();
     if (nch > 0) {
-        dma_record(0, 0);
-        dma_record(1, 1);
-        if (role == 0) dma_v(0);
+        if (role == 1) {
+            dma_record(0, 0);
+            dma_record(1, 1);
+        } else {
+            dma_v(0);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();   // h^T, the first two records and the first chunk's v complete
@@ -285,11 +304,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     };
     half8 fkh[8];   // Khat^T fragments of this wave's state rows: (tt, kk) at 4 tt + kk
     half8 vf[4];    // v_new operand, k step kk: tokens 16 kk + 8 hl + 0..7 of column cl
-    // After the first barrier: the record DMA of chunk c + 2 into buffer b; the state
-    // update h <- e^{G_last} h + Khat^T v_new of this wave's rows (the output wave
-    // also stages the next chunk's v^T); the fp16 h^T copy; the second barrier.
-    auto update_state = [&](int64_t c, int b) {
-        dma_record(c + 2, b);
+    // After the first barrier: the state update h <- e^{G_last} h + Khat^T v_new of
+    // this wave's rows, the fp16 h^T copy, the second barrier.
+    auto update_state = [&]() {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) vf[kk] = lds_h8(ps, L::VnT + (cl * S72 + 16 * kk + 8 * hl) * 2);
 #pragma unroll
@@ -298,18 +315,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
             hacc[1] = mfma32(fkh[4 + kk], vf[kk], hacc[1]);
         }
         write_ht();
-        // Chunk c + 1's record DMA (issued a chunk ago) must be complete before the
-        // barrier publishes it; this chunk's record DMA may stay in flight, and so may
-        // the chain wave's v DMA of chunk c + 1 (four operations, issued between them).
-        // (The output wave's o stores of the previous chunk, issued between them too,
-        // are not counted: it waits for those as well.)
-        if (role == 0) {
-            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
-        } else {
-            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-        }
+        // Chunk c + 1's record DMA (issued by the output wave at the end of the last
+        // chunk, its latest memory operations) must be complete before the barrier
+        // publishes it.
+        if (role == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();   // h^T and chunk c + 1's record complete; reads of v_new^T and the old h^T done
         read_ht();
     };
@@ -323,10 +332,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
             decay_state(b);
             // Z = v - (k e^G) h: two token tiles, accumulators starting from v, read from
             // Vs in the accumulator layout (token 32 m + 8 (r / 4) + 4 hl + r % 4,
-            // column cl).  v of this chunk has landed once only the record DMA issued
-            // after it is in flight; Vs is then free for the next chunk's v.
-            if (dma_mine == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+            // column cl).  This chunk's v (the wave's only memory operations in flight)
+            // has landed; once read, Vs is free for the next chunk's v.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             f32x16 z[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -381,7 +389,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
                 }
             }
             lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
-            update_state(c, b);
+            update_state();
         }
     } else {
         for (int64_t c = 0; c < nch; ++c) {
@@ -408,7 +416,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
 #pragma unroll
             for (int f = 0; f < 8; ++f) fkh[f] = frag(b, WS_KH + (8 * role + f) * WS_FRAG);
             lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
-            update_state(c, b);
+            update_state();
             // o^T += v_new^T Aqk^T (Aqk lower triangular by 32x32 blocks)
             oacc[0] = mfma32(vf[0], fq[frag_lt(0, 0)], oacc[0]);
             oacc[1] = mfma32(vf[0], fq[frag_lt(1, 0)], oacc[1]);
@@ -431,6 +439,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
                     }
                 }
             }
+            // Record of chunk c + 2 into buffer b, whose last reads came before the
+            // first barrier.
+            dma_record(c + 2, b);
         }
     }
 
