@@ -93,6 +93,60 @@ def load_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def decode_bytes(N, Hq, Hv, beta_bytes, d=128):
+    """Algorithmic bytes of one decode step: the state read and written once, the
+    token's q, k (per q/k head), v, g, beta and o (per value head)."""
+    return N * Hv * (2 * d * d * 4 + d * (2 + 4 + 2) + beta_bytes) + N * Hq * d * 2 * 2
+
+
+def bench_decode(args):
+    """kda_decode on a batch of N single tokens (Hq = Hv = 64, fp32 beta, fp32
+    state updated in place): HIP events around each launch on its stream."""
+    import torch
+    from gated_delta_rule_35_amd import kda_decode
+    from gated_delta_rule_35_amd.inputs import make_inputs
+    if args.gpus != 1:
+        print("bench.py measures one GPU only", file=sys.stderr, flush=True)
+        sys.exit(2)
+    N, H = args.decode, 64
+    log(f"generating decode inputs: N={N} sequences x {H} heads")
+    x = make_inputs(N, 1, H, H, torch.float32, h0=True, seed=0)
+    dev = torch.device("cuda:0")
+    s = {k: x[k][:, 0].contiguous().to(dev) for k in ("q", "k", "v", "g", "beta")}
+    state = x["h0"].to(dev)
+    out = torch.empty_like(s["v"])
+    stream = torch.cuda.current_stream(dev)
+    scale = 128 ** -0.5
+    for _ in range(args.warmup):
+        kda_decode(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, state, out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        kda_decode(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, state, out=out)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    t = sum(ms) / len(ms) / 1e3
+    nbytes = decode_bytes(N, H, H, 4)
+    gbs = nbytes / t / 1e9
+    log(f"decode N={N}: kernel avg {t * 1e3:.4f} ms (min {min(ms):.4f}), {gbs:.0f} GB/s")
+    rec = {"metric": "KDA decode step tokens/s (one token per sequence, H=64, d=128, fp32 state)",
+           "value": round(N / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"decode_n{N}_h{H}", "N_sequences": N, "Hq": H, "Hv": H, "dk": 128, "dv": 128,
+                      "beta_dtype": "fp32", "state": "fp32, updated in place"},
+           "kernel_ms_avg": round(t * 1e3, 5), "algorithmic_bytes_per_step": nbytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "scope": "kda_decode_kernel: algorithmic bytes over its average duration"},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +155,8 @@ def main():
     ap.add_argument("--workload", default="mha_b2_h64_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64, help="value heads in the oracle's timing sample")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="instead of the forward, time kda_decode: one step for N sequences x 64 heads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the benchmark, run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -112,6 +168,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": 3}))
+        return
+    if args.decode:
+        bench_decode(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "

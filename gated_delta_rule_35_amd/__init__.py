@@ -1,4 +1,4 @@
-"""MI355X-native Kimi Delta Attention (KDA) chunked forward.
+"""MI355X-native Kimi Delta Attention (KDA): chunked forward and decode step.
 
 The compute lives in libkda.so (hand-written HIP for gfx950, C ABI in
 include/kda.h).  This package is a thin ctypes binding: it turns torch tensors
@@ -6,8 +6,8 @@ into C descriptors and passes the current HIP stream; every step of the forward
 pass runs in the library's kernels.  There is no fallback: if libkda.so is
 missing or the tensors are not on the GPU, the call raises.
 """
-from .binding import (KdaError, kda_fwd, kda_fwd_intra, kda_fwd_scan, kda_fwd_trace,  # noqa: F401
+from .binding import (KdaError, kda_decode, kda_fwd, kda_fwd_intra, kda_fwd_scan, kda_fwd_trace,  # noqa: F401
                       kda_fwd_workspace_size, kda_dv_slices, library_path, load_library)
 
-__all__ = ["KdaError", "kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_workspace_size",
-           "kda_dv_slices", "library_path", "load_library"]
+__all__ = ["KdaError", "kda_decode", "kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace",
+           "kda_fwd_workspace_size", "kda_dv_slices", "library_path", "load_library"]

@@ -1,7 +1,8 @@
 """ctypes binding of libkda.so (argument marshalling only).
 
-Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_trace,
-kda_fwd_workspace_size, kda_status_string, kda_dv_slices.  Tensors are passed
+Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_intra, kda_fwd_scan,
+kda_fwd_trace, kda_decode, kda_fwd_workspace_size, kda_status_string,
+kda_dv_slices.  Tensors are passed
 as kda_tensor_t descriptors built from torch tensors (data pointer, dtype,
 shape, strides); the stream is torch's current HIP stream unless one is given.
 The workspace is a uint8 device tensor from torch's caching allocator unless
@@ -21,7 +22,7 @@ KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
-EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_workspace_size",
+EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_decode", "kda_fwd_workspace_size",
             "kda_status_string", "kda_dv_slices"]
 
 
@@ -65,6 +66,8 @@ def load_library(path=None):
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_void_p]
+    lib.kda_decode.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_dv_slices.argtypes = [ctypes.c_int64, ctypes.c_int64]
@@ -201,3 +204,25 @@ def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state
         out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace)
     return out, final_state
+
+
+def kda_decode(q, k, v, g, beta, scale, state, out=None, new_state=None, stream=None):
+    """One recurrent step for a batch of single tokens (q, k [N, Hq, 128]; v, g
+    [N, Hv, 128]; beta [N, Hv]).  `state` [N, Hv, 128, 128] fp32 or None (a zero
+    state); the new state goes to `new_state`, by default `state` itself (updated
+    in place; allocated when state is None).  Returns (out, new_state)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    if new_state is None:
+        new_state = state if state is not None else torch.empty(
+            (v.shape[0], v.shape[1], q.shape[2], v.shape[2]), dtype=torch.float32, device=v.device)
+    tensors = (q, k, v, g, beta, state, new_state, out)
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kda_decode needs every tensor on the GPU")
+    descs = [describe(t) for t in tensors]
+    s = _stream_handle(stream, tensors)
+    _check(lib, lib.kda_decode(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
+                               float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), s))
+    return out, new_state

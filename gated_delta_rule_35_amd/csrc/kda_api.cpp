@@ -201,6 +201,68 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
                trace, kBoth, stream);
 }
 
+kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                        const kda_tensor_t* beta, float scale, const kda_tensor_t* state_in,
+                        const kda_tensor_t* state_out, const kda_tensor_t* out, void* stream) {
+    kda_status_t st;
+    if ((st = check_tensor(q, 3, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(k, 3, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(v, 3, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(g, 3, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if (!beta) return KDA_ERR_NULL;
+    if ((st = check_tensor(beta, 2, KDA_BF16, KDA_F32, elem_size(beta->dtype))) != KDA_OK) return st;
+    if ((st = check_tensor(out, 3, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if (state_in && (st = check_tensor(state_in, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(state_out, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+
+    const int64_t N = q->shape[0], Hq = q->shape[1], Hv = v->shape[1];
+    if (q->shape[2] != kHeadDim || v->shape[2] != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if (!same_shape(k, q->shape, 3)) return KDA_ERR_SHAPE;
+    if (v->shape[0] != N) return KDA_ERR_SHAPE;
+    const int64_t vs[3] = {N, Hv, kHeadDim};
+    if (!same_shape(g, vs, 3) || !same_shape(out, vs, 3)) return KDA_ERR_SHAPE;
+    const int64_t bs[2] = {N, Hv};
+    if (!same_shape(beta, bs, 2)) return KDA_ERR_SHAPE;
+    const int64_t ss[4] = {N, Hv, kHeadDim, kHeadDim};
+    if (state_in && !same_shape(state_in, ss, 4)) return KDA_ERR_SHAPE;
+    if (!same_shape(state_out, ss, 4)) return KDA_ERR_SHAPE;
+    if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
+    if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
+    if (N * Hv > (int64_t(1) << 31) - 1) return KDA_ERR_UNSUPPORTED;
+    // The new state may overwrite the old one in place, or go elsewhere; a partial
+    // overlap would let one work-group's writes reach another's unread rows.
+    if (state_in && state_in->data != state_out->data) {
+        const char* a = static_cast<const char*>(state_in->data);
+        const char* b = static_cast<const char*>(state_out->data);
+        const int64_t bytes = N * Hv * kHeadDim * kHeadDim * 4;
+        if (a < b + bytes && b < a + bytes) return KDA_ERR_LAYOUT;
+    }
+
+    kda::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.k = static_cast<const uint16_t*>(k->data);
+    p.v = static_cast<const uint16_t*>(v->data);
+    p.g = static_cast<const float*>(g->data);
+    p.beta = beta->data;
+    p.beta_f32 = beta->dtype == KDA_F32 ? 1 : 0;
+    p.s_in = state_in ? static_cast<const float*>(state_in->data) : nullptr;
+    p.s_out = static_cast<float*>(state_out->data);
+    p.o = static_cast<uint16_t*>(out->data);
+    p.N = static_cast<int32_t>(N);
+    p.Hq = static_cast<int32_t>(Hq);
+    p.Hv = static_cast<int32_t>(Hv);
+    p.scale = scale;
+    if (N == 0) return KDA_OK;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (kda::launch_kda_decode(p, hs) != hipSuccess) return KDA_ERR_HIP;
+    if (std::getenv("KDA_DEBUG_SYNC")) {
+        if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 const char* kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";

@@ -32,6 +32,23 @@ struct KdaParams {
     float* tr_h;
 };
 
+// One recurrent step for a batch of single tokens (decode).
+struct DecodeParams {
+    const uint16_t* q;     // [N, Hq, 128] bf16 bits
+    const uint16_t* k;     // [N, Hq, 128] bf16 bits
+    const uint16_t* v;     // [N, Hv, 128] bf16 bits
+    const float* g;        // [N, Hv, 128]
+    const void* beta;      // [N, Hv] bf16 bits or fp32
+    const float* s_in;     // [N, Hv, 128, 128] or nullptr (zero state)
+    float* s_out;          // [N, Hv, 128, 128]; may equal s_in
+    uint16_t* o;           // [N, Hv, 128] bf16 bits
+    int32_t N, Hq, Hv;
+    int32_t beta_f32;
+    float scale;
+};
+
+hipError_t launch_kda_decode(const DecodeParams& p, hipStream_t stream);
+
 // Workspace bytes for the given sizes (one record per chunk slot and value head).
 int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
 

@@ -175,6 +175,28 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
                            void* workspace, int64_t workspace_size,
                            const kda_trace_t* trace, void* stream);
 
+/*
+ * kda_decode -- one recurrent step for a batch of N single tokens: the decode
+ * half of inference, continuing from a state such as kda_fwd's final_state
+ * ("cuLA REPO_LAYOUT.md", entry decode/: the KDA decode reference).  For every
+ * sequence n and value head hv (q/k head hv / (Hv / Hq)):
+ *
+ *     S' = (I - beta k k^T) Diag(exp g) S + beta k v^T,   o = scale * S'^T q
+ *
+ * with S = state_in[n, hv] (a zero state when state_in is NULL) and S' written
+ * to state_out[n, hv].  Shapes: q, k [N, Hq, 128] bf16; v [N, Hv, 128] bf16;
+ * g [N, Hv, 128] fp32 log-decay; beta [N, Hv] bf16 or fp32; states
+ * [N, Hv, 128 (key), 128 (value)] fp32; out [N, Hv, 128] bf16.  All arithmetic is
+ * fp32; o is rounded to bf16 once.  state_out may be state_in itself (in-place
+ * update) or a separate buffer; a partial overlap returns KDA_ERR_LAYOUT.
+ * Memory is caller-owned; the call allocates nothing and is asynchronous on
+ * `stream`; repeated calls give bitwise-identical results.  Errors as for kda_fwd.
+ */
+kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                        const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                        const kda_tensor_t* state_in, const kda_tensor_t* state_out,
+                        const kda_tensor_t* out, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status_t status);
 

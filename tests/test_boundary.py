@@ -194,3 +194,69 @@ def test_workspace_checked_before_launch(lib):
     b = good(B=2, T_=100, Hv=4)
     b["q"] = T([2, 100, 2, 64])
     expect(lib, b, "KDA_ERR_UNSUPPORTED", ws=FAKE, ws_size=0)
+
+
+# ---- kda_decode ----
+
+def good_decode(N=2, Hq=2, Hv=4, beta_dtype=binding.KDA_F32, state=True):
+    return dict(q=T([N, Hq, 128]), k=T([N, Hq, 128]), v=T([N, Hv, 128]), g=T([N, Hv, 128], binding.KDA_F32),
+                beta=T([N, Hv], beta_dtype), s_in=T([N, Hv, 128, 128], binding.KDA_F32) if state else None,
+                s_out=T([N, Hv, 128, 128], binding.KDA_F32), out=T([N, Hv, 128]))
+
+
+def call_decode(lib, a, scale=0.088):
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    return lib.kda_decode(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale,
+                          r(a.get("s_in")), r(a.get("s_out")), r(a.get("out")), None)
+
+
+def expect_decode(lib, a, name, **kw):
+    st = call_decode(lib, a, **kw)
+    assert binding.STATUS_NAMES[st] == name, (binding.STATUS_NAMES[st], name)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    for key in ("q", "k", "v", "g", "beta", "s_out", "out"):
+        a = good_decode()
+        a[key] = None
+        expect_decode(lib, a, "KDA_ERR_NULL")
+    a = good_decode()
+    a["g"] = T([2, 4, 128], binding.KDA_BF16)
+    expect_decode(lib, a, "KDA_ERR_DTYPE")
+    a = good_decode()
+    a["s_in"] = T([2, 4, 128, 128], binding.KDA_BF16)
+    expect_decode(lib, a, "KDA_ERR_DTYPE")
+    a = good_decode()
+    a["v"] = T([3, 4, 128])
+    expect_decode(lib, a, "KDA_ERR_SHAPE")
+    a = good_decode()
+    a["beta"] = T([2, 3], binding.KDA_F32)
+    expect_decode(lib, a, "KDA_ERR_SHAPE")
+    a = good_decode()
+    a["s_out"] = T([2, 4, 128, 64], binding.KDA_F32)
+    expect_decode(lib, a, "KDA_ERR_SHAPE")
+    a = good_decode(Hq=3, Hv=4)
+    expect_decode(lib, a, "KDA_ERR_UNSUPPORTED")
+    a = good_decode()
+    a["q"] = T([2, 2, 64])
+    a["k"] = T([2, 2, 64])
+    expect_decode(lib, a, "KDA_ERR_UNSUPPORTED")
+    a = good_decode()
+    a["out"] = T([2, 4, 128], data=FAKE + 8)
+    expect_decode(lib, a, "KDA_ERR_LAYOUT")
+    for s in (0.0, -1.0, float("nan")):
+        expect_decode(lib, good_decode(), "KDA_ERR_VALUE", scale=s)
+
+
+def test_decode_rejects_partly_overlapping_states(lib):
+    a = good_decode()
+    a["s_out"] = T([2, 4, 128, 128], binding.KDA_F32, data=FAKE + 64 * 1024)
+    expect_decode(lib, a, "KDA_ERR_LAYOUT")
+
+
+def test_decode_empty_batch_needs_no_launch(lib):
+    a = good_decode(N=0)
+    for key in a:
+        if a[key] is not None:
+            a[key].data = None
+    expect_decode(lib, a, "KDA_OK")
