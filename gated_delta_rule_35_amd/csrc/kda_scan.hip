@@ -145,13 +145,15 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
 
     // ---- record DMA ----
     // Chunk c's record into LDS buffer b, by the two output waves (which have slack
-    // at the end of each chunk): 1 KB pieces, piece i by the output wave of pair
-    // i % 2, lane l's 16 bytes to byte 16 l of the piece.  The loads are issued as
-    // one block of inline assembly, stepping M0 (the LDS address) and the scalar
-    // offset, so that the compiler, which cannot tell them apart from the fragment
-    // reads of the other buffer, adds no waits; their completion is awaited
-    // explicitly before the barrier that publishes them.  A write of M0 is followed
-    // by one other instruction before the DMA that uses it.
+    // at the end of each chunk): 1 KB pieces, lane l's 16 bytes to byte 16 l of a
+    // piece; the output wave of pair 0 takes pieces 0 .. 29, that of pair 1 pieces
+    // 30 .. 60.  The loads are issued as inline assembly so that the compiler, which
+    // cannot tell them apart from the fragment reads of the other buffer, adds no
+    // waits; their completion is awaited explicitly before the barrier that
+    // publishes them.  Four consecutive pieces share one write of M0 (the LDS
+    // address; writing it stalls the DMA issue): the instruction offset 0, 1 K,
+    // 2 K or 3 K moves both the global and the LDS address.  A write of M0 is
+    // followed by one other instruction before the DMA that uses it.
     //   Pieces 0 .. 59 lie inside the record, so the scalar offset may carry their
     // position; piece 60 (the last 512 bytes) carries it in the per-lane offset, so
     // that the range check drops its lanes 32 .. 63.  For chunks past the sequence
@@ -161,21 +163,27 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     auto dma_record = [&](int64_t c, int b) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES,
                                                    chunk_rows(c) ? WS_RECORD_BYTES : 0);
-        uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + pr * WS_FRAG);
-        uint32_t soff = pr * WS_FRAG;
+        uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + pr * 30 * WS_FRAG);
+        uint32_t soff = pr * 30 * WS_FRAG;
         const int vlane = lane * 16;
+        // pieces 30 pr .. 30 pr + 29: seven groups of four, then two
         asm volatile(
             "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
-            ".rept 30\n\t"
+            ".rept 7\n\t"
             "buffer_load_dwordx4 %2, %3, %1 offen lds\n\t"
-            "s_add_u32 m0, m0, 2048\n\t"
-            "s_add_u32 %1, %1, 2048\n\t"
-            ".endr"
+            "buffer_load_dwordx4 %2, %3, %1 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %2, %3, %1 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %2, %3, %1 offen offset:3072 lds\n\t"
+            "s_add_u32 m0, m0, 4096\n\t"
+            "s_add_u32 %1, %1, 4096\n\t"
+            ".endr\n\t"
+            "buffer_load_dwordx4 %2, %3, %1 offen lds\n\t"
+            "buffer_load_dwordx4 %2, %3, %1 offen offset:1024 lds"
             : "+s"(m0), "+s"(soff)
             : "v"(vlane), "s"(r)
             : "memory", "scc");
-        if (pr == 0) {   // piece 60
+        if (pr == 1) {   // piece 60
             const uint32_t m60 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + 60 * WS_FRAG);
             const int vlast = 60 * WS_FRAG + vlane;
             asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m60), "v"(vlast),
