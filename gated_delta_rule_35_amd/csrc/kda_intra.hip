@@ -168,15 +168,15 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // Work-group -> (slot, value head).  Work-groups are dealt to the 8 XCDs round
-    // robin; each XCD takes a contiguous range of items, so the value heads of one
-    // chunk (which share q and k under grouped values) meet in one L2.
-    const int64_t total = p.nslots * p.Hv;
-    int64_t item = blockIdx.x;
-    if ((total & 7) == 0) item = (int64_t)(blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int64_t slot = item / p.Hv;
-    const int hv = (int)(item % p.Hv);
-    const int hq = hv / (p.Hv / p.Hq);
+    // Work-group -> (slot, value head): slots in order, value heads fastest.
+    // Work-groups are dealt to the 8 XCDs round robin; the value heads that share
+    // one q/k head (grouped values) are taken Hq work-groups apart, so that (Hq a
+    // multiple of 8) they run on one XCD, whose L2 then serves their q and k.
+    const int64_t slot = blockIdx.x / p.Hv;
+    const int r = (int)(blockIdx.x % p.Hv);
+    const int grp = p.Hv / p.Hq;
+    const int hv = grp == 1 ? r : (r % p.Hq) * grp + r / p.Hq;
+    const int hq = hv / grp;
 
     // slot -> (sequence, chunk): the first slot of sequence n, floor(bos_n / 64) + n,
     // does not decrease with n; take the last sequence whose first slot is <= slot.
