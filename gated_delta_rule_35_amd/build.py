@@ -2,7 +2,10 @@
 
 hipcc compiles the kernels and the C-ABI front end into one shared object next to
 this file.  -packed-fp32-ops is turned off for the device code: the compiler then
-never forms packed fp32 instructions.
+never forms packed fp32 instructions.  -amdgpu-mfma-vgpr-form keeps MFMA
+accumulators in ordinary VGPRs while they fit: the scan kernel's state and
+products are scaled and converted by VALU instructions every chunk, which cannot
+read accumulation registers, so the other form costs a register move per element.
 """
 import os
 import subprocess
@@ -17,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp"] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
