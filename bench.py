@@ -39,8 +39,11 @@ METRIC = "KDA fwd tokens/s (B=2,H=64,d=128,T=8192); ms/call; % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 MAC_PER_CHUNK_HEAD = 4_512_416
+# The forward kernels' sources and the build script that holds their compiler
+# flags: counters taken on other code than these are not reported.
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_35_amd", "csrc", f)
-                  for f in ("kda_intra.hip", "kda_scan.hip", "kda_device.h", "kda_kernel.h")]
+                  for f in ("kda_intra.hip", "kda_scan.hip", "kda_device.h", "kda_kernel.h")] + \
+                 [os.path.join(ROOT, "gated_delta_rule_35_amd", "build.py")]
 RECORD_BYTES = 61952   # workspace record per (chunk, value head)
 # The pages' own time for this exact workload ("cuLA PR #131: SM100/SM103 KDA
 # forward to pure CuTeDSL", Performance table, fp32 beta, T=8192, B=2, H=64,
