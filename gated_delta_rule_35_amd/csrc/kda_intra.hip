@@ -135,27 +135,23 @@ __device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2
 }
 
 // 4x4 transpose of 32-bit words across each quad of lanes: on entry quad lane j
-// holds x[0..3]; on exit it holds x[p] = (x[j] of quad lane p).  A per-lane
-// rotation, three fixed quad permutations (DPP) and the inverse rotation.
+// holds x[0..3]; on exit it holds x[p] = (x[j] of quad lane p).  Two butterfly
+// stages: lanes j and j ^ 2 swap the 2x2 blocks off the diagonal, then lanes j and
+// j ^ 1 swap the off-diagonal elements of each 2x2 block (DPP quad_perm
+// [2,3,0,1], then [1,0,3,2]).
 __device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int j) {
-    const bool o1 = (j & 1) != 0, o2 = (j & 2) != 0;
-    uint32_t t[4];
+    const bool b1 = (j & 2) != 0, b0 = (j & 1) != 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {   // t[k] = x[(k + j) % 4]
-        const uint32_t u = o1 ? x[(k + 1) & 3] : x[k];
-        const uint32_t w = o1 ? x[(k + 3) & 3] : x[(k + 2) & 3];
-        t[k] = o2 ? w : u;
+    for (int e = 0; e < 2; ++e) {   // element pairs (0, 2), (1, 3)
+        const uint32_t send = b1 ? x[e] : x[e + 2];
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4e, 0xf, 0xf, false);
+        if (b1) x[e] = recv; else x[e + 2] = recv;
     }
-    // t[k] <- t[k] of quad lane (j - k) % 4; DPP quad_perm selectors [3,0,1,2],
-    // [2,3,0,1], [1,2,3,0].
-    t[1] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[1], 0x93, 0xf, 0xf, false);
-    t[2] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[2], 0x4e, 0xf, 0xf, false);
-    t[3] = (uint32_t)__builtin_amdgcn_mov_dpp((int)t[3], 0x39, 0xf, 0xf, false);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {   // x[p] = t[(j - p) % 4]
-        const uint32_t u = o1 ? t[(1 - p) & 3] : t[(0 - p) & 3];
-        const uint32_t w = o1 ? t[(3 - p) & 3] : t[(2 - p) & 3];
-        x[p] = o2 ? w : u;
+    for (int e = 0; e < 4; e += 2) {   // element pairs (0, 1), (2, 3)
+        const uint32_t send = b0 ? x[e] : x[e + 1];
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xb1, 0xf, 0xf, false);
+        if (b0) x[e] = recv; else x[e + 1] = recv;
     }
 }
 
