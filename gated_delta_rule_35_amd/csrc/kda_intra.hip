@@ -134,6 +134,34 @@ __device__ __forceinline__ void block_scalars(const f32x2 (&tot)[4], const f32x2
     }
 }
 
+// The MFMA operands of the eight rows 16 IB + 8 hh + rr of a half block, lane cp
+// holding channels 2 cp, 2 cp + 1: q e^{G - G_b} (Aq), k e^{G - G_b} (Ak),
+// k e^{G_b - G} (Bd) and, for each later block I2 = IB + 1 + d, k e^{G_{b_I2} - G}
+// (the rows of the block pair (I2, IB) in Bo), from F = e^{G - G_b},
+// R = e^{G_e - G}, invr = e^{G_b - G_e} and lam[d] = e^{G_{b_I2} - G_e}.
+template <int IB>
+__device__ __forceinline__ void write_operands(char* smem, const uint32_t (&qw)[8], const uint32_t (&kw)[8],
+                                               const float (&F)[8][2], const float (&R)[8][2], const float (&invr)[2],
+                                               const float (&lam)[3][2], int hh, int cp) {
+    using L = IntraLds;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+        const int row = 16 * IB + 8 * hh + rr;
+        const float q0 = bf_lo(qw[rr]), q1 = bf_hi(qw[rr]);
+        const float k0 = bf_lo(kw[rr]), k1 = bf_hi(kw[rr]);
+        const int o = swz(row, 2 * cp);
+        *reinterpret_cast<uint32_t*>(smem + L::Aq + o) = pack_h2(q0 * F[rr][0], q1 * F[rr][1]);
+        *reinterpret_cast<uint32_t*>(smem + L::Ak + o) = pack_h2(k0 * F[rr][0], k1 * F[rr][1]);
+        const float kr0 = k0 * R[rr][0], kr1 = k1 * R[rr][1];
+        *reinterpret_cast<uint32_t*>(smem + L::Bd + o) = pack_h2(kr0 * invr[0], kr1 * invr[1]);
+#pragma unroll
+        for (int d = 0; d < 3 - IB; ++d) {
+            const int o2 = swz(16 * pair_index(IB + 1 + d, IB) + (row & 15), 2 * cp);
+            *reinterpret_cast<uint32_t*>(smem + L::Bo + o2) = pack_h2(kr0 * lam[d][0], kr1 * lam[d][1]);
+        }
+    }
+}
+
 // 4x4 transpose of 32-bit words across each quad of lanes: on entry quad lane j
 // holds x[0..3]; on exit it holds x[p] = (x[j] of quad lane p).  Two butterfly
 // stages: lanes j and j ^ 2 swap the 2x2 blocks off the diagonal, then lanes j and
@@ -338,25 +366,14 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
         }
     }
     if (guard_local) *sFlag = 1;
-    // Intra operands (rows of this half block, two channels per 32-bit word).
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-        const int row = 8 * hb + rr;
-        const float q0 = bf_lo(qw[rr]), q1 = bf_hi(qw[rr]);
-        const float k0 = bf_lo(kw[rr]), k1 = bf_hi(kw[rr]);
-        const int o = swz(row, 2 * cp);
-        *reinterpret_cast<uint32_t*>(smem + L::Aq + o) = pack_h2(q0 * F[rr][0], q1 * F[rr][1]);
-        *reinterpret_cast<uint32_t*>(smem + L::Ak + o) = pack_h2(k0 * F[rr][0], k1 * F[rr][1]);
-        const float kr0 = k0 * R[rr][0], kr1 = k1 * R[rr][1];
-        *reinterpret_cast<uint32_t*>(smem + L::Bd + o) = pack_h2(kr0 * invr[0], kr1 * invr[1]);
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            const int I2 = Ib + 1 + d;
-            if (I2 < 4) {
-                const int o2 = swz(16 * pair_index(I2, Ib) + (row & 15), 2 * cp);
-                *reinterpret_cast<uint32_t*>(smem + L::Bo + o2) = pack_h2(kr0 * lam[d][0], kr1 * lam[d][1]);
-            }
-        }
+    // Intra operands (rows of this half block, two channels per 32-bit word); one
+    // copy of the loop per block, so that each wave writes its 3 - Ib off-diagonal
+    // operands without a branch per row.
+    switch (Ib) {
+        case 0: write_operands<0>(smem, qw, kw, F, R, invr, lam, hh, cp); break;
+        case 1: write_operands<1>(smem, qw, kw, F, R, invr, lam, hh, cp); break;
+        case 2: write_operands<2>(smem, qw, kw, F, R, invr, lam, hh, cp); break;
+        default: write_operands<3>(smem, qw, kw, F, R, invr, lam, hh, cp); break;
     }
     // The scan kernel's operands of this chunk, straight to the record.  scale q e^G
     // and -(k e^G) go out as 16-byte row pieces of 8 channels, gathered from the
