@@ -421,6 +421,11 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     // 20 jobs of 16x16 output tiles: (matrix, I, J) with J <= I.  Each tile is
     // computed transposed (rows j, cols i) so that a lane holds 4 consecutive j of
     // one row i.
+    // Lane l reads, in k step kk, the 16-byte piece 4 kk + l / 16 of row l % 16 of
+    // a 16-row operand block: the same swizzled offset within every block.
+    int swo[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) swo[kk] = swz_piece(lane & 15, 4 * kk + (lane >> 4));
     f32x4 iacc[3];
     int jobI[3], jobJ[3], jobM[3];
 #pragma unroll
@@ -432,18 +437,18 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
             const int I = pidx >= 6 ? 3 : (pidx >= 3 ? 2 : (pidx >= 1 ? 1 : 0));
             const int J = pidx - I * (I + 1) / 2;
             jobM[u] = m; jobI[u] = I; jobJ[u] = J;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int rb = (I == J) ? 16 * J + (lane & 15) : 16 * pair_index(I, J) + (lane & 15);
-            const int baseB = (I == J) ? L::Bd : L::Bo;
-            const int ra = 16 * I + (lane & 15);
-            const int baseA = m == 0 ? L::Aq : L::Ak;
+            const int baseB = (I == J) ? L::Bd + 16 * J * 256 : L::Bo + 16 * pair_index(I, J) * 256;
+            const int baseA = (m == 0 ? L::Aq : L::Ak) + 16 * I * 256;
+            // all eight operand pieces first, then the four MFMAs
+            half8 a[4], b[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int kc = 4 * kk + (lane >> 4);
-                const half8 a = lds_h8(smem, baseB + swz_piece(rb, kc));
-                const half8 b = lds_h8(smem, baseA + swz_piece(ra, kc));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+                a[kk] = lds_h8(smem, baseB + swo[kk]);
+                b[kk] = lds_h8(smem, baseA + swo[kk]);
             }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kk], b[kk], acc, 0, 0, 0);
             iacc[u] = acc;
         }
     }
