@@ -231,6 +231,14 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
         for (int kk = 0; kk < 8; ++kk) hf[kk] = lds_h8(ps, L::HT + (cl * S136 + 16 * kk + 8 * hl) * 2);
     };
 
+    // Z's accumulator layout gathers four consecutive tokens of one column per lane
+    // (register 4 q + e of tile m: token 32 m + 8 q + 4 hl + e, column cl).  One
+    // transposing LDS read (ds_read_b64_tr_b16) per (m, q) delivers them: in each
+    // group of 16 lanes, lane 4 a + b receives element b of the 8-byte pieces
+    // addressed by lanes a, a + 4, a + 8, a + 12 of the group, so lane s addresses
+    // token 32 m + 8 q + 4 (s / 32) + (s / 4) % 4, columns 16 ((s / 16) % 2) + 4 (s % 4) ..
+    const int vs_lane = (4 * (lane >> 5) + ((lane >> 2) & 3)) * DVW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
     // v of chunk c (the pair's 32 columns) into the pair's Vs by DMA (chain wave):
     // four 1 KB pieces, lane l of piece u taking token 16 u + l / 4, channels
     // 8 (l % 4) .. + 7, so Vs is row-major [token][32].  Rows past the sequence end
@@ -347,9 +355,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int tok = 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    z[m][r] = bf2f(*reinterpret_cast<const uint16_t*>(ps + L::Vs + (tok * DVW + cl) * 2));
+                for (int q = 0; q < 4; ++q) {
+                    const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16*)(ps + L::Vs + (vs_lane + (32 * m + 8 * q) * DVW) * 2));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[m][4 * q + e] = bf2f((uint16_t)t[e]);
                 }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
