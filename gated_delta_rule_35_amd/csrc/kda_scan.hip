@@ -1,6 +1,6 @@
 // State-dependent stages of the KDA chunked forward for gfx950 (MI355X, CDNA4).
 //
-// One work-group of four wave64s owns one (sequence, value head, 64-wide dv
+// One work-group of six wave64s owns one (sequence, value head, 64-wide dv
 // slice) and walks that sequence's chunks of 64 tokens in order.  Per chunk it
 // runs the stages that depend on the recurrent state ("cuLA PR #131:
 // SM100/SM103 KDA forward to pure CuTeDSL", Summary: recompute W/U; "cuLA
@@ -12,14 +12,15 @@
 //   a6     o = (scale q e^G) h + Aqk v_new
 //
 // Everything state-independent comes from the intra kernel's workspace record of
-// the chunk, stored as MFMA operand fragments.  The work-group copies each record
+// the chunk, stored as MFMA operand fragments.  Two loader waves copy each record
 // once into LDS by DMA (buffer loads that write LDS directly), two chunks ahead,
-// double-buffered; every wave then reads its fragments from there.  v comes the
+// double-buffered, between the two barriers of each chunk; every compute wave then
+// reads its fragments from there.  v comes the
 // same way, one chunk ahead.  The kernel reads only v and the records from
 // memory, and writes o and the final state; its loops hold no loads into
 // registers, so every wait for memory is an explicit, counted one.
 //
-// Roles.  Two wave pairs, each owning 32 dv columns.  A pair's state h (128 x 32,
+// Roles.  Two wave pairs, each owning 32 dv columns, and two loader waves.  A pair's state h (128 x 32,
 // fp32) is split by rows between its two waves, which keep their 32 x 32 tiles
 // in MFMA accumulators for the whole sequence; only fp16 copies of h and v_new
 // cross between them, through LDS.  Per chunk:
@@ -32,8 +33,10 @@
 //   both:         own state rows h <- e^{G_last} h + Khat^T v_new; fp16 h^T -> LDS
 //   barrier
 //   output wave:  o^T += v_new^T Aqk^T; o stored (bf16) straight from the
-//                 accumulators, four channels per lane store; the record DMA of
-//                 chunk + 2 into the buffer this chunk was read from
+//                 accumulators, four channels per lane store
+//   loader waves: after the first barrier, the record DMA of chunk + 2 into the
+//                 buffer this chunk was read from; before the second, wait for
+//                 chunk + 1's
 // All products run on v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulate).
 #include "kda_device.h"
 
@@ -41,7 +44,7 @@ namespace kda {
 
 namespace {
 
-constexpr int SCAN_THREADS = 256;   // four waves: two (chain, output) pairs
+constexpr int SCAN_THREADS = 384;   // two (chain, output) pairs and two record loaders
 constexpr int DVW = 32;             // dv columns per pair
 constexpr int PAIRS = 2;
 constexpr int SLICES = DK / (DVW * PAIRS);                   // work-groups per (sequence, head)
@@ -100,7 +103,8 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int pr = wave >> 1, role = wave & 1;   // pair; role 0: chain, 1: output
+    const int pr = (wave >> 1) & 1, role = wave & 1;   // pair; role 0: chain, 1: output (waves 0..3)
+    const bool loader = wave >= 4;                   // waves 4, 5: record DMA
     const int hl = lane >> 5, cl = lane & 31;
     char* const ps = smem + L::Pair + pr * L::PAIR_BYTES;   // this pair's LDS
 
@@ -144,10 +148,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     };
 
     // ---- record DMA ----
-    // Chunk c's record into LDS buffer b, by the two output waves (which have slack
-    // at the end of each chunk): 1 KB pieces, lane l's 16 bytes to byte 16 l of a
-    // piece; the output wave of pair 0 takes pieces 0 .. 29, that of pair 1 pieces
-    // 30 .. 60.  The loads are issued as inline assembly so that the compiler, which
+    // Chunk c's record into LDS buffer b, by the two loader waves: 1 KB pieces, lane
+    // l's 16 bytes to byte 16 l of a piece; loader 0 takes pieces 0 .. 29, loader 1
+    // pieces 30 .. 60.  The loads are issued as inline assembly so that the compiler, which
     // cannot tell them apart from the fragment reads of the other buffer, adds no
     // waits; their completion is awaited explicitly before the barrier that
     // publishes them.  Four consecutive pieces share one write of M0 (the LDS
@@ -163,10 +166,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     auto dma_record = [&](int64_t c, int b) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(p.ws + ((slot0 + c) * p.Hv + hv) * WS_RECORD_BYTES,
                                                    chunk_rows(c) ? WS_RECORD_BYTES : 0);
-        uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + pr * 30 * WS_FRAG);
-        uint32_t soff = pr * 30 * WS_FRAG;
+        const int lr = wave & 1;   // loader 0: pieces 0 .. 29, loader 1: 30 .. 60
+        uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + lr * 30 * WS_FRAG);
+        uint32_t soff = lr * 30 * WS_FRAG;
         const int vlane = lane * 16;
-        // pieces 30 pr .. 30 pr + 29: seven groups of four, then two
+        // pieces 30 lr .. 30 lr + 29: seven groups of four, then two
         asm volatile(
             "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
             : "+s"(m0), "+s"(soff)
             : "v"(vlane), "s"(r)
             : "memory", "scc");
-        if (pr == 1) {   // piece 60
+        if (lr == 1) {   // piece 60
             const uint32_t m60 = __builtin_amdgcn_readfirstlane(lds_rec + b * REC_LDS + 60 * WS_FRAG);
             const int vlast = 60 * WS_FRAG + vlane;
             asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m60), "v"(vlast),
@@ -191,6 +195,25 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
                          : "memory");
         }
     };
+    if (loader) {
+        // Record loaders: chunk c + 2's record into buffer c % 2 once the first barrier
+        // of chunk c has passed (the buffer's last reads came before it); before the
+        // second barrier, the record of chunk c + 1 (the older DMA) is complete.
+        if (nch > 0) {
+            dma_record(0, 0);
+            dma_record(1, 1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        for (int64_t c = 0; c < nch; ++c) {
+            lds_barrier();   // first barrier of chunk c
+            dma_record(c + 2, (int)(c & 1));
+            if (wave == 4) asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(31)" ::: "memory");
+            lds_barrier();   // second barrier of chunk c: chunk c + 1's record complete
+        }
+        return;
+    }
     auto frag = [&](int b, int off) -> half8 {
         return *reinterpret_cast<const half8*>(smem + L::Rec + b * REC_LDS + off + lane * 16);
     };
@@ -259,14 +282,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     };
 
     write_ht();
-    if (nch > 0) {
-        if (role == 1) {
-            dma_record(0, 0);
-            dma_record(1, 1);
-        } else {
-            dma_v(0);
-        }
-    }
+    if (nch > 0 && role == 0) dma_v(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();   // h^T, the first two records and the first chunk's v complete
     read_ht();
@@ -331,10 +347,6 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
             hacc[1] = mfma32(fkh[4 + kk], vf[kk], hacc[1]);
         }
         write_ht();
-        // Chunk c + 1's record DMA (issued by the output wave at the end of the last
-        // chunk, its latest memory operations) must be complete before the barrier
-        // publishes it.
-        if (role == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();   // h^T and chunk c + 1's record complete; reads of v_new^T and the old h^T done
         read_ht();
     };
@@ -457,9 +469,6 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
                     }
                 }
             }
-            // Record of chunk c + 2 into buffer b, whose last reads came before the
-            // first barrier.
-            dma_record(c + 2, b);
         }
     }
 
