@@ -48,7 +48,11 @@ RECORD_BYTES = 61952   # workspace record per (chunk, value head)
 # The pages' own time for this exact workload ("cuLA PR #131: SM100/SM103 KDA
 # forward to pure CuTeDSL", Performance table, fp32 beta, T=8192, B=2, H=64,
 # CuTeDSL column), measured on NVIDIA SM100/SM103: context, not the target.
-PAGES_MS = {"mha_b2_h64_t8192": 0.8564}
+PAGES_MS = {"mha_b2_h64_t8192": 0.8564,
+            # the same table: fp32 beta rows for T = 512, 1024, 4096; bf16 beta for T = 4096
+            # without initial state; the grouped-value row (bf16 beta)
+            "mha_b2_h64_t512": 0.0810, "mha_b2_h64_t1024": 0.1326, "mha_b2_h64_t4096_h0": 0.4263,
+            "mha_b2_h64_t4096": 0.4362, "gva_b1_hq16_hv64_t4096": 0.2379}
 KERNELS = ("kda_intra_kernel", "kda_scan_kernel")
 
 
