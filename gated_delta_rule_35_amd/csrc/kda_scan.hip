@@ -150,10 +150,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     // ---- record DMA ----
     // Chunk c's record into LDS buffer b, by the two loader waves: 1 KB pieces, lane
     // l's 16 bytes to byte 16 l of a piece; loader 0 takes pieces 0 .. 29, loader 1
-    // pieces 30 .. 60.  The loads are issued as inline assembly so that the compiler, which
-    // cannot tell them apart from the fragment reads of the other buffer, adds no
-    // waits; their completion is awaited explicitly before the barrier that
-    // publishes them.  Four consecutive pieces share one write of M0 (the LDS
+    // pieces 30 .. 60.  The loads are issued as inline assembly, so the compiler
+    // adds no waits for them; their completion is awaited explicitly (counted)
+    // before the barrier that publishes them.  Four consecutive pieces share one write of M0 (the LDS
     // address; writing it stalls the DMA issue): the instruction offset 0, 1 K,
     // 2 K or 3 K moves both the global and the LDS address.  A write of M0 is
     // followed by one other instruction before the DMA that uses it.
@@ -208,6 +207,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
         for (int64_t c = 0; c < nch; ++c) {
             lds_barrier();   // first barrier of chunk c
             dma_record(c + 2, (int)(c & 1));
+            // all but the DMA just issued (30 loads on loader 0, 31 on loader 1)
             if (wave == 4) asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
             else asm volatile("s_waitcnt vmcnt(31)" ::: "memory");
             lds_barrier();   // second barrier of chunk c: chunk c + 1's record complete
