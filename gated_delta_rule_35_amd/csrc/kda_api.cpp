@@ -51,6 +51,17 @@ kda_status_t check_tensor(const kda_tensor_t* t, int ndim, kda_dtype_t d0, kda_d
     return KDA_OK;
 }
 
+// Two state arrays of `bytes` each that share memory without starting at the
+// same address.  A state may be updated in place, or written elsewhere; with a
+// partial overlap one work-group's writes would land in tiles another has not
+// read yet.
+bool partly_overlap(const void* in, const void* out, int64_t bytes) {
+    if (in == out || bytes <= 0) return false;
+    const char* a = static_cast<const char*>(in);
+    const char* b = static_cast<const char*>(out);
+    return a < b + bytes && b < a + bytes;
+}
+
 bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
     for (int i = 0; i < nd; ++i)
         if (a->shape[i] != s[i]) return false;
@@ -93,6 +104,7 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (h0 && !same_shape(h0, ss, 4)) return KDA_ERR_SHAPE;
     if (hT && !same_shape(hT, ss, 4)) return KDA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
+    if (h0 && hT && partly_overlap(h0->data, hT->data, N * Hv * kHeadDim * kHeadDim * 4)) return KDA_ERR_LAYOUT;
     // Per-block byte offsets of the kernel's buffer loads are 32-bit.
     if (Hv > (int64_t(1) << 16) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
     const int S = kda::scan_slices();
@@ -230,14 +242,8 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
     if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
     if (N * Hv > (int64_t(1) << 31) - 1) return KDA_ERR_UNSUPPORTED;
-    // The new state may overwrite the old one in place, or go elsewhere; a partial
-    // overlap would let one work-group's writes reach another's unread rows.
-    if (state_in && state_in->data != state_out->data) {
-        const char* a = static_cast<const char*>(state_in->data);
-        const char* b = static_cast<const char*>(state_out->data);
-        const int64_t bytes = N * Hv * kHeadDim * kHeadDim * 4;
-        if (a < b + bytes && b < a + bytes) return KDA_ERR_LAYOUT;
-    }
+    if (state_in && partly_overlap(state_in->data, state_out->data, N * Hv * kHeadDim * kHeadDim * 4))
+        return KDA_ERR_LAYOUT;
 
     kda::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q->data);

@@ -95,7 +95,8 @@ int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int6
  * Results are bitwise reproducible from call to call (no atomics; each output
  * element has exactly one writer and a fixed reduction order).
  * initial_state may alias final_state (each state tile is read before it is
- * written, by the same work-group).
+ * written, by the same work-group); a partial overlap of the two returns
+ * KDA_ERR_LAYOUT.
  * workspace: device memory of at least kda_fwd_workspace_size() bytes,
  * 16-byte aligned, owned by the caller and not used by anything else until the
  * call's work on `stream` has finished; its contents need no initialisation.

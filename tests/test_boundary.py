@@ -133,6 +133,16 @@ def test_layout(lib):
     expect(lib, a, "KDA_ERR_LAYOUT")
 
 
+def test_partly_overlapping_states(lib):
+    a = good(B=2)
+    st = lambda off: T([2, 2, 128, 128], binding.KDA_F32, data=FAKE + off)  # noqa: E731
+    expect(lib, a, "KDA_ERR_LAYOUT", h0=st(0), hT=st(64 * 1024), ws=FAKE, ws_size=0)
+    expect(lib, a, "KDA_ERR_LAYOUT", h0=st(64 * 1024), hT=st(0), ws=FAKE, ws_size=0)
+    # in place, or fully apart: the workspace check is the next one to fail
+    expect(lib, a, "KDA_ERR_WORKSPACE", h0=st(0), hT=st(0), ws=FAKE, ws_size=0)
+    expect(lib, a, "KDA_ERR_WORKSPACE", h0=st(0), hT=st(4 * 2 * 2 * 128 * 128), ws=FAKE, ws_size=0)
+
+
 def test_scale_value(lib):
     for s in (0.0, -1.0, float("inf"), float("nan")):
         expect(lib, good(), "KDA_ERR_VALUE", scale=s)
