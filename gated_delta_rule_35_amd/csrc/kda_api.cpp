@@ -45,9 +45,10 @@ kda_status_t check_tensor(const kda_tensor_t* t, int ndim, kda_dtype_t d0, kda_d
     for (int i = 0; i < ndim; ++i)
         if (t->shape[i] < 0) return KDA_ERR_SHAPE;
     const int64_t n = numel(t);
-    if (n > 0 && !t->data) return KDA_ERR_NULL;
+    if (n == 0) return KDA_OK;   // addresses no element: data and strides are not used
+    if (!t->data) return KDA_ERR_NULL;
     if (!contiguous(t)) return KDA_ERR_LAYOUT;
-    if (n > 0 && (reinterpret_cast<uintptr_t>(t->data) % align) != 0) return KDA_ERR_LAYOUT;
+    if ((reinterpret_cast<uintptr_t>(t->data) % align) != 0) return KDA_ERR_LAYOUT;
     return KDA_OK;
 }
 

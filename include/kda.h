@@ -24,7 +24,8 @@
  * Tensors are described by kda_tensor_t: a device pointer, a dtype, a rank
  * and per-dimension sizes and strides counted in elements.  All tensors must
  * be dense row-major (contiguous) and their data 16-byte aligned (beta and
- * cu_seqlens: aligned to their element size).  The caller owns all memory it
+ * cu_seqlens: aligned to their element size); a tensor with no elements may
+ * have any strides and a NULL pointer.  The caller owns all memory it
  * passes; the library keeps no pointer after a call returns.
  *
  * Shapes (B batch rows, T tokens per row, Hq query/key heads, Hv value heads,
@@ -109,7 +110,10 @@ int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int6
  * Precision: q, k, v are bf16; the MFMA operands derived from them are fp16
  * and all accumulation, the gate cumsum, the inversion and the state are
  * fp32.  A chunk whose decay within a 16-token block exceeds exp(-8) on some
- * channel takes an exact fp32 path for its diagonal blocks.
+ * channel takes an exact fp32 path for its diagonal blocks.  The fp16
+ * operands bound the range: entries of the state and of v_new must stay
+ * below 65504 in magnitude (L2-normalised q and k, values of order one and
+ * g <= 0 keep them orders of magnitude below it).
  */
 kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                      const kda_tensor_t* g, const kda_tensor_t* beta, float scale,

@@ -154,6 +154,17 @@ def test_empty_problem_needs_no_launch(lib):
         a[key].data = None
     expect(lib, a, "KDA_OK")
     expect(lib, good(), "KDA_OK", cu=T([1], binding.KDA_I32))  # zero sequences
+    # torch gives an empty tensor the strides of a size-1 dimension in its place:
+    # an empty tensor addresses no element, so its strides are not checked
+    a = good(B=2, T_=0)
+    for key in ("q", "k", "v", "g", "beta", "out"):
+        sh = [a[key].shape[i] for i in range(a[key].ndim)]
+        st, acc = [], 1
+        for n in reversed(sh):
+            st.insert(0, acc)
+            acc *= max(n, 1)
+        a[key] = T(sh, a[key].dtype, data=None, strides=st)
+    expect(lib, a, "KDA_OK")
 
 
 def test_status_strings(lib):

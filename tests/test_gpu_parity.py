@@ -110,6 +110,45 @@ def test_strong_decay_takes_exact_path():
     check_against_oracle(x, label="strong decay")
 
 
+@pytest.mark.parametrize("case", ["beta0", "g0", "beta0_g0", "q0", "kv_memory"])
+def test_degenerate_cases(case):
+    """The recurrence's degenerate cases: beta = 0 (no write, the state only
+    decays), g = 0 (no decay, the plain delta rule), both (the state passes through
+    unchanged), q = 0 (zero output) and the key-value memory (g = 0, beta = 1,
+    one-hot keys e_(t mod 128): each write replaces one key's value)."""
+    _say(f"degenerate case {case}: B=2 H=2 T=150")
+    x = make_inputs(2, 150, 2, 2, torch.float32, h0=case != "kv_memory", seed=21)
+    if case.startswith("beta0"):
+        x["beta"].zero_()
+    if case.endswith("g0"):
+        x["g"].zero_()
+    if case == "q0":
+        x["q"].zero_()
+    if case == "kv_memory":
+        x["g"].zero_()
+        x["beta"].fill_(1.0)
+        x["k"].zero_()
+        t = torch.arange(150)
+        x["k"][:, t, :, t % 128] = 1.0
+    o, hT = check_against_oracle(x, label=case)
+    if case == "beta0_g0":   # v_new is exactly zero and the decay exactly one
+        assert np.array_equal(hT, x["h0"].numpy())
+    if case == "q0":
+        assert not np.any(o)
+
+
+def test_zero_length_batch_passes_the_state_through():
+    _say("B=2 H=3 T=0 with h0 and final_state")
+    x = make_inputs(2, 0, 3, 3, torch.float32, h0=True, seed=22)
+    o, hT = run_gpu(x)
+    assert o.shape == (2, 0, 3, 128)
+    assert np.array_equal(hT, x["h0"].numpy())
+    d = to_device(x)
+    _, hT0 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, final_state=True)
+    torch.cuda.synchronize()
+    assert not torch.any(hT0)   # no initial state: a zero final state
+
+
 def test_stage_intermediates_match_oracle_chunked_form():
     """Stage-by-stage parity (gate cumsum, Aqk, Akk, T, W, U, v_new, chunk states)
     against the oracle's chunked form on a small case with tails."""
