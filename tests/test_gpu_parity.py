@@ -339,6 +339,22 @@ def test_many_sequences_random_lengths():
 
 # ---- the named workloads at their full sizes, checked on sampled heads ----
 
+def test_long_sequence_carries_the_state_over_1024_chunks():
+    _say("long sequence B=1 H=2 T=65536 (1024 chunks) with h0")
+    x = make_inputs(1, 65536, 2, 2, torch.float32, h0=True, seed=31)
+    check_against_oracle(x, label="T=65536")
+
+
+def test_wide_grid_many_grouped_heads():
+    """Hv = 1024 value heads over Hq = 256 q/k heads: 2048 scan work-groups and
+    the grouped item mapping far from the small-head cases; the oracle checks
+    heads spread over the range, including the first and last of a group."""
+    heads = [0, 3, 4, 511, 1020, 1023]
+    _say(f"wide grid B=2 T=80 Hq=256 Hv=1024, oracle on heads {heads}")
+    x = make_inputs(2, 80, 256, 1024, torch.bfloat16, h0=True, seed=32)
+    check_against_oracle(x, heads=heads, Hq=256, Hv=1024, label="Hv=1024")
+
+
 FULL = [
     ("mha_b2_h64_t4096", [0, 17, 63]),
     ("mha_b2_h64_t8192", [5, 40]),
