@@ -16,14 +16,14 @@ once, o written once, the initial state read if given, the final state
 written) divided by the summed average durations of the two kernels, against
 8 TB/s.  Each kernel is also reported against its own algorithmic bytes (what
 it must move in this design: the intra kernel reads q, k, g, beta and writes
-one 59,904-byte record per chunk and value head; the scan kernel reads v and
+one 61,952-byte record per chunk and value head; the scan kernel reads v and
 the records and writes o and the states).  The MFMA side uses the
 algorithmic flop count of the chunked method (4,512,416 MAC per full 64-token
 chunk and value head).
 
 cpu_baseline: the fp64 CPU oracle (token recurrence, OpenMP over sequence x head)
-timed on a bounded sample of the same workload, scaled to tokens/s of the full
-head count.
+timed on a bounded sample of the same workload (by default all of it, run
+repeatedly for at least 10 s), scaled to tokens/s of the full head count.
 """
 import argparse
 import hashlib
@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--workload", default="mha_b2_h64_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64, help="value heads in the oracle's timing sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the oracle's sample is run repeatedly until this much wall time has passed")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="instead of the forward, time kda_decode: one step for N sequences x 64 heads")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -274,15 +276,20 @@ def main():
                    beta=x["beta"][:, :, hs], h0=x["h0"][:, hs] if x["h0"] is not None else None)
         # widen to fp64 before the clock starts: the conversion is marshalling, not the oracle
         sub = {k: (v.to(torch.float64).contiguous().numpy() if v is not None else None) for k, v in sub.items()}
-        log(f"cpu baseline: oracle on {len(hs)} of {w.Hv} value heads, all {N} sequences")
-        t0 = time.perf_counter()
-        oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale, cu_seqlens=cu, h0=sub["h0"])
-        cpu_s = time.perf_counter() - t0
-        cpu_tok = n_tok * len(hs) / w.Hv / cpu_s
+        log(f"cpu baseline: oracle on {len(hs)} of {w.Hv} value heads, all {N} sequences, repeated for "
+            f">= {args.cpu_seconds:.0f} s")
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale, cu_seqlens=cu, h0=sub["h0"])
+            reps += 1
+            cpu_s = time.perf_counter() - t0
+            if cpu_s >= args.cpu_seconds:
+                break
+        cpu_tok = n_tok * len(hs) / w.Hv * reps / cpu_s
         cpu = {"value": round(cpu_tok, 1), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"fp64 token recurrence over value heads 0..{len(hs) - 1} of {w.Hv} (all {N} sequences, "
-                         f"{n_tok} tokens each head) in {cpu_s:.1f} s, scaled to {w.Hv} heads"}
-        log(f"cpu baseline {cpu_tok:.1f} tokens/s on {cpu['cores']} threads ({cpu_s:.1f} s)")
+                         f"{n_tok} tokens each head), {reps} runs in {cpu_s:.1f} s, scaled to {w.Hv} heads"}
+        log(f"cpu baseline {cpu_tok:.1f} tokens/s on {cpu['cores']} threads ({reps} runs, {cpu_s:.1f} s)")
 
     rec = {
         "metric": METRIC,
