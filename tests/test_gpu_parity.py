@@ -365,7 +365,26 @@ FULL = [
 
 @pytest.mark.parametrize("name,heads", FULL)
 def test_full_size_workloads_on_sampled_heads(name, heads):
+    """Every head of the full workload runs; the oracle checks the sampled ones.
+    The two stage calls with a caller workspace (the launch configuration
+    bench.py times) must then give kda_fwd's results bit for bit."""
+    from gated_delta_rule_35_amd import kda_fwd_intra, kda_fwd_scan, kda_fwd_workspace_size
     w = WORKLOADS[name]
     _say(f"full workload {name}, oracle on heads {heads}")
     x, cu = workload_inputs(w)
     check_against_oracle(x, cu, heads=heads, Hq=w.Hq, Hv=w.Hv, scale=w.scale, label=name)
+    _say(f"full workload {name}: stage calls vs kda_fwd, bitwise")
+    d = to_device(x)
+    cu_d = cu.to("cuda") if cu is not None else None
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                     final_state=True)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    ws = torch.empty(kda_fwd_workspace_size(B * T, h1.shape[0], w.Hv), dtype=torch.uint8, device="cuda")
+    o2, h2 = torch.empty_like(o1), torch.empty_like(h1)
+    kda_fwd_intra(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
+                  out=o2, final_state=h2)
+    kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
+                 out=o2, final_state=h2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
