@@ -154,6 +154,113 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def oracle_cpu_baseline(x, cu, w, N, n_tok, scale, seconds, heads):
+    """The fp64 oracle (token recurrence) on value heads 0 .. heads-1 of the
+    workload, run repeatedly for at least `seconds`; tokens/s scaled to all heads."""
+    import torch
+    import oracle
+    hs = list(range(min(heads, w.Hv)))
+    group = w.Hv // w.Hq
+    qk = [h // group for h in hs]
+    sub = dict(q=x["q"][:, :, qk], k=x["k"][:, :, qk], v=x["v"][:, :, hs], g=x["g"][:, :, hs],
+               beta=x["beta"][:, :, hs], h0=x["h0"][:, hs] if x["h0"] is not None else None)
+    # widen to fp64 before the clock starts: the conversion is marshalling, not the oracle
+    sub = {k: (v.to(torch.float64).contiguous().numpy() if v is not None else None) for k, v in sub.items()}
+    log(f"cpu baseline: oracle on {len(hs)} of {w.Hv} value heads, all {N} sequences, repeated for >= {seconds:.0f} s")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale, cu_seqlens=cu, h0=sub["h0"])
+        reps += 1
+        cpu_s = time.perf_counter() - t0
+        if cpu_s >= seconds:
+            break
+    cpu_tok = n_tok * len(hs) / w.Hv * reps / cpu_s
+    cpu = {"value": round(cpu_tok, 1), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+           "sample": f"fp64 token recurrence over value heads 0..{len(hs) - 1} of {w.Hv} (all {N} sequences, "
+                     f"{n_tok} tokens each head), {reps} runs in {cpu_s:.1f} s, scaled to {w.Hv} heads"}
+    log(f"cpu baseline {cpu_tok:.1f} tokens/s on {cpu['cores']} threads ({reps} runs, {cpu_s:.1f} s)")
+    return cpu
+
+
+def bench_cp(args):
+    """kda_fwd_cp (the segmented forward) on a fixed-length workload with few heads:
+    HIP events around each whole call (intra kernel, two scan launches and the
+    composition) on its stream, and kda_fwd on the same inputs for comparison."""
+    import torch
+    from gated_delta_rule_35_amd import (kda_fwd, kda_fwd_cp, kda_fwd_cp_segment_chunks, kda_fwd_cp_workspace_size,
+                                         kda_fwd_workspace_size)
+    from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
+    if args.gpus != 1:
+        print("bench.py measures one GPU only", file=sys.stderr, flush=True)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    if w.varlen_total:
+        print("the segmented forward takes fixed-length batches only", file=sys.stderr, flush=True)
+        sys.exit(2)
+    log(f"generating inputs for {w.name}")
+    x, _ = workload_inputs(w)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    n_tok = B * T
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    out = torch.empty_like(d["v"])
+    hT = torch.empty((B, w.Hv, 128, 128), dtype=torch.float32, device=dev)
+    L = args.cp if args.cp > 0 else kda_fwd_cp_segment_chunks(B, T, w.Hv)
+    if L <= 0:
+        print(f"{w.name}: the segment heuristic picks the ordinary path (B * Hv fills the GPU or T is short); "
+              "pass --cp N to force N chunks per segment", file=sys.stderr, flush=True)
+        sys.exit(2)
+    P = -(-((T + 63) // 64) // L)
+    ws_cp = torch.empty(kda_fwd_cp_workspace_size(B, T, w.Hv, L), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda_fwd_workspace_size(B * T, B, w.Hv), dtype=torch.uint8, device=dev)
+    a = (d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(call):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            call()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        return wall / args.steps * 1e3, sum(ms) / len(ms)
+
+    log(f"kda_fwd_cp: {L} chunks per segment, {P} segments per row; {args.steps} steps")
+    step_ms, call_ms = timed(lambda: kda_fwd_cp(*a, L, initial_state=d["h0"], out=out, final_state=hT, workspace=ws_cp))
+    log(f"kda_fwd (ordinary): {args.steps} steps")
+    plain_step_ms, plain_call_ms = timed(lambda: kda_fwd(*a, initial_state=d["h0"], out=out, final_state=hT,
+                                                         workspace=ws))
+    log(f"segmented {call_ms:.4f} ms/call, ordinary {plain_call_ms:.4f} ms/call ({plain_call_ms / call_ms:.2f}x)")
+    beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
+    nbytes = algorithmic_bytes(n_tok, B, w.Hq, w.Hv, beta_bytes, w.has_h0)
+    gbs = nbytes / (call_ms / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = oracle_cpu_baseline(x, None, w, B, n_tok, w.scale, args.cpu_seconds, args.cpu_heads)
+    rec = {"metric": "KDA fwd tokens/s, segmented scan (context parallelism inside one GPU); ms/call",
+           "value": round(n_tok / (step_ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": w.name, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128, "chunk": 64,
+                      "segment_chunks": L, "segments_per_row": P,
+                      "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0)},
+           "call_ms_avg": round(call_ms, 5), "ordinary_kda_fwd_ms_avg": round(plain_call_ms, 5),
+           "speedup_vs_ordinary": round(plain_call_ms / call_ms, 3),
+           "algorithmic_bytes_per_step": nbytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "scope": "whole segmented forward: the forward's algorithmic bytes over the average duration "
+                                 "of a call (all its launches)"},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +273,9 @@ def main():
                     help="the oracle's sample is run repeatedly until this much wall time has passed")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="instead of the forward, time kda_decode: one step for N sequences x 64 heads")
+    ap.add_argument("--cp", type=int, default=-1, metavar="L",
+                    help="instead of the headline, time kda_fwd_cp on --workload with L chunks per segment "
+                         "(0: the library's suggestion) against kda_fwd")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the benchmark, run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -180,6 +290,9 @@ def main():
         return
     if args.decode:
         bench_decode(args)
+        return
+    if args.cp >= 0:
+        bench_cp(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -268,28 +381,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        hs = list(range(min(args.cpu_heads, w.Hv)))
-        group = w.Hv // w.Hq
-        qk = [h // group for h in hs]
-        sub = dict(q=x["q"][:, :, qk], k=x["k"][:, :, qk], v=x["v"][:, :, hs], g=x["g"][:, :, hs],
-                   beta=x["beta"][:, :, hs], h0=x["h0"][:, hs] if x["h0"] is not None else None)
-        # widen to fp64 before the clock starts: the conversion is marshalling, not the oracle
-        sub = {k: (v.to(torch.float64).contiguous().numpy() if v is not None else None) for k, v in sub.items()}
-        log(f"cpu baseline: oracle on {len(hs)} of {w.Hv} value heads, all {N} sequences, repeated for "
-            f">= {args.cpu_seconds:.0f} s")
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale, cu_seqlens=cu, h0=sub["h0"])
-            reps += 1
-            cpu_s = time.perf_counter() - t0
-            if cpu_s >= args.cpu_seconds:
-                break
-        cpu_tok = n_tok * len(hs) / w.Hv * reps / cpu_s
-        cpu = {"value": round(cpu_tok, 1), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"fp64 token recurrence over value heads 0..{len(hs) - 1} of {w.Hv} (all {N} sequences, "
-                         f"{n_tok} tokens each head), {reps} runs in {cpu_s:.1f} s, scaled to {w.Hv} heads"}
-        log(f"cpu baseline {cpu_tok:.1f} tokens/s on {cpu['cores']} threads ({reps} runs, {cpu_s:.1f} s)")
+        cpu = oracle_cpu_baseline(x, cu, w, N, n_tok, scale, args.cpu_seconds, args.cpu_heads)
 
     rec = {
         "metric": METRIC,

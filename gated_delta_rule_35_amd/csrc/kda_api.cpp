@@ -69,10 +69,12 @@ bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
     return true;
 }
 
-kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
-                 const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
-                 const kda_tensor_t* out, const kda_tensor_t* hT, void* workspace, int64_t workspace_size,
-                 const kda_trace_t* trace, int stages, void* stream) {
+// Every host-side check of a forward call (tensors, shapes, sizes), and the kernel
+// parameters it implies; the workspace is checked by the caller.
+kda_status_t prepare(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                     const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
+                     const kda_tensor_t* out, const kda_tensor_t* hT, kda::KdaParams& p, int64_t& B, int64_t& T,
+                     int64_t& N) {
     kda_status_t st;
     if ((st = check_tensor(q, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
     if ((st = check_tensor(k, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
@@ -85,7 +87,9 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (h0 && (st = check_tensor(h0, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
     if (hT && (st = check_tensor(hT, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
 
-    const int64_t B = q->shape[0], T = q->shape[1], Hq = q->shape[2], Hv = v->shape[2];
+    B = q->shape[0];
+    T = q->shape[1];
+    const int64_t Hq = q->shape[2], Hv = v->shape[2];
     if (q->shape[3] != kHeadDim || v->shape[3] != kHeadDim) return KDA_ERR_UNSUPPORTED;
     if (!same_shape(k, q->shape, 4)) return KDA_ERR_SHAPE;
     if (v->shape[0] != B || v->shape[1] != T) return KDA_ERR_SHAPE;
@@ -95,7 +99,7 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (!same_shape(beta, bs, 3)) return KDA_ERR_SHAPE;
     if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
     if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
-    int64_t N = B;
+    N = B;
     if (cu) {
         if (B != 1) return KDA_ERR_UNSUPPORTED;
         if (cu->shape[0] < 1) return KDA_ERR_SHAPE;
@@ -108,16 +112,8 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (h0 && hT && partly_overlap(h0->data, hT->data, N * Hv * kHeadDim * kHeadDim * 4)) return KDA_ERR_LAYOUT;
     // Per-block byte offsets of the kernel's buffer loads are 32-bit.
     if (Hv > (int64_t(1) << 16) || N > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
-    const int S = kda::scan_slices();
-    if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
-    const int64_t nslots = (B * T + 63) / 64 + N;
-    if (nslots * Hv > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
-    const int64_t ws_need = kda::workspace_bytes(B * T, N, Hv);
-    if (workspace && (workspace_size < ws_need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
-        return KDA_ERR_WORKSPACE;
-    if (!workspace && stages != kBoth) return KDA_ERR_WORKSPACE;   // a lone stage needs the caller's workspace
 
-    kda::KdaParams p{};
+    p = kda::KdaParams{};
     p.q = static_cast<const uint16_t*>(q->data);
     p.k = static_cast<const uint16_t*>(k->data);
     p.v = static_cast<const uint16_t*>(v->data);
@@ -133,6 +129,36 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     p.Hq = static_cast<int32_t>(Hq);
     p.Hv = static_cast<int32_t>(Hv);
     p.scale = scale;
+    return KDA_OK;
+}
+
+kda_status_t finish(hipError_t e, hipStream_t hs) {
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (std::getenv("KDA_DEBUG_SYNC")) {
+        if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                 const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
+                 const kda_tensor_t* out, const kda_tensor_t* hT, void* workspace, int64_t workspace_size,
+                 const kda_trace_t* trace, int stages, void* stream) {
+    kda::KdaParams p;
+    int64_t B, T, N;
+    kda_status_t st = prepare(q, k, v, g, beta, scale, cu, h0, out, hT, p, B, T, N);
+    if (st != KDA_OK) return st;
+    const int64_t Hv = p.Hv;
+    const int S = kda::scan_slices();
+    if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const int64_t nslots = (B * T + 63) / 64 + N;
+    if (nslots * Hv > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    const int64_t ws_need = kda::workspace_bytes(B * T, N, Hv);
+    if (workspace && (workspace_size < ws_need || reinterpret_cast<uintptr_t>(workspace) % 16 != 0))
+        return KDA_ERR_WORKSPACE;
+    if (!workspace && stages != kBoth) return KDA_ERR_WORKSPACE;   // a lone stage needs the caller's workspace
+
     if (trace) {
         p.tr_G = trace->G;
         p.tr_Aqk = trace->Aqk;
@@ -155,12 +181,31 @@ kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_
     if (T > 0 && (stages & kIntra)) e = kda::launch_kda_intra(p, trace != nullptr, hs);
     if (e == hipSuccess && (stages & kScan)) e = kda::launch_kda_scan(p, trace != nullptr, hs);
     if (!workspace && ws && hipFreeAsync(ws, hs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
-    if (e != hipSuccess) return KDA_ERR_HIP;
-    if (std::getenv("KDA_DEBUG_SYNC")) {
-        if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERR_HIP;
-        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    return finish(e, hs);
+}
+
+// ---- segmented forward ----
+// Workspace of a segmented call: the records of all segments, then the segments'
+// state maps M and offsets b (segments 1 .. P-2) and the states entering segments
+// 1 .. P-1, each [segment][row][Hv][128][128] fp32.  With fewer than three
+// segments the call is an ordinary forward and needs kda_fwd's workspace.
+struct SegLayout {
+    int64_t P = 0, rec = 0, maps = 0, total = 0;
+};
+
+SegLayout seg_layout(int64_t B, int64_t T, int64_t Hv, int64_t seg_chunks) {
+    SegLayout c;
+    const int64_t nch = (T + 63) / 64;
+    c.P = seg_chunks > 0 ? (nch + seg_chunks - 1) / seg_chunks : 0;
+    if (c.P < 3) {
+        c.total = kda::workspace_bytes(B * T, B, Hv);
+        return c;
     }
-    return KDA_OK;
+    const int64_t blk = B * Hv * kHeadDim * kHeadDim * 4;   // one segment's states
+    c.rec = (kda::workspace_bytes(B * T, B * c.P, Hv) + 255) & ~int64_t(255);
+    c.maps = blk * (c.P - 2);
+    c.total = c.rec + 2 * c.maps + blk * (c.P - 1);
+    return c;
 }
 
 }  // namespace
@@ -214,6 +259,119 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
                trace, kBoth, stream);
 }
 
+int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks) {
+    if (batch < 0 || seq_len < 0 || num_value_heads < 0 || segment_chunks < 1) return -1;
+    return seg_layout(batch, seq_len, num_value_heads, segment_chunks).total;
+}
+
+int64_t kda_fwd_cp_segment_chunks(int64_t batch, int64_t seq_len, int64_t num_value_heads, int32_t num_cus) {
+    if (batch <= 0 || seq_len <= 0 || num_value_heads <= 0 || num_cus <= 0) return 0;
+    const int64_t nch = (seq_len + 63) / 64, per_seg = batch * num_value_heads * kda::scan_slices();
+    auto waves = [&](int64_t wgs) { return (wgs + num_cus - 1) / num_cus; };
+    // Cost in chunk steps: the scan waves of each phase times the chunks they walk,
+    // plus one step per composed map and eight for the two extra launches; the
+    // ordinary scan walks every chunk.
+    const int64_t base = waves(per_seg) * nch;
+    int64_t best = 0, best_cost = base;
+    for (int64_t P = 3; P <= 64 && P <= nch; ++P) {
+        const int64_t L = (nch + P - 1) / P, Pe = (nch + L - 1) / L;   // segments actually formed
+        if (Pe < 3) continue;
+        const int64_t cost = (waves(per_seg * (1 + 2 * (Pe - 2))) + waves(per_seg * (Pe - 1))) * L + (Pe - 2) + 8;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = L;
+        }
+    }
+    return 5 * best_cost <= 4 * base ? best : 0;   // only when it saves a fifth or more
+}
+
+kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                        const kda_tensor_t* beta, float scale, const kda_tensor_t* initial_state,
+                        const kda_tensor_t* out, const kda_tensor_t* final_state, int64_t segment_chunks,
+                        void* workspace, int64_t workspace_size, void* stream) {
+    kda::KdaParams p;
+    int64_t B, T, N;
+    kda_status_t st = prepare(q, k, v, g, beta, scale, nullptr, initial_state, out, final_state, p, B, T, N);
+    if (st != KDA_OK) return st;
+    if (segment_chunks < 1) return KDA_ERR_VALUE;
+    const int64_t Hv = p.Hv;
+    const SegLayout c = seg_layout(B, T, Hv, segment_chunks);
+    if (c.P < 3)   // one or two segments: nothing runs side by side; the ordinary path
+        return run(q, k, v, g, beta, scale, nullptr, initial_state, out, final_state, workspace, workspace_size,
+                   nullptr, kBoth, stream);
+    if (!workspace || workspace_size < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return KDA_ERR_WORKSPACE;
+    const int64_t P = c.P, nseg = B * P;
+    const int S = kda::scan_slices();
+    if (nseg > (int64_t(1) << 24)) return KDA_ERR_UNSUPPORTED;
+    const int64_t nslots = (B * T + 63) / 64 + nseg;
+    if (nslots * Hv > kMaxBlocks || (B + 2 * B * (P - 2)) * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+
+    char* ws = static_cast<char*>(workspace);
+    float* Mb = reinterpret_cast<float*>(ws + c.rec);
+    float* Bb = reinterpret_cast<float*>(ws + c.rec + c.maps);
+    float* Hin = reinterpret_cast<float*>(ws + c.rec + 2 * c.maps);
+    const int64_t blk_f = B * Hv * kHeadDim * kHeadDim;   // floats per segment of states
+    p.ws = ws;
+    p.seg_tokens = segment_chunks * 64;
+    p.seg_rows = static_cast<int32_t>(B);
+    p.seg_per_row = static_cast<int32_t>(P);
+    p.nslots = nslots;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+    // 1. intra kernel over every segment of every row
+    kda::KdaParams pi = p;
+    pi.N = static_cast<int32_t>(nseg);
+    hipError_t e = kda::launch_kda_intra(pi, false, hs);
+    // 2. side by side: segment 0 of each row from the initial state (output and its
+    //    final state), and the maps of segments 1 .. P-2: M from the identity with
+    //    v = 0, b from zero with v
+    kda::ScanJobs J1{};
+    J1.njobs = 3;
+    kda::KdaParams& j0 = J1.job[0];
+    j0 = p;
+    j0.N = static_cast<int32_t>(B);
+    j0.seg_first = 0;
+    j0.hT = Hin;
+    kda::KdaParams& jm = J1.job[1];
+    jm = p;
+    jm.N = static_cast<int32_t>(B * (P - 2));
+    jm.seg_first = 1;
+    jm.h0 = nullptr;
+    jm.h0_identity = 1;
+    jm.v_zero = 1;
+    jm.o = nullptr;
+    jm.hT = Mb;
+    kda::KdaParams& jb = J1.job[2];
+    jb = p;
+    jb.N = static_cast<int32_t>(B * (P - 2));
+    jb.seg_first = 1;
+    jb.h0 = nullptr;
+    jb.o = nullptr;
+    jb.hT = Bb;
+    if (e == hipSuccess) e = kda::launch_kda_scan_jobs(J1, hs);
+    // 3. the states entering segments 2 .. P-1
+    if (e == hipSuccess)
+        e = kda::launch_kda_compose(Mb, Bb, Hin, static_cast<int>(B), static_cast<int>(Hv), static_cast<int>(P - 2), hs);
+    // 4. side by side: segments 1 .. P-1 from their entering states; the last one
+    //    writes the final state
+    kda::ScanJobs J2{};
+    J2.njobs = 2;
+    kda::KdaParams& ja = J2.job[0];
+    ja = p;
+    ja.N = static_cast<int32_t>(B * (P - 2));
+    ja.seg_first = 1;
+    ja.h0 = Hin;
+    ja.hT = nullptr;
+    kda::KdaParams& jz = J2.job[1];
+    jz = p;
+    jz.N = static_cast<int32_t>(B);
+    jz.seg_first = static_cast<int32_t>(P - 1);
+    jz.h0 = Hin + (P - 2) * blk_f;
+    if (e == hipSuccess) e = kda::launch_kda_scan_jobs(J2, hs);
+    return finish(e, hs);
+}
+
 kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                         const kda_tensor_t* beta, float scale, const kda_tensor_t* state_in,
                         const kda_tensor_t* state_out, const kda_tensor_t* out, void* stream) {
@@ -262,12 +420,7 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
     p.scale = scale;
     if (N == 0) return KDA_OK;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (kda::launch_kda_decode(p, hs) != hipSuccess) return KDA_ERR_HIP;
-    if (std::getenv("KDA_DEBUG_SYNC")) {
-        if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERR_HIP;
-        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
-    }
-    return KDA_OK;
+    return finish(kda::launch_kda_decode(p, hs), hs);
 }
 
 const char* kda_status_string(kda_status_t s) {

@@ -63,8 +63,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Token range of sequence n, clamped to [0, T) so that malformed cu_seqlens can
-// never send an access out of bounds.
+// Token range of (record) sequence n, clamped to [0, T) so that malformed
+// cu_seqlens can never send an access out of bounds.  With segments, sequence n
+// is segment n % seg_per_row of batch row n / seg_per_row.
 __device__ __forceinline__ void seq_bounds(const KdaParams& p, int n, int64_t& bos, int64_t& len) {
     if (p.cu) {
         int64_t a = p.cu[n], e = p.cu[n + 1];
@@ -72,10 +73,23 @@ __device__ __forceinline__ void seq_bounds(const KdaParams& p, int n, int64_t& b
         e = e < a ? a : (e > p.T ? p.T : e);
         bos = a;
         len = e - a;
+    } else if (p.seg_tokens) {
+        const int b = n / p.seg_per_row, s = n % p.seg_per_row;
+        const int64_t off = (int64_t)s * p.seg_tokens, rest = p.T - off;
+        bos = (int64_t)b * p.T + off;
+        len = rest < 0 ? 0 : (rest > p.seg_tokens ? p.seg_tokens : rest);
     } else {
         bos = (int64_t)n * p.T;
         len = p.T;
     }
+}
+
+// Sequence n of a scan job: its token range and its record sequence (the index
+// the intra kernel's slots were laid out with).  Without segments the two
+// indices agree.
+__device__ __forceinline__ void job_seq(const KdaParams& p, int n, int64_t& bos, int64_t& len, int& n_rec) {
+    n_rec = p.seg_tokens ? (n % p.seg_rows) * p.seg_per_row + p.seg_first + n / p.seg_rows : n;
+    seq_bounds(p, n_rec, bos, len);
 }
 
 // Workspace slot of chunk c of sequence n (first token bos): floor(start / 64) + n.

@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     // slot -> (sequence, chunk): the first slot of sequence n, floor(bos_n / 64) + n,
     // does not decrease with n; take the last sequence whose first slot is <= slot.
     int n;
-    if (!p.cu && p.T % CH == 0) {
+    if (!p.cu && !p.seg_tokens && p.T % CH == 0) {
         n = (int)(slot / (p.T / CH + 1));   // sequence n has slots n (T/64 + 1) .. + T/64 - 1
     } else {
         int lo = 0, hi = p.N - 1;

@@ -21,6 +21,18 @@ struct KdaParams {
     int32_t N, Hq, Hv;
     int32_t beta_f32;
     float scale;
+    // Segments (fixed length only; seg_tokens = 0: none).  Row b of the batch is cut
+    // into seg_per_row segments of seg_tokens tokens (a multiple of 64; the last one
+    // may be shorter), and segment s of row b is record sequence b * seg_per_row + s:
+    // the intra kernel runs over all of them (N = rows * seg_per_row).  A scan job
+    // walks segments seg_first .. seg_first + N / seg_rows - 1 of every row, its
+    // sequence n being segment seg_first + n / seg_rows of row n % seg_rows; h0, hT
+    // and o are indexed by that n (segment-major).
+    int64_t seg_tokens;
+    int32_t seg_rows, seg_per_row, seg_first;
+    // Scan job variants: the state enters as the identity (h0 ignored), and / or v
+    // reads as zero.  o == nullptr: no output is written.
+    int32_t h0_identity, v_zero;
     // Optional fp32 dumps of the intermediates (all nullptr in production launches).
     float* tr_G;
     float* tr_Aqk;
@@ -59,5 +71,21 @@ hipError_t launch_kda_intra(const KdaParams& p, bool trace, hipStream_t stream);
 // for one slice of the value head's dv columns.
 int scan_slices();
 hipError_t launch_kda_scan(const KdaParams& p, bool trace, hipStream_t stream);
+
+// Up to three scan jobs in one grid (so that they run side by side): job j has
+// job[j].N * job[j].Hv * scan_slices() work-groups; jobs with N = 0 are skipped.
+constexpr int MAX_SCAN_JOBS = 3;
+struct ScanJobs {
+    KdaParams job[MAX_SCAN_JOBS];
+    int32_t end[MAX_SCAN_JOBS];   // first work-group past job j (filled by launch_kda_scan_jobs)
+    int32_t njobs;
+};
+hipError_t launch_kda_scan_jobs(ScanJobs jobs, hipStream_t stream);
+
+// Affine maps of consecutive segments composed in order, per (row, value head):
+// h_in[s + 1] = M[s] h_in[s] + b[s] for s = 0 .. nsteps - 1, where h_in[0] is given.
+// All arrays segment-major: [segment][rows][Hv][128][128] fp32.
+hipError_t launch_kda_compose(const float* M, const float* b, float* h_in, int rows, int Hv, int nsteps,
+                              hipStream_t stream);
 
 }  // namespace kda

@@ -97,9 +97,14 @@ __device__ __forceinline__ float rec_kg(const char* rec, int i, int c) {
 
 }  // namespace
 
-template <bool TRACE>
-__global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaParams p) {
+template <bool TRACE, bool MULTI>
+__global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const ScanJobs J) {
     using L = ScanLds;
+    // The job this work-group belongs to, and its index within the job (a single
+    // job: job 0, whose parameters then sit at fixed kernel-argument offsets).
+    const int jb = !MULTI ? 0 : (blockIdx.x < (unsigned)J.end[0] ? 0 : (blockIdx.x < (unsigned)J.end[1] ? 1 : 2));
+    const KdaParams& p = J.job[jb];
+    const int bid = (int)blockIdx.x - (jb == 0 ? 0 : J.end[jb - 1]);
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -114,20 +119,21 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     const int npairs = p.N * p.Hv;
     int pair, s;
     if ((npairs & 7) == 0) {
-        const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+        const int x = bid & 7, loc = bid >> 3;
         pair = (loc / SLICES) * 8 + x;
         s = loc % SLICES;
     } else {
-        pair = blockIdx.x / SLICES;
-        s = blockIdx.x % SLICES;
+        pair = bid / SLICES;
+        s = bid % SLICES;
     }
     const int n = pair / p.Hv, hv = pair % p.Hv;
     int64_t bos, len;
-    seq_bounds(p, n, bos, len);
+    int n_rec;   // the record sequence (equal to n without segments)
+    job_seq(p, n, bos, len, n_rec);
     const int64_t nch = (len + CH - 1) / CH;
     const int64_t v_tok = (int64_t)p.Hv * DK;   // token stride of v, o
     const int dv0 = (PAIRS * s + pr) * DVW;     // this pair's dv columns
-    const int64_t slot0 = chunk_slot(bos, n, 0);   // record slot of chunk c: slot0 + c
+    const int64_t slot0 = chunk_slot(bos, n_rec, 0);   // record slot of chunk c: slot0 + c
 
     int64_t trace_chunk = 0;   // index of this sequence's first chunk in the h dump
     if (TRACE && p.tr_h) {
@@ -226,7 +232,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) hacc[tt][r] = 0.f;
-        if (p.h0) {
+        if (p.h0_identity) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                hacc[tt][r] = (32 * (2 * role + tt) + 8 * (r >> 2) + 4 * hl + (r & 3) == dv0 + cl) ? 1.f : 0.f;
+        } else if (p.h0) {
             const float* src = p.h0 + ((int64_t)n * p.Hv + hv) * DK * DK + dv0;
             const int lo = cl + 4 * hl * DK;
 #pragma unroll
@@ -270,7 +280,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     auto dma_v = [&](int64_t c) {
         const int Lc = chunk_rows(c);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (bos + c * CH) * v_tok + (int64_t)hv * DK + dv0,
-                                                    Lc ? ((Lc - 1) * v_tok + DVW) * 2 : 0);
+                                                    Lc && !p.v_zero ? ((Lc - 1) * v_tok + DVW) * 2 : 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_vs + u * WS_FRAG);
@@ -421,6 +431,17 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
             lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
             update_state();
         }
+    } else if (!p.o) {
+        // No output (the runs that only produce a segment's state map): this wave
+        // keeps its half of the state rows, with the same two barriers per chunk.
+        for (int64_t c = 0; c < nch; ++c) {
+            const int b = (int)(c & 1);
+            decay_state(b);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) fkh[f] = frag(b, WS_KH + (8 * role + f) * WS_FRAG);
+            lds_barrier();   // v_new^T complete; every read of record buffer b and of v^T done
+            update_state();
+        }
     } else {
         for (int64_t c = 0; c < nch; ++c) {
             const int64_t tok0 = bos + c * CH;
@@ -488,18 +509,39 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const KdaPara
     }
 }
 
-template <bool TRACE>
-static hipError_t launch(const KdaParams& p, int nblocks, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_scan_kernel<TRACE>), dim3(nblocks), dim3(SCAN_THREADS), 0, stream, p);
+// Fills the jobs' work-group ranges; returns the grid size (0: nothing to run, -1: too large).
+static int64_t job_ranges(ScanJobs& J) {
+    int64_t total = 0;
+    for (int j = 0; j < MAX_SCAN_JOBS; ++j) {
+        if (j < J.njobs) total += (int64_t)J.job[j].N * J.job[j].Hv * SLICES;
+        if (total > INT32_MAX) return -1;
+        J.end[j] = (int32_t)total;
+    }
+    return total;
+}
+
+template <bool TRACE, bool MULTI>
+static hipError_t launch(const ScanJobs& J, int nblocks, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_scan_kernel<TRACE, MULTI>), dim3(nblocks), dim3(SCAN_THREADS), 0, stream, J);
     return hipGetLastError();
 }
 
 int scan_slices() { return SLICES; }
 
 hipError_t launch_kda_scan(const KdaParams& p, bool trace, hipStream_t stream) {
-    const int64_t nblocks = (int64_t)p.N * p.Hv * SLICES;
-    if (nblocks == 0) return hipSuccess;
-    return trace ? launch<true>(p, (int)nblocks, stream) : launch<false>(p, (int)nblocks, stream);
+    ScanJobs J{};
+    J.job[0] = p;
+    J.njobs = 1;
+    const int64_t nblocks = job_ranges(J);
+    if (nblocks <= 0) return nblocks == 0 ? hipSuccess : hipErrorInvalidValue;
+    return trace ? launch<true, false>(J, (int)nblocks, stream) : launch<false, false>(J, (int)nblocks, stream);
+}
+
+hipError_t launch_kda_scan_jobs(ScanJobs J, hipStream_t stream) {
+    if (J.njobs < 1 || J.njobs > MAX_SCAN_JOBS) return hipErrorInvalidValue;
+    const int64_t nblocks = job_ranges(J);
+    if (nblocks <= 0) return nblocks == 0 ? hipSuccess : hipErrorInvalidValue;
+    return launch<false, true>(J, (int)nblocks, stream);
 }
 
 }  // namespace kda

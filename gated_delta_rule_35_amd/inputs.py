@@ -55,6 +55,10 @@ WORKLOADS = {
     "mha_b2_h64_t4096_h0": Workload("mha_b2_h64_t4096_h0", 2, 4096, 64, 64, torch.float32, True),
     "gva_b1_hq16_hv64_t4096": Workload("gva_b1_hq16_hv64_t4096", 1, 4096, 16, 64, torch.bfloat16, False),
     "varlen_h64_16k": Workload("varlen_h64_16k", 1, 16384, 64, 64, torch.float32, False, varlen_total=16384),
+    # few heads per GPU: one long sequence, and the headline batch's share of one GPU
+    # under 8-way head sharding (the segmented forward's workloads)
+    "mha_b1_h8_t65536": Workload("mha_b1_h8_t65536", 1, 65536, 8, 8, torch.float32, True),
+    "mha_b2_h8_t8192": Workload("mha_b2_h8_t8192", 2, 8192, 8, 8, torch.float32, True),
 }
 
 

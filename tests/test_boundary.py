@@ -281,3 +281,59 @@ def test_decode_empty_batch_needs_no_launch(lib):
         if a[key] is not None:
             a[key].data = None
     expect_decode(lib, a, "KDA_OK")
+
+
+# ---- kda_fwd_cp ----
+
+def call_cp(lib, a, seg, scale=0.088, h0=None, hT=None, ws=None, ws_size=0):
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    return lib.kda_fwd_cp(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale,
+                          r(h0), r(a.get("out")), r(hT), seg, ws, ws_size, None)
+
+
+def test_cp_workspace_size(lib):
+    rec = 61952
+    # fewer than three segments: kda_fwd's workspace
+    assert lib.kda_fwd_cp_workspace_size(2, 1000, 4, 8) == lib.kda_fwd_workspace_size(2000, 2, 4)
+    # B=2, T=8192 (128 chunks), Hv=8, 16 chunks per segment: P = 8
+    B, T, H, P = 2, 8192, 8, 8
+    recs = ((B * T + 63) // 64 + B * P) * H * rec
+    recs = (recs + 255) // 256 * 256
+    blk = B * H * 128 * 128 * 4
+    assert lib.kda_fwd_cp_workspace_size(B, T, H, 16) == recs + 2 * (P - 2) * blk + (P - 1) * blk
+    # a partial last segment counts: 1000 tokens = 16 chunks, 5 per segment -> 4 segments
+    assert lib.kda_fwd_cp_workspace_size(1, 1000, 2, 5) > lib.kda_fwd_workspace_size(1000, 1, 2)
+    for bad in ((-1, 10, 2, 1), (1, -1, 2, 1), (1, 10, -2, 1), (1, 10, 2, 0)):
+        assert lib.kda_fwd_cp_workspace_size(*bad) == -1
+
+
+def test_cp_checked_before_launch(lib):
+    a = good(B=2, T_=1024)   # 16 chunks
+    st = lambda: T([2, 2, 128, 128], binding.KDA_F32)  # noqa: E731
+    for seg in (0, -3):
+        assert binding.STATUS_NAMES[call_cp(lib, a, seg, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_VALUE"
+    # segmented (4 segments): the workspace is required and sized by kda_fwd_cp_workspace_size
+    need = lib.kda_fwd_cp_workspace_size(2, 1024, 2, 4)
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4)] == "KDA_ERR_WORKSPACE"
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, ws=FAKE, ws_size=need - 1)] == "KDA_ERR_WORKSPACE"
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, ws=FAKE + 8, ws_size=need)] == "KDA_ERR_WORKSPACE"
+    # the tensor checks of kda_fwd come first
+    b = good(B=2, T_=1024)
+    b["q"] = T([2, 1024, 2, 64])
+    assert binding.STATUS_NAMES[call_cp(lib, b, 4, ws=FAKE, ws_size=need)] == "KDA_ERR_UNSUPPORTED"
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, h0=st(), hT=T([2, 2, 128, 128], binding.KDA_F32,
+                                                                  data=FAKE + 4096))] == "KDA_ERR_LAYOUT"
+    for s in (0.0, float("nan")):
+        assert binding.STATUS_NAMES[call_cp(lib, a, 4, scale=s, ws=FAKE, ws_size=need)] == "KDA_ERR_VALUE"
+
+
+def test_cp_segment_suggestion(lib):
+    # a batch that fills the chip, or short sequences: the ordinary path
+    assert lib.kda_fwd_cp_segment_chunks(2, 8192, 64, 256) == 0
+    assert lib.kda_fwd_cp_segment_chunks(1, 1024, 8, 256) == 0
+    # few heads, long sequences: at least three segments
+    for B, T, H in ((1, 65536, 8), (2, 8192, 8), (1, 32768, 16)):
+        L = lib.kda_fwd_cp_segment_chunks(B, T, H, 256)
+        assert L >= 1 and -(-(T // 64) // L) >= 3, (B, T, H, L)
+    for bad in ((0, 8192, 8, 256), (1, 0, 8, 256), (1, 8192, 0, 256), (1, 8192, 8, 0)):
+        assert lib.kda_fwd_cp_segment_chunks(*bad) == 0

@@ -1,0 +1,100 @@
+"""GPU parity of the segmented forward (kda_fwd_cp: each sequence cut into
+segments whose state maps are composed, so the scan walks them side by side)
+against the fp64 CPU oracle, through the C ABI.
+
+The result is the recurrence itself, so the oracle is the same token recurrence
+the other parity tests use; the tolerances are the same.  Each test prints the
+case it is about to launch before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_35_amd import kda_fwd, kda_fwd_cp, load_library
+from gated_delta_rule_35_amd.inputs import make_inputs
+from tests.kda_check import O_MAX_ABS, O_REL_F, STATE_REL_F, rel_frob_per_head, state_rel_frob, to_device
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 128 ** -0.5
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    load_library()  # fails loudly if the HIP library is not built
+    yield
+
+
+def run_cp(x, seg_chunks, want_state=True):
+    d = to_device(x)
+    o, hT = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, seg_chunks, initial_state=d["h0"],
+                       final_state=True if want_state else None)
+    torch.cuda.synchronize()
+    return o, hT
+
+
+def check_cp(x, seg_chunks, label):
+    o, hT = run_cp(x, seg_chunks)
+    o, hT = o.float().cpu().numpy(), hT.cpu().numpy()
+    o_ref, h_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], SCALE, h0=x["h0"])
+    rel = rel_frob_per_head(o, o_ref)
+    mx = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    srel = state_rel_frob(hT, h_ref)
+    _say(f"{label}: o relF={rel:.3e} maxabs={mx:.3e} state relF={srel:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    assert rel <= O_REL_F, rel
+    assert mx <= O_MAX_ABS, mx
+    assert srel <= STATE_REL_F, srel
+
+
+@pytest.mark.parametrize("B,T,Hq,Hv,seg,beta,h0", [
+    (1, 1000, 2, 2, 3, torch.float32, True),     # 6 segments, the last one a partial chunk
+    (3, 640, 3, 3, 1, torch.float32, True),      # one chunk per segment: 10 segments, 8 composed maps
+    (2, 4096, 2, 8, 8, torch.bfloat16, False),   # grouped values, 8 segments
+    (1, 193, 2, 2, 1, torch.float32, True),      # 4 segments of one chunk, 1-token tail
+])
+def test_segmented_matches_oracle(B, T, Hq, Hv, seg, beta, h0):
+    _say(f"kda_fwd_cp B={B} T={T} Hq={Hq} Hv={Hv} segment_chunks={seg} h0={h0}")
+    x = make_inputs(B, T, Hq, Hv, beta, h0=h0, seed=200 + T)
+    check_cp(x, seg, f"cp B={B} T={T} seg={seg}")
+
+
+def test_segmented_long_sequence():
+    _say("kda_fwd_cp B=1 T=65536 H=2 segment_chunks=64 (16 segments) with h0")
+    x = make_inputs(1, 65536, 2, 2, torch.float32, h0=True, seed=201)
+    check_cp(x, 64, "cp T=65536")
+
+
+def test_two_segments_or_fewer_is_kda_fwd_bitwise():
+    _say("kda_fwd_cp with 2 segments vs kda_fwd, B=2 T=256 H=2")
+    x = make_inputs(2, 256, 2, 2, torch.float32, h0=True, seed=202)
+    d = to_device(x)
+    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o2, h2 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 2, initial_state=d["h0"],
+                        final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
+
+
+def test_segmented_is_repeatable_and_may_update_the_state_in_place():
+    _say("kda_fwd_cp repeat and in-place state, B=2 T=1024 H=4 segment_chunks=4")
+    x = make_inputs(2, 1024, 4, 4, torch.float32, h0=True, seed=203)
+    d = to_device(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 4)
+    o1, h1 = kda_fwd_cp(*args, initial_state=d["h0"], final_state=True)
+    o2, h2 = kda_fwd_cp(*args, initial_state=d["h0"], final_state=True)
+    st = d["h0"].clone()
+    o3, h3 = kda_fwd_cp(*args, initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    for o in (o2, o3):
+        assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
+    for h in (h2, h3):
+        assert torch.equal(h1.view(torch.int32), h.view(torch.int32))
