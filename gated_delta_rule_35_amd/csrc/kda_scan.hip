@@ -38,6 +38,13 @@
 //                 buffer this chunk was read from; before the second, wait for
 //                 chunk + 1's
 // All products run on v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulate).
+//
+// A grid may hold up to three jobs (ScanJobs), each a full set of parameters over
+// its own sequences: the segmented forward runs a sequence's segments side by side
+// this way (segment 0 from the initial state next to the later segments' state
+// maps: from the identity with v read as zero, and from zero, neither with output).
+// The ordinary forward launches the single-job instantiation, whose parameters sit
+// at fixed kernel-argument offsets.
 #include "kda_device.h"
 
 namespace kda {
