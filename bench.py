@@ -187,7 +187,7 @@ def bench_cp(args):
     HIP events around each whole call (intra kernel, two scan launches and the
     composition) on its stream, and kda_fwd on the same inputs for comparison."""
     import torch
-    from gated_delta_rule_35_amd import (kda_fwd, kda_fwd_cp, kda_fwd_cp_segment_chunks, kda_fwd_cp_workspace_size,
+    from gated_delta_rule_35_amd import (kda_fwd, kda_fwd_cp, kda_fwd_cp_plan, kda_fwd_cp_workspace_size,
                                          kda_fwd_workspace_size)
     from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
     if args.gpus != 1:
@@ -205,13 +205,18 @@ def bench_cp(args):
     d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     out = torch.empty_like(d["v"])
     hT = torch.empty((B, w.Hv, 128, 128), dtype=torch.float32, device=dev)
-    L = args.cp if args.cp > 0 else kda_fwd_cp_segment_chunks(B, T, w.Hv)
-    if L <= 0:
-        print(f"{w.name}: the segment heuristic picks the ordinary path (B * Hv fills the GPU or T is short); "
-              "pass --cp N to force N chunks per segment", file=sys.stderr, flush=True)
-        sys.exit(2)
-    P = -(-((T + 63) // 64) // L)
-    ws_cp = torch.empty(kda_fwd_cp_workspace_size(B, T, w.Hv, L), dtype=torch.uint8, device=dev)
+    if args.cp > 0:
+        L, L0 = args.cp, (args.cp_first or args.cp)
+    else:
+        pl = kda_fwd_cp_plan(B, T, w.Hv)
+        if pl is None:
+            print(f"{w.name}: the segment plan picks the ordinary path (B * Hv fills the GPU or T is short); "
+                  "pass --cp N to force N chunks per segment", file=sys.stderr, flush=True)
+            sys.exit(2)
+        L, L0 = pl
+    nch = (T + 63) // 64
+    P = 1 if nch <= L0 else 1 + -(-(nch - L0) // L)
+    ws_cp = torch.empty(kda_fwd_cp_workspace_size(B, T, w.Hv, L, L0), dtype=torch.uint8, device=dev)
     ws = torch.empty(kda_fwd_workspace_size(B * T, B, w.Hv), dtype=torch.uint8, device=dev)
     a = (d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale)
     stream = torch.cuda.current_stream(dev)
@@ -231,8 +236,9 @@ def bench_cp(args):
         ms = [e[0].elapsed_time(e[1]) for e in ev]
         return wall / args.steps * 1e3, sum(ms) / len(ms)
 
-    log(f"kda_fwd_cp: {L} chunks per segment, {P} segments per row; {args.steps} steps")
-    step_ms, call_ms = timed(lambda: kda_fwd_cp(*a, L, initial_state=d["h0"], out=out, final_state=hT, workspace=ws_cp))
+    log(f"kda_fwd_cp: first segment {L0} chunks, then {L} per segment, {P} segments per row; {args.steps} steps")
+    step_ms, call_ms = timed(lambda: kda_fwd_cp(*a, L, L0, initial_state=d["h0"], out=out, final_state=hT,
+                                                workspace=ws_cp))
     log(f"kda_fwd (ordinary): {args.steps} steps")
     plain_step_ms, plain_call_ms = timed(lambda: kda_fwd(*a, initial_state=d["h0"], out=out, final_state=hT,
                                                          workspace=ws))
@@ -248,7 +254,7 @@ def bench_cp(args):
            "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16", "data": "synthetic",
            "config": {"workload": w.name, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128, "chunk": 64,
-                      "segment_chunks": L, "segments_per_row": P,
+                      "segment_chunks": L, "first_segment_chunks": L0, "segments_per_row": P,
                       "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0)},
            "call_ms_avg": round(call_ms, 5), "ordinary_kda_fwd_ms_avg": round(plain_call_ms, 5),
            "speedup_vs_ordinary": round(plain_call_ms / call_ms, 3),
@@ -276,6 +282,8 @@ def main():
     ap.add_argument("--cp", type=int, default=-1, metavar="L",
                     help="instead of the headline, time kda_fwd_cp on --workload with L chunks per segment "
                          "(0: the library's suggestion) against kda_fwd")
+    ap.add_argument("--cp-first", type=int, default=0, metavar="L0",
+                    help="with --cp L: chunks of the first segment (default L)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the benchmark, run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()

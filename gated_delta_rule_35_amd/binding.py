@@ -23,7 +23,7 @@ _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
 EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode",
-            "kda_fwd_workspace_size", "kda_fwd_cp_workspace_size", "kda_fwd_cp_segment_chunks", "kda_status_string",
+            "kda_fwd_workspace_size", "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_status_string",
             "kda_dv_slices"]
 
 
@@ -67,13 +67,14 @@ def load_library(path=None):
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
-    lib.kda_fwd_cp.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_int64, ctypes.c_void_p,
-                               ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_fwd_cp.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.kda_fwd_cp.restype = ctypes.c_int
-    lib.kda_fwd_cp_workspace_size.argtypes = [ctypes.c_int64] * 4
+    lib.kda_fwd_cp_workspace_size.argtypes = [ctypes.c_int64] * 5
     lib.kda_fwd_cp_workspace_size.restype = ctypes.c_int64
-    lib.kda_fwd_cp_segment_chunks.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
-    lib.kda_fwd_cp_segment_chunks.restype = ctypes.c_int64
+    lib.kda_fwd_cp_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.kda_fwd_cp_plan.restype = ctypes.c_int32
     lib.kda_decode.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_void_p]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -214,22 +215,27 @@ def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state
     return out, final_state
 
 
-def kda_fwd_cp_workspace_size(batch, seq_len, num_value_heads, segment_chunks):
-    return int(load_library().kda_fwd_cp_workspace_size(batch, seq_len, num_value_heads, segment_chunks))
+def kda_fwd_cp_workspace_size(batch, seq_len, num_value_heads, segment_chunks, first_segment_chunks=0):
+    return int(load_library().kda_fwd_cp_workspace_size(batch, seq_len, num_value_heads, segment_chunks,
+                                                        first_segment_chunks))
 
 
-def kda_fwd_cp_segment_chunks(batch, seq_len, num_value_heads, num_cus=None):
-    """Suggested segment length for kda_fwd_cp, or 0 (use kda_fwd).  num_cus
-    defaults to the current GPU's compute units."""
+def kda_fwd_cp_plan(batch, seq_len, num_value_heads, num_cus=None):
+    """(segment_chunks, first_segment_chunks) for kda_fwd_cp, or None when kda_fwd
+    is about as fast.  num_cus defaults to the current GPU's compute units."""
     if num_cus is None:
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    return int(load_library().kda_fwd_cp_segment_chunks(batch, seq_len, num_value_heads, num_cus))
+    seg, first = ctypes.c_int64(0), ctypes.c_int64(0)
+    ok = load_library().kda_fwd_cp_plan(batch, seq_len, num_value_heads, num_cus, ctypes.byref(seg),
+                                        ctypes.byref(first))
+    return (int(seg.value), int(first.value)) if ok else None
 
 
-def kda_fwd_cp(q, k, v, g, beta, scale, segment_chunks, initial_state=None, out=None, final_state=None, stream=None,
-               workspace=None):
-    """kda_fwd for a fixed-length batch with each sequence cut into segments of
-    `segment_chunks` chunks that the scan walks side by side (see include/kda.h).
+def kda_fwd_cp(q, k, v, g, beta, scale, segment_chunks, first_segment_chunks=0, initial_state=None, out=None,
+               final_state=None, stream=None, workspace=None):
+    """kda_fwd for a fixed-length batch with each sequence cut into segments (the
+    first of `first_segment_chunks` chunks, 0: `segment_chunks`, the others of
+    `segment_chunks`) that the scan walks side by side (see include/kda.h).
     Returns (out, final_state); final_state=True allocates it.  `workspace`: a
     uint8 device tensor of at least kda_fwd_cp_workspace_size() bytes, or None
     (allocated here from torch's caching allocator)."""
@@ -246,7 +252,8 @@ def kda_fwd_cp(q, k, v, g, beta, scale, segment_chunks, initial_state=None, out=
     descs = [describe(t) for t in tensors]
     s = _stream_handle(stream, tensors)
     if workspace is None and q.dim() == 4 and v.dim() == 4:
-        size = kda_fwd_cp_workspace_size(q.shape[0], q.shape[1], v.shape[2], max(int(segment_chunks), 1))
+        size = kda_fwd_cp_workspace_size(q.shape[0], q.shape[1], v.shape[2], max(int(segment_chunks), 1),
+                                         max(int(first_segment_chunks), 0))
         workspace = torch.empty(max(size, 0), dtype=torch.uint8, device=v.device)
         if stream is not None and isinstance(stream, torch.cuda.Stream):
             workspace.record_stream(stream)
@@ -254,7 +261,7 @@ def kda_fwd_cp(q, k, v, g, beta, scale, segment_chunks, initial_state=None, out=
     ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib, lib.kda_fwd_cp(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
                                float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), int(segment_chunks),
-                               ws_ptr, ws_size, s))
+                               int(first_segment_chunks), ws_ptr, ws_size, s))
     return out, final_state
 
 

@@ -193,10 +193,16 @@ struct SegLayout {
     int64_t P = 0, rec = 0, maps = 0, total = 0;
 };
 
-SegLayout seg_layout(int64_t B, int64_t T, int64_t Hv, int64_t seg_chunks) {
+// Segments per row: the first of first_chunks chunks, then seg_chunks each.
+int64_t segment_count(int64_t nch, int64_t seg_chunks, int64_t first_chunks) {
+    if (nch <= 0 || seg_chunks <= 0 || first_chunks <= 0) return 0;
+    return nch <= first_chunks ? 1 : 1 + (nch - first_chunks + seg_chunks - 1) / seg_chunks;
+}
+
+SegLayout seg_layout(int64_t B, int64_t T, int64_t Hv, int64_t seg_chunks, int64_t first_chunks) {
     SegLayout c;
     const int64_t nch = (T + 63) / 64;
-    c.P = seg_chunks > 0 ? (nch + seg_chunks - 1) / seg_chunks : 0;
+    c.P = segment_count(nch, seg_chunks, first_chunks);
     if (c.P < 3) {
         c.total = kda::workspace_bytes(B * T, B, Hv);
         return c;
@@ -259,43 +265,64 @@ kda_status_t kda_fwd_trace(const kda_tensor_t* q, const kda_tensor_t* k, const k
                trace, kBoth, stream);
 }
 
-int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks) {
-    if (batch < 0 || seq_len < 0 || num_value_heads < 0 || segment_chunks < 1) return -1;
-    return seg_layout(batch, seq_len, num_value_heads, segment_chunks).total;
+int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks,
+                                  int64_t first_segment_chunks) {
+    if (batch < 0 || seq_len < 0 || num_value_heads < 0 || segment_chunks < 1 || first_segment_chunks < 0) return -1;
+    const int64_t first = first_segment_chunks ? first_segment_chunks : segment_chunks;
+    return seg_layout(batch, seq_len, num_value_heads, segment_chunks, first).total;
 }
 
-int64_t kda_fwd_cp_segment_chunks(int64_t batch, int64_t seq_len, int64_t num_value_heads, int32_t num_cus) {
+int32_t kda_fwd_cp_plan(int64_t batch, int64_t seq_len, int64_t num_value_heads, int32_t num_cus,
+                        int64_t* segment_chunks, int64_t* first_segment_chunks) {
+    if (segment_chunks) *segment_chunks = 0;
+    if (first_segment_chunks) *first_segment_chunks = 0;
     if (batch <= 0 || seq_len <= 0 || num_value_heads <= 0 || num_cus <= 0) return 0;
     const int64_t nch = (seq_len + 63) / 64, per_seg = batch * num_value_heads * kda::scan_slices();
-    auto waves = [&](int64_t wgs) { return (wgs + num_cus - 1) / num_cus; };
-    // Cost in chunk steps: the scan waves of each phase times the chunks they walk,
-    // plus one step per composed map and eight for the two extra launches; the
-    // ordinary scan walks every chunk.
-    const int64_t base = waves(per_seg) * nch;
-    int64_t best = 0, best_cost = base;
-    for (int64_t P = 3; P <= 64 && P <= nch; ++P) {
-        const int64_t L = (nch + P - 1) / P, Pe = (nch + L - 1) / L;   // segments actually formed
-        if (Pe < 3) continue;
-        const int64_t cost = (waves(per_seg * (1 + 2 * (Pe - 2))) + waves(per_seg * (Pe - 1))) * L + (Pe - 2) + 8;
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = L;
+    if (per_seg >= num_cus) return 0;   // the ordinary scan already fills the GPU
+    auto waves = [&](int64_t wgs, int64_t slots) { return (wgs + slots - 1) / slots; };
+    // Cost in chunk steps.  Step 2: segment 0's pass holds per_seg CUs for its L0
+    // chunks while the maps of segments 1 .. P-2 pass through the other CUs in
+    // waves of L chunks (and through all of them once segment 0 is done); step 4:
+    // the remaining segments in waves of L; plus one step per composed map and
+    // eight for the extra launches.  The ordinary scan walks every chunk once.
+    const int64_t base = nch;
+    int64_t best_cost = base, best_L = 0, best_L0 = 0;
+    for (int64_t L = 1; L <= nch; ++L) {
+        for (int64_t m = 1; m <= 4; ++m) {
+            const int64_t L0 = m * L, P = segment_count(nch, L, L0);
+            if (P < 3 || P > 64) continue;
+            const int64_t maps = 2 * per_seg * (P - 2);
+            const int64_t beside = (L0 / L) * (num_cus - per_seg);   // map work-groups done within L0
+            const int64_t step2 = maps <= beside ? L0 : L0 + L * waves(maps - beside, num_cus);
+            const int64_t cost = step2 + L * waves(per_seg * (P - 1), num_cus) + (P - 2) + 8;
+            if (cost < best_cost) {
+                best_cost = cost;
+                best_L = L;
+                best_L0 = L0;
+            }
         }
     }
-    return 5 * best_cost <= 4 * base ? best : 0;   // only when it saves a fifth or more
+    // Only when it saves a fifth or more: the model is coarse (the time of a chunk
+    // step grows with the number of work-groups running), and a smaller predicted
+    // saving measured as none (grouped values, B = 1, Hv = 64, T = 4096).
+    if (5 * best_cost > 4 * base) return 0;
+    if (segment_chunks) *segment_chunks = best_L;
+    if (first_segment_chunks) *first_segment_chunks = best_L0;
+    return 1;
 }
 
 kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                         const kda_tensor_t* beta, float scale, const kda_tensor_t* initial_state,
                         const kda_tensor_t* out, const kda_tensor_t* final_state, int64_t segment_chunks,
-                        void* workspace, int64_t workspace_size, void* stream) {
+                        int64_t first_segment_chunks, void* workspace, int64_t workspace_size, void* stream) {
     kda::KdaParams p;
     int64_t B, T, N;
     kda_status_t st = prepare(q, k, v, g, beta, scale, nullptr, initial_state, out, final_state, p, B, T, N);
     if (st != KDA_OK) return st;
-    if (segment_chunks < 1) return KDA_ERR_VALUE;
+    if (segment_chunks < 1 || first_segment_chunks < 0) return KDA_ERR_VALUE;
+    const int64_t first_chunks = first_segment_chunks ? first_segment_chunks : segment_chunks;
     const int64_t Hv = p.Hv;
-    const SegLayout c = seg_layout(B, T, Hv, segment_chunks);
+    const SegLayout c = seg_layout(B, T, Hv, segment_chunks, first_chunks);
     if (c.P < 3)   // one or two segments: nothing runs side by side; the ordinary path
         return run(q, k, v, g, beta, scale, nullptr, initial_state, out, final_state, workspace, workspace_size,
                    nullptr, kBoth, stream);
@@ -314,6 +341,7 @@ kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
     const int64_t blk_f = B * Hv * kHeadDim * kHeadDim;   // floats per segment of states
     p.ws = ws;
     p.seg_tokens = segment_chunks * 64;
+    p.seg0_tokens = first_chunks * 64;
     p.seg_rows = static_cast<int32_t>(B);
     p.seg_per_row = static_cast<int32_t>(P);
     p.nslots = nslots;

@@ -65,7 +65,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Token range of (record) sequence n, clamped to [0, T) so that malformed
 // cu_seqlens can never send an access out of bounds.  With segments, sequence n
-// is segment n % seg_per_row of batch row n / seg_per_row.
+// is segment n % seg_per_row of batch row n / seg_per_row (segment 0 of
+// seg0_tokens tokens, each later one of seg_tokens).
 __device__ __forceinline__ void seq_bounds(const KdaParams& p, int n, int64_t& bos, int64_t& len) {
     if (p.cu) {
         int64_t a = p.cu[n], e = p.cu[n + 1];
@@ -75,9 +76,10 @@ __device__ __forceinline__ void seq_bounds(const KdaParams& p, int n, int64_t& b
         len = e - a;
     } else if (p.seg_tokens) {
         const int b = n / p.seg_per_row, s = n % p.seg_per_row;
-        const int64_t off = (int64_t)s * p.seg_tokens, rest = p.T - off;
+        const int64_t off = s == 0 ? 0 : p.seg0_tokens + (int64_t)(s - 1) * p.seg_tokens;
+        const int64_t cap = s == 0 ? p.seg0_tokens : p.seg_tokens, rest = p.T - off;
         bos = (int64_t)b * p.T + off;
-        len = rest < 0 ? 0 : (rest > p.seg_tokens ? p.seg_tokens : rest);
+        len = rest < 0 ? 0 : (rest > cap ? cap : rest);
     } else {
         bos = (int64_t)n * p.T;
         len = p.T;

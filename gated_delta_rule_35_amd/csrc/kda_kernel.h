@@ -22,13 +22,14 @@ struct KdaParams {
     int32_t beta_f32;
     float scale;
     // Segments (fixed length only; seg_tokens = 0: none).  Row b of the batch is cut
-    // into seg_per_row segments of seg_tokens tokens (a multiple of 64; the last one
-    // may be shorter), and segment s of row b is record sequence b * seg_per_row + s:
+    // into seg_per_row segments: the first of seg0_tokens tokens, the others of
+    // seg_tokens (both multiples of 64; the last one may be shorter), and segment s
+    // of row b is record sequence b * seg_per_row + s:
     // the intra kernel runs over all of them (N = rows * seg_per_row).  A scan job
     // walks segments seg_first .. seg_first + N / seg_rows - 1 of every row, its
     // sequence n being segment seg_first + n / seg_rows of row n % seg_rows; h0, hT
     // and o are indexed by that n (segment-major).
-    int64_t seg_tokens;
+    int64_t seg_tokens, seg0_tokens;
     int32_t seg_rows, seg_per_row, seg_first;
     // Scan job variants: the state enters as the identity (h0 ignored), and / or v
     // reads as zero.  o == nullptr: no output is written.

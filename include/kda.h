@@ -131,42 +131,50 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
  * idles through a long sequence.  Over one segment the chunked recurrence is
  * affine in the state that enters it, h_out = M h_in + b, and M and b do not
  * depend on h_in (the state maps of the chunked method, "cuLA REPO_LAYOUT.md",
- * the chunk delta-H entry; the recurrence is the one above).  Segment s covers
- * chunks s * segment_chunks .. (s + 1) * segment_chunks - 1 of its row; with P
+ * the chunk delta-H entry; the recurrence is the one above).  Segment 0 covers
+ * the first first_segment_chunks chunks of its row (0: segment_chunks), each
+ * later segment the next segment_chunks (the last may be shorter); with P
  * segments per row the call runs
  *   1. the intra-chunk kernel over every segment;
  *   2. side by side: segment 0 of each row from initial_state, and, for segments
  *      1 .. P-2, M (from the identity with v = 0) and b (from zero with v);
  *   3. the entering states h_in[s + 1] = M[s] h_in[s] + b[s], in fp32;
  *   4. side by side: segments 1 .. P-1 from their entering states.
- * The sequential depth is two segments' chunks (steps 2 and 4) instead of all
- * P segments', at the price of 2 (P - 2) + 1 times the scan work-groups of an
- * ordinary call in step 2; it pays when B * Hv * 2 is well below the number of
- * CUs and the sequences are long.
+ * The sequential depth is segment 0's chunks plus one later segment's (steps 2
+ * and 4) instead of the whole row, at the price of 2 (P - 2) + 1 times the scan
+ * work-groups of an ordinary call in step 2; it pays when B * Hv * 2 is well
+ * below the number of CUs and the sequences are long.  A first segment longer
+ * than the others lets the maps run in several waves beside it.
  *
  * Arguments are kda_fwd's (no cu_seqlens: the segment boundaries are computed
- * on the host from the shapes), plus segment_chunks >= 1 (KDA_ERR_VALUE
- * otherwise).  workspace (required, 16-byte aligned, caller-owned, no
- * initialisation) must hold kda_fwd_cp_workspace_size() bytes.  With fewer
+ * on the host from the shapes), plus segment_chunks >= 1 and
+ * first_segment_chunks >= 0 (KDA_ERR_VALUE otherwise).  workspace (required,
+ * 16-byte aligned, caller-owned, no initialisation) must hold
+ * kda_fwd_cp_workspace_size() bytes.  With fewer
  * than three segments the call is exactly kda_fwd.  Results are bitwise
  * repeatable; they agree with kda_fwd to within the rounding of the fp16 MFMA
  * operands (the maps are formed with the same operand precision as the
  * state), not bit for bit.  initial_state may alias final_state.
  */
 /*
- * kda_fwd_cp_segment_chunks -- a segment length (in 64-token chunks) for
- * kda_fwd_cp on a GPU with num_cus compute units, or 0 when the ordinary
- * kda_fwd is expected to be about as fast (B * Hv fills the chip, or the
- * sequences are short).  Host arithmetic only: it minimises the scan's waves of
- * work-groups times the chunks each walks, plus the composition steps.
+ * kda_fwd_cp_plan -- segment lengths (in 64-token chunks) for kda_fwd_cp on a
+ * GPU with num_cus compute units.  Returns 1 and fills segment_chunks and
+ * first_segment_chunks (either pointer may be NULL) when the segmented call is
+ * expected to save a fifth or more; returns 0 and writes zeros when the ordinary
+ * kda_fwd is about as fast (B * Hv fills the GPU, or the sequences are short).
+ * Host arithmetic only: it minimises the chunk steps of the scan's waves of
+ * work-groups, plus the composition steps and the extra launches.
  */
-int64_t kda_fwd_cp_segment_chunks(int64_t batch, int64_t seq_len, int64_t num_value_heads, int32_t num_cus);
-int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks);
+int32_t kda_fwd_cp_plan(int64_t batch, int64_t seq_len, int64_t num_value_heads, int32_t num_cus,
+                        int64_t* segment_chunks, int64_t* first_segment_chunks);
+/* Workspace bytes of a kda_fwd_cp call; -1 for negative sizes or segment_chunks < 1. */
+int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks,
+                                  int64_t first_segment_chunks);
 kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                         const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                         const kda_tensor_t* initial_state, const kda_tensor_t* out,
                         const kda_tensor_t* final_state, int64_t segment_chunks,
-                        void* workspace, int64_t workspace_size, void* stream);
+                        int64_t first_segment_chunks, void* workspace, int64_t workspace_size, void* stream);
 
 /*
  * kda_fwd_intra, kda_fwd_scan -- the two kernels of kda_fwd as separate calls,

@@ -285,38 +285,46 @@ def test_decode_empty_batch_needs_no_launch(lib):
 
 # ---- kda_fwd_cp ----
 
-def call_cp(lib, a, seg, scale=0.088, h0=None, hT=None, ws=None, ws_size=0):
+def call_cp(lib, a, seg, first=0, scale=0.088, h0=None, hT=None, ws=None, ws_size=0):
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
     return lib.kda_fwd_cp(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale,
-                          r(h0), r(a.get("out")), r(hT), seg, ws, ws_size, None)
+                          r(h0), r(a.get("out")), r(hT), seg, first, ws, ws_size, None)
 
 
 def test_cp_workspace_size(lib):
     rec = 61952
     # fewer than three segments: kda_fwd's workspace
-    assert lib.kda_fwd_cp_workspace_size(2, 1000, 4, 8) == lib.kda_fwd_workspace_size(2000, 2, 4)
+    assert lib.kda_fwd_cp_workspace_size(2, 1000, 4, 8, 0) == lib.kda_fwd_workspace_size(2000, 2, 4)
+    assert lib.kda_fwd_cp_workspace_size(2, 8192, 4, 16, 120) == lib.kda_fwd_workspace_size(16384, 2, 4)
     # B=2, T=8192 (128 chunks), Hv=8, 16 chunks per segment: P = 8
     B, T, H, P = 2, 8192, 8, 8
-    recs = ((B * T + 63) // 64 + B * P) * H * rec
-    recs = (recs + 255) // 256 * 256
     blk = B * H * 128 * 128 * 4
-    assert lib.kda_fwd_cp_workspace_size(B, T, H, 16) == recs + 2 * (P - 2) * blk + (P - 1) * blk
+
+    def expect(P):
+        recs = ((B * T + 63) // 64 + B * P) * H * rec
+        return (recs + 255) // 256 * 256 + 2 * (P - 2) * blk + (P - 1) * blk
+    assert lib.kda_fwd_cp_workspace_size(B, T, H, 16, 0) == expect(8)
+    assert lib.kda_fwd_cp_workspace_size(B, T, H, 16, 16) == expect(8)
+    # a first segment of 32 chunks, then 16 each: 1 + ceil(96 / 16) = 7 segments
+    assert lib.kda_fwd_cp_workspace_size(B, T, H, 16, 32) == expect(7)
     # a partial last segment counts: 1000 tokens = 16 chunks, 5 per segment -> 4 segments
-    assert lib.kda_fwd_cp_workspace_size(1, 1000, 2, 5) > lib.kda_fwd_workspace_size(1000, 1, 2)
-    for bad in ((-1, 10, 2, 1), (1, -1, 2, 1), (1, 10, -2, 1), (1, 10, 2, 0)):
+    assert lib.kda_fwd_cp_workspace_size(1, 1000, 2, 5, 0) > lib.kda_fwd_workspace_size(1000, 1, 2)
+    for bad in ((-1, 10, 2, 1, 0), (1, -1, 2, 1, 0), (1, 10, -2, 1, 0), (1, 10, 2, 0, 0), (1, 10, 2, 1, -1)):
         assert lib.kda_fwd_cp_workspace_size(*bad) == -1
 
 
 def test_cp_checked_before_launch(lib):
     a = good(B=2, T_=1024)   # 16 chunks
     st = lambda: T([2, 2, 128, 128], binding.KDA_F32)  # noqa: E731
-    for seg in (0, -3):
-        assert binding.STATUS_NAMES[call_cp(lib, a, seg, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_VALUE"
+    for seg, first in ((0, 0), (-3, 0), (4, -1)):
+        assert binding.STATUS_NAMES[call_cp(lib, a, seg, first, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_VALUE"
     # segmented (4 segments): the workspace is required and sized by kda_fwd_cp_workspace_size
-    need = lib.kda_fwd_cp_workspace_size(2, 1024, 2, 4)
+    need = lib.kda_fwd_cp_workspace_size(2, 1024, 2, 4, 0)
     assert binding.STATUS_NAMES[call_cp(lib, a, 4)] == "KDA_ERR_WORKSPACE"
     assert binding.STATUS_NAMES[call_cp(lib, a, 4, ws=FAKE, ws_size=need - 1)] == "KDA_ERR_WORKSPACE"
     assert binding.STATUS_NAMES[call_cp(lib, a, 4, ws=FAKE + 8, ws_size=need)] == "KDA_ERR_WORKSPACE"
+    need2 = lib.kda_fwd_cp_workspace_size(2, 1024, 2, 3, 6)   # 6 + 3 + 3 + 3 + 1 chunks: 5 segments
+    assert binding.STATUS_NAMES[call_cp(lib, a, 3, 6, ws=FAKE, ws_size=need2 - 1)] == "KDA_ERR_WORKSPACE"
     # the tensor checks of kda_fwd come first
     b = good(B=2, T_=1024)
     b["q"] = T([2, 1024, 2, 64])
@@ -327,13 +335,24 @@ def test_cp_checked_before_launch(lib):
         assert binding.STATUS_NAMES[call_cp(lib, a, 4, scale=s, ws=FAKE, ws_size=need)] == "KDA_ERR_VALUE"
 
 
-def test_cp_segment_suggestion(lib):
-    # a batch that fills the chip, or short sequences: the ordinary path
-    assert lib.kda_fwd_cp_segment_chunks(2, 8192, 64, 256) == 0
-    assert lib.kda_fwd_cp_segment_chunks(1, 1024, 8, 256) == 0
-    # few heads, long sequences: at least three segments
+def plan(lib, B, T, H, cus=256):
+    seg, first = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    ok = lib.kda_fwd_cp_plan(B, T, H, cus, ctypes.byref(seg), ctypes.byref(first))
+    return ok, seg.value, first.value
+
+
+def test_cp_plan(lib):
+    # a batch that fills the GPU, or short sequences: the ordinary path, zeros written
+    assert plan(lib, 2, 8192, 64) == (0, 0, 0)
+    assert plan(lib, 1, 1024, 8) == (0, 0, 0)
+    assert plan(lib, 1, 4096, 64) == (0, 0, 0)   # grouped values with 64 value heads: measured no gain
+    # few heads, long sequences: at least three segments, the first no shorter than the others
     for B, T, H in ((1, 65536, 8), (2, 8192, 8), (1, 32768, 16)):
-        L = lib.kda_fwd_cp_segment_chunks(B, T, H, 256)
-        assert L >= 1 and -(-(T // 64) // L) >= 3, (B, T, H, L)
+        ok, L, L0 = plan(lib, B, T, H)
+        nch = T // 64
+        assert ok == 1 and L >= 1 and L0 >= L, (B, T, H, L, L0)
+        assert nch > L0 and 1 + -(-(nch - L0) // L) >= 3, (B, T, H, L, L0)
     for bad in ((0, 8192, 8, 256), (1, 0, 8, 256), (1, 8192, 0, 256), (1, 8192, 8, 0)):
-        assert lib.kda_fwd_cp_segment_chunks(*bad) == 0
+        assert plan(lib, *bad) == (0, 0, 0)
+    # NULL outputs are allowed
+    assert lib.kda_fwd_cp_plan(1, 65536, 8, 256, None, None) == 1

@@ -32,16 +32,16 @@ def _gpu():
     yield
 
 
-def run_cp(x, seg_chunks, want_state=True):
+def run_cp(x, seg_chunks, first_chunks=0, want_state=True):
     d = to_device(x)
-    o, hT = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, seg_chunks, initial_state=d["h0"],
-                       final_state=True if want_state else None)
+    o, hT = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, seg_chunks, first_chunks,
+                       initial_state=d["h0"], final_state=True if want_state else None)
     torch.cuda.synchronize()
     return o, hT
 
 
-def check_cp(x, seg_chunks, label):
-    o, hT = run_cp(x, seg_chunks)
+def check_cp(x, seg_chunks, label, first_chunks=0):
+    o, hT = run_cp(x, seg_chunks, first_chunks)
     o, hT = o.float().cpu().numpy(), hT.cpu().numpy()
     o_ref, h_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], SCALE, h0=x["h0"])
     rel = rel_frob_per_head(o, o_ref)
@@ -54,16 +54,18 @@ def check_cp(x, seg_chunks, label):
     assert srel <= STATE_REL_F, srel
 
 
-@pytest.mark.parametrize("B,T,Hq,Hv,seg,beta,h0", [
-    (1, 1000, 2, 2, 3, torch.float32, True),     # 6 segments, the last one a partial chunk
-    (3, 640, 3, 3, 1, torch.float32, True),      # one chunk per segment: 10 segments, 8 composed maps
-    (2, 4096, 2, 8, 8, torch.bfloat16, False),   # grouped values, 8 segments
-    (1, 193, 2, 2, 1, torch.float32, True),      # 4 segments of one chunk, 1-token tail
+@pytest.mark.parametrize("B,T,Hq,Hv,seg,first,beta,h0", [
+    (1, 1000, 2, 2, 3, 0, torch.float32, True),     # 6 segments, the last one a partial chunk
+    (3, 640, 3, 3, 1, 0, torch.float32, True),      # one chunk per segment: 10 segments, 8 composed maps
+    (2, 4096, 2, 8, 8, 0, torch.bfloat16, False),   # grouped values, 8 segments
+    (1, 193, 2, 2, 1, 0, torch.float32, True),      # 4 segments of one chunk, 1-token tail
+    (2, 1500, 2, 2, 3, 7, torch.float32, True),     # a 7-chunk first segment, then 3 each; a 28-token tail
+    (1, 4096, 1, 4, 16, 32, torch.bfloat16, False), # grouped values, first segment of half the sequence
 ])
-def test_segmented_matches_oracle(B, T, Hq, Hv, seg, beta, h0):
-    _say(f"kda_fwd_cp B={B} T={T} Hq={Hq} Hv={Hv} segment_chunks={seg} h0={h0}")
+def test_segmented_matches_oracle(B, T, Hq, Hv, seg, first, beta, h0):
+    _say(f"kda_fwd_cp B={B} T={T} Hq={Hq} Hv={Hv} segment_chunks={seg} first={first} h0={h0}")
     x = make_inputs(B, T, Hq, Hv, beta, h0=h0, seed=200 + T)
-    check_cp(x, seg, f"cp B={B} T={T} seg={seg}")
+    check_cp(x, seg, f"cp B={B} T={T} seg={seg} first={first}", first)
 
 
 def test_segmented_long_sequence():
@@ -79,9 +81,12 @@ def test_two_segments_or_fewer_is_kda_fwd_bitwise():
     o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
     o2, h2 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 2, initial_state=d["h0"],
                         final_state=True)
+    o3, h3 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 1, 3, initial_state=d["h0"],
+                        final_state=True)   # 3 + 1 chunks: two segments
     torch.cuda.synchronize()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
-    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
+    for o, h in ((o2, h2), (o3, h3)):
+        assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
+        assert torch.equal(h1.view(torch.int32), h.view(torch.int32))
 
 
 def test_segmented_is_repeatable_and_may_update_the_state_in_place():
