@@ -103,3 +103,32 @@ def test_segmented_is_repeatable_and_may_update_the_state_in_place():
         assert torch.equal(o1.view(torch.int16), o.view(torch.int16))
     for h in (h2, h3):
         assert torch.equal(h1.view(torch.int32), h.view(torch.int32))
+
+
+@pytest.mark.parametrize("name,heads", [("mha_b1_h8_t65536", [0, 7]), ("mha_b2_h8_t8192", [2, 5])])
+def test_bench_workloads_with_the_plan(name, heads):
+    """The few-head workloads bench.py --cp times, with the segment lengths it
+    takes from kda_fwd_cp_plan; the oracle checks the sampled heads."""
+    from gated_delta_rule_35_amd import kda_fwd_cp_plan
+    from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
+    from tests.kda_check import head_subset
+    w = WORKLOADS[name]
+    x, _ = workload_inputs(w)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    plan = kda_fwd_cp_plan(B, T, w.Hv)
+    assert plan is not None
+    L, L0 = plan
+    _say(f"{name} with the plan ({L0} chunks, then {L}), oracle on heads {heads}")
+    d = to_device(x)
+    o, hT = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, L, L0, initial_state=d["h0"],
+                       final_state=True)
+    torch.cuda.synchronize()
+    o = o[:, :, heads].float().cpu().numpy()
+    hT = hT[:, heads].cpu().numpy()
+    sub = head_subset(x, heads, w.Hq, w.Hv)
+    o_ref, h_ref = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], w.scale, h0=sub["h0"])
+    rel = rel_frob_per_head(o, o_ref)
+    mx = float(np.max(np.abs(o - o_ref)))
+    srel = state_rel_frob(hT, h_ref)
+    _say(f"{name}: o relF={rel:.3e} maxabs={mx:.3e} state relF={srel:.3e}")
+    assert rel <= O_REL_F and mx <= O_MAX_ABS and srel <= STATE_REL_F, (rel, mx, srel)
