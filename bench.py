@@ -122,20 +122,42 @@ def bench_decode(args):
     s = {k: x[k][:, 0].contiguous().to(dev) for k in ("q", "k", "v", "g", "beta")}
     state = x["h0"].to(dev)
     out = torch.empty_like(s["v"])
-    stream = torch.cuda.current_stream(dev)
     scale = 128 ** -0.5
-    for _ in range(args.warmup):
+
+    def one():
         kda_decode(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, state, out=out)
+
+    per_launch = args.graph if args.graph > 0 else 1
+    if args.graph > 0:
+        # K steps (the state updated in place each time) captured once into a HIP
+        # graph; a timed launch replays all K
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.graph):
+                one()
+        launch = graph.replay
+        log(f"decode: {args.graph} steps per graph replay")
+    else:
+        launch = one
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        launch()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        kda_decode(s["q"], s["k"], s["v"], s["g"], s["beta"], scale, state, out=out)
+        launch()
         e[1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    wall = (time.perf_counter() - t0) / per_launch
+    ms = [e[0].elapsed_time(e[1]) / per_launch for e in ev]
     t = sum(ms) / len(ms) / 1e3
     nbytes = decode_bytes(N, H, H, 4)
     gbs = nbytes / t / 1e9
@@ -145,11 +167,13 @@ def bench_decode(args):
            "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": f"decode_n{N}_h{H}", "N_sequences": N, "Hq": H, "Hv": H, "dk": 128, "dv": 128,
-                      "beta_dtype": "fp32", "state": "fp32, updated in place"},
+                      "beta_dtype": "fp32", "state": "fp32, updated in place", "steps_per_graph": args.graph or None},
            "kernel_ms_avg": round(t * 1e3, 5), "algorithmic_bytes_per_step": nbytes,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                        "scope": "kda_decode_kernel: algorithmic bytes over its average duration"},
+                        "scope": ("kda_decode_kernel: algorithmic bytes over its average duration" if not args.graph else
+                                  f"kda_decode_kernel: algorithmic bytes over the time per step of a {args.graph}-step "
+                                  "HIP graph replay")},
            "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
@@ -279,6 +303,8 @@ def main():
                     help="the oracle's sample is run repeatedly until this much wall time has passed")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="instead of the forward, time kda_decode: one step for N sequences x 64 heads")
+    ap.add_argument("--graph", type=int, default=0, metavar="K",
+                    help="with --decode: capture K steps in one HIP graph and time its replays (per step)")
     ap.add_argument("--cp", type=int, default=-1, metavar="L",
                     help="instead of the headline, time kda_fwd_cp on --workload with L chunks per segment "
                          "(0: the library's suggestion) against kda_fwd")
