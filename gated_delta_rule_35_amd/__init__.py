@@ -1,4 +1,4 @@
-"""MI355X-native Kimi Delta Attention (KDA): chunked forward and decode step.
+"""MI355X-native Kimi Delta Attention (KDA): chunked forward, decode step and backward.
 
 The compute lives in libkda.so (hand-written HIP for gfx950, C ABI in
 include/kda.h).  This package is a thin ctypes binding: it turns torch tensors
@@ -6,10 +6,10 @@ into C descriptors and passes the current HIP stream; every step of the forward
 pass runs in the library's kernels.  There is no fallback: if libkda.so is
 missing or the tensors are not on the GPU, the call raises.
 """
-from .binding import (KdaError, kda_decode, kda_dv_slices, kda_fwd, kda_fwd_cp,  # noqa: F401
+from .binding import (KdaError, kda_bwd, kda_bwd_workspace_size, kda_decode, kda_dv_slices, kda_fwd, kda_fwd_cp,  # noqa: F401
                       kda_fwd_cp_plan, kda_fwd_cp_workspace_size, kda_fwd_intra, kda_fwd_scan,
                       kda_fwd_trace, kda_fwd_workspace_size, library_path, load_library)
 
-__all__ = ["KdaError", "kda_decode", "kda_dv_slices", "kda_fwd", "kda_fwd_cp", "kda_fwd_cp_plan",
+__all__ = ["KdaError", "kda_bwd", "kda_bwd_workspace_size", "kda_decode", "kda_dv_slices", "kda_fwd", "kda_fwd_cp", "kda_fwd_cp_plan",
            "kda_fwd_cp_workspace_size", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_workspace_size",
            "library_path", "load_library"]

@@ -23,8 +23,8 @@ _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
 EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode",
-            "kda_fwd_workspace_size", "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_status_string",
-            "kda_dv_slices"]
+            "kda_bwd", "kda_fwd_workspace_size", "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan",
+            "kda_bwd_workspace_size", "kda_status_string", "kda_dv_slices"]
 
 
 class KdaTensor(ctypes.Structure):
@@ -77,6 +77,11 @@ def load_library(path=None):
     lib.kda_fwd_cp_plan.restype = ctypes.c_int32
     lib.kda_decode.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_void_p]
     lib.kda_decode.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float] + [tp] * 9 + [ctypes.c_void_p, ctypes.c_int64,
+                                                                           ctypes.c_void_p]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd_workspace_size.argtypes = [ctypes.c_int64] * 4
+    lib.kda_bwd_workspace_size.restype = ctypes.c_int64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_dv_slices.argtypes = [ctypes.c_int64, ctypes.c_int64]
@@ -285,3 +290,43 @@ def kda_decode(q, k, v, g, beta, scale, state, out=None, new_state=None, stream=
     _check(lib, lib.kda_decode(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
                                float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), s))
     return out, new_state
+
+
+def kda_bwd_workspace_size(batch, seq_len, num_qk_heads, num_value_heads):
+    """Bytes of device workspace kda_bwd needs (see include/kda.h)."""
+    return int(load_library().kda_bwd_workspace_size(batch, seq_len, num_qk_heads, num_value_heads))
+
+
+def kda_bwd(q, k, v, g, beta, scale, d_out, initial_state=None, d_final_state=None, grads=None,
+            d_initial_state=False, stream=None, workspace=None):
+    """Gradients of the forward over a fixed-length batch: q, k [B, T, Hq, 128] and
+    v, d_out [B, T, Hv, 128] bf16; g [B, T, Hv, 128] fp32; beta [B, T, Hv].
+    Returns a dict with dq, dk, dv, dg, dbeta (fp32, the inputs' shapes) and dh0
+    ([B, Hv, 128, 128] fp32 when d_initial_state is True or a tensor, else None).
+    `grads` may hold preallocated outputs under those names."""
+    lib = load_library()
+    B, T, Hq, _ = q.shape
+    Hv = v.shape[2]
+    dev = v.device
+    out = dict(grads or {})
+    f32 = torch.float32
+    for name, shape in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dg", g.shape), ("dbeta", beta.shape)):
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=f32, device=dev)
+    if isinstance(d_initial_state, torch.Tensor):
+        out["dh0"] = d_initial_state
+    elif d_initial_state:
+        out["dh0"] = torch.empty((B, Hv, q.shape[3], v.shape[3]), dtype=f32, device=dev)
+    else:
+        out["dh0"] = None
+    tensors = (q, k, v, g, beta, initial_state, d_out, d_final_state, out["dq"], out["dk"], out["dv"], out["dg"],
+               out["dbeta"], out["dh0"])
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kda_bwd needs every tensor on the GPU")
+    descs = [describe(t) for t in tensors]
+    s = _stream_handle(stream, tensors)
+    ws, ws_size = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    _check(lib, lib.kda_bwd(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
+                            float(scale), *[_ref(d) for d in descs[5:]], ws, ws_size, s))
+    return out

@@ -451,6 +451,126 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
     return finish(kda::launch_kda_decode(p, hs), hs);
 }
 
+}  // extern "C"
+
+// ---- backward ----
+namespace {
+// Workspace of kda_bwd, in 256-byte aligned blocks: the chunk operands (G, Aqk, T,
+// Abar), the states entering the chunks, the state gradients leaving them, then,
+// when Hq < Hv, dq and dk per value head.
+struct BwdLayout {
+    int64_t prep, hs, dhs, dqv, dkv, total;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hv) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t units = B * ((T + 63) / 64) * Hv;
+    BwdLayout L{};
+    L.prep = 0;
+    L.hs = L.prep + up(units * kda::BWP_FLOATS * 4);
+    L.dhs = L.hs + up(units * kHeadDim * kHeadDim * 4);
+    L.dqv = L.dhs + up(units * kHeadDim * kHeadDim * 4);
+    const int64_t per = Hq < Hv ? up(B * T * Hv * kHeadDim * 4) : 0;
+    L.dkv = L.dqv + per;
+    L.total = L.dkv + per;
+    return L;
+}
+}  // namespace
+
+extern "C" {
+
+int64_t kda_bwd_workspace_size(int64_t batch, int64_t seq_len, int64_t num_qk_heads, int64_t num_value_heads) {
+    if (batch < 0 || seq_len < 0 || num_qk_heads <= 0 || num_value_heads <= 0) return -1;
+    return bwd_layout(batch, seq_len, num_qk_heads, num_value_heads).total;
+}
+
+kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                     const kda_tensor_t* beta, float scale, const kda_tensor_t* initial_state,
+                     const kda_tensor_t* d_out, const kda_tensor_t* d_final_state, const kda_tensor_t* dq,
+                     const kda_tensor_t* dk, const kda_tensor_t* dv, const kda_tensor_t* dg,
+                     const kda_tensor_t* dbeta, const kda_tensor_t* d_initial_state, void* workspace,
+                     int64_t workspace_size, void* stream) {
+    kda_status_t st;
+    if ((st = check_tensor(q, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(k, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(v, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(g, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if (!beta) return KDA_ERR_NULL;
+    if ((st = check_tensor(beta, 3, KDA_BF16, KDA_F32, elem_size(beta->dtype))) != KDA_OK) return st;
+    if (initial_state && (st = check_tensor(initial_state, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(d_out, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+    if (d_final_state && (st = check_tensor(d_final_state, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(dq, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(dk, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(dv, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(dg, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+    if ((st = check_tensor(dbeta, 3, KDA_F32, KDA_F32, 4)) != KDA_OK) return st;
+    if (d_initial_state && (st = check_tensor(d_initial_state, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
+
+    const int64_t B = q->shape[0], T = q->shape[1], Hq = q->shape[2], Hv = v->shape[2];
+    if (q->shape[3] != kHeadDim || v->shape[3] != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    if (!same_shape(k, q->shape, 4) || !same_shape(dq, q->shape, 4) || !same_shape(dk, q->shape, 4))
+        return KDA_ERR_SHAPE;
+    if (v->shape[0] != B || v->shape[1] != T) return KDA_ERR_SHAPE;
+    const int64_t gs[4] = {B, T, Hv, kHeadDim};
+    if (!same_shape(g, gs, 4) || !same_shape(d_out, gs, 4) || !same_shape(dv, gs, 4) || !same_shape(dg, gs, 4))
+        return KDA_ERR_SHAPE;
+    const int64_t bs[3] = {B, T, Hv};
+    if (!same_shape(beta, bs, 3) || !same_shape(dbeta, bs, 3)) return KDA_ERR_SHAPE;
+    const int64_t ss[4] = {B, Hv, kHeadDim, kHeadDim};
+    if (initial_state && !same_shape(initial_state, ss, 4)) return KDA_ERR_SHAPE;
+    if (d_final_state && !same_shape(d_final_state, ss, 4)) return KDA_ERR_SHAPE;
+    if (d_initial_state && !same_shape(d_initial_state, ss, 4)) return KDA_ERR_SHAPE;
+    if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
+    if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
+    const int64_t nc = (T + 63) / 64;
+    if (B * nc * Hv > kMaxBlocks || B * Hv * 8 > kMaxBlocks || B > (int64_t(1) << 24) || Hv > (int64_t(1) << 16))
+        return KDA_ERR_UNSUPPORTED;
+    if (B * T * Hq * kHeadDim > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
+    const BwdLayout L = bwd_layout(B, T, Hq, Hv);
+    if (workspace && (workspace_size < L.total || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        return KDA_ERR_WORKSPACE;
+
+    kda::BwdParams p{};
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.k = static_cast<const uint16_t*>(k->data);
+    p.v = static_cast<const uint16_t*>(v->data);
+    p.dO = static_cast<const uint16_t*>(d_out->data);
+    p.g = static_cast<const float*>(g->data);
+    p.beta = beta->data;
+    p.beta_f32 = beta->dtype == KDA_F32 ? 1 : 0;
+    p.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
+    p.dhT = d_final_state ? static_cast<const float*>(d_final_state->data) : nullptr;
+    p.dq = static_cast<float*>(dq->data);
+    p.dk = static_cast<float*>(dk->data);
+    p.dv = static_cast<float*>(dv->data);
+    p.dg = static_cast<float*>(dg->data);
+    p.dbeta = static_cast<float*>(dbeta->data);
+    p.dh0 = d_initial_state ? static_cast<float*>(d_initial_state->data) : nullptr;
+    p.T = T;
+    p.B = static_cast<int32_t>(B);
+    p.Hq = static_cast<int32_t>(Hq);
+    p.Hv = static_cast<int32_t>(Hv);
+    p.nc = static_cast<int32_t>(nc);
+    p.scale = scale;
+    if (B == 0 || (T == 0 && !d_initial_state)) return KDA_OK;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (!ws && T > 0 && hipMallocAsync(&ws, (size_t)L.total, hs) != hipSuccess) return KDA_ERR_HIP;
+    char* base = static_cast<char*>(ws);
+    if (base) {
+        p.prep = reinterpret_cast<float*>(base + L.prep);
+        p.hs = reinterpret_cast<float*>(base + L.hs);
+        p.dhs = reinterpret_cast<float*>(base + L.dhs);
+        p.dqv = Hq < Hv ? reinterpret_cast<float*>(base + L.dqv) : p.dq;
+        p.dkv = Hq < Hv ? reinterpret_cast<float*>(base + L.dkv) : p.dk;
+    }
+    hipError_t e = kda::launch_kda_bwd(p, hs);
+    if (!workspace && ws && hipFreeAsync(ws, hs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+    return finish(e, hs);
+}
+
 const char* kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";

@@ -1,0 +1,521 @@
+// KDA backward pass on gfx950 (MI355X): gradients of the chunked forward with
+// respect to q, k, v, g, beta and the initial state, for fixed-length batches.
+//
+// The pages list chunk backward kernels beside the forward ("cuLA REPO_LAYOUT.md",
+// the kda/ entries for chunk_bwd and the WY dq/dk/dg kernels) but give no
+// equation; these are the forward's chunk equations differentiated.  Per
+// 64-token chunk of one (sequence, value head), with h the state entering it,
+// G the chunk-local inclusive cumsum of g, kg = k e^G, qg = scale q e^G,
+// kh = k e^(G_last - G), gam = e^G_last, Aqk[i][j] = scale sum_c q_i k_j
+// e^(G_i - G_j) (j <= i), Abar[i][j] = sum_c k_i k_j e^(G_i - G_j) (j < i),
+// T = (I + diag(beta) Abar)^-1 and Tb = T diag(beta), the forward is
+//
+//   Z = v - kg h,  v_new = Tb Z,  o = qg h + Aqk v_new,  h' = gam * h + kh^T v_new
+//
+// and, for given do and dh' (the gradient of the state leaving the chunk),
+//
+//   dv_new = Aqk^T do + kh dh',  dZ = Tb^T dv_new,  dv = dZ,
+//   dh     = gam * dh' + qg^T do - kg^T dZ,
+//
+// with the operand gradients d(qg) = do h^T, d(kg) = -dZ h^T, d(kh) = v_new dh'^T,
+// dAqk = lower(do v_new^T), dTb = dv_new Z^T, dgam = rowsum(dh' * h), taken back to
+// q, k, beta and g through their definitions (dA = -T^T dT T^T on the strict lower
+// triangle, and dg the reverse cumsum of dG within the chunk).
+//
+// Five kernels, all fp32 on the vector ALUs with LDS tiles:
+//   prep    one work-group per (chunk, value head): G, Aqk, Abar and T
+//   states  one per (sequence, value head, 16 value columns): walks the chunks
+//           forward and stores each chunk's entering state h
+//   dstate  the same grid, walking the chunks backward: stores each chunk's dh'
+//           and writes the initial state's gradient
+//   grad    one per (chunk, value head): dv, dbeta, and dq, dk, dg per value head
+//   group   sums dq and dk over the value heads that share a q/k head
+// Every output element has one writer and a fixed summation order, so results
+// are bitwise reproducible.
+#include "kda_device.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int BW_C = 64;      // chunk length
+constexpr int BW_D = 128;     // head dimension
+constexpr int BW_LD = 129;    // row stride of [64][128] LDS tiles: odd, so a column read across rows spreads over banks
+constexpr int BW_MD = 65;     // row stride of [64][64] LDS tiles
+constexpr int BW_SL = 16;     // value columns per scan work-group
+constexpr int BW_SD = 17;     // row stride of [*][16] LDS tiles
+constexpr int BW_NSL = BW_D / BW_SL;
+constexpr int64_t BW_STATE = (int64_t)BW_D * BW_D;
+
+__device__ __forceinline__ float ld_beta(const BwdParams& p, int64_t idx) {
+    return p.beta_f32 ? static_cast<const float*>(p.beta)[idx] : bf2f(static_cast<const uint16_t*>(p.beta)[idx]);
+}
+
+struct ChunkIdx {
+    int b, ci, hv, hq, len;
+    int64_t t0, ch;   // first token of the chunk within its row; (chunk, value head) index
+};
+
+// Work-group index of a (chunk, value head) grid: blk = (b * nc + ci) * Hv + hv.
+__device__ __forceinline__ ChunkIdx chunk_of(const BwdParams& p, int64_t blk) {
+    ChunkIdx x;
+    x.hv = (int)(blk % p.Hv);
+    const int64_t cid = blk / p.Hv;
+    x.b = (int)(cid / p.nc);
+    x.ci = (int)(cid % p.nc);
+    x.hq = x.hv / (p.Hv / p.Hq);
+    x.t0 = (int64_t)x.ci * BW_C;
+    const int64_t rest = p.T - x.t0;
+    x.len = rest < BW_C ? (int)rest : BW_C;
+    x.ch = blk;
+    return x;
+}
+
+__device__ __forceinline__ int64_t qk_off(const BwdParams& p, int b, int64_t t, int hq) {
+    return (((int64_t)b * p.T + t) * p.Hq + hq) * BW_D;
+}
+__device__ __forceinline__ int64_t vh_off(const BwdParams& p, int b, int64_t t, int hv) {
+    return (((int64_t)b * p.T + t) * p.Hv + hv) * BW_D;
+}
+
+// ---------------------------------------------------------------- prep
+__global__ void __launch_bounds__(256) kda_bwd_prep_kernel(const BwdParams p) {
+    __shared__ float sQ[BW_C * BW_LD], sK[BW_C * BW_LD], sG[BW_C * BW_LD];
+    __shared__ float sA[BW_C * BW_MD], sT[BW_C * BW_MD], sB[BW_C];
+    const int tid = threadIdx.x;
+    const ChunkIdx x = chunk_of(p, blockIdx.x);
+    for (int e = tid; e < BW_C * BW_D; e += 256) {
+        const int i = e >> 7, c = e & 127;
+        float qv = 0.f, kv = 0.f, gv = 0.f;   // rows past the sequence's end: q = k = 0, g = 0
+        if (i < x.len) {
+            const int64_t t = x.t0 + i;
+            qv = bf2f(p.q[qk_off(p, x.b, t, x.hq) + c]);
+            kv = bf2f(p.k[qk_off(p, x.b, t, x.hq) + c]);
+            gv = p.g[vh_off(p, x.b, t, x.hv) + c];
+        }
+        sQ[i * BW_LD + c] = qv;
+        sK[i * BW_LD + c] = kv;
+        sG[i * BW_LD + c] = gv;
+    }
+    if (tid < BW_C) sB[tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
+    __syncthreads();
+    if (tid < BW_D) {   // chunk-local inclusive cumsum; padded rows repeat the last valid G
+        float run = 0.f;
+        for (int i = 0; i < BW_C; ++i) {
+            run += sG[i * BW_LD + tid];
+            sG[i * BW_LD + tid] = run;
+        }
+    }
+    __syncthreads();
+    float* pr = p.prep + x.ch * BWP_FLOATS;
+    for (int e = tid; e < BW_C * BW_D; e += 256) pr[BWP_G + e] = sG[(e >> 7) * BW_LD + (e & 127)];
+    // Aqk (j <= i) and Abar (j < i): one wave per row i, lane j.
+    for (int e = tid; e < BW_C * BW_C; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        float aq = 0.f, ak = 0.f;
+        if (j <= i) {
+            for (int c = 0; c < BW_D; ++c) {
+                const float d = fexp(sG[i * BW_LD + c] - sG[j * BW_LD + c]) * sK[j * BW_LD + c];
+                aq += sQ[i * BW_LD + c] * d;
+                ak += sK[i * BW_LD + c] * d;
+            }
+            if (j == i) ak = 0.f;
+        }
+        pr[BWP_AQK + e] = p.scale * aq;
+        pr[BWP_ABAR + e] = ak;
+        sA[i * BW_MD + j] = ak;
+    }
+    __syncthreads();
+    // T = (I + diag(beta) Abar)^-1 by forward substitution: lane j owns column j,
+    // T[i][j] = delta_ij - beta_i sum_{j <= m < i} Abar[i][m] T[m][j].
+    if (tid < BW_C) {
+        const int j = tid;
+        for (int i = 0; i < BW_C; ++i) {
+            float t = 0.f;
+            if (i == j) {
+                t = 1.f;
+            } else if (i > j) {
+                float s = 0.f;
+                for (int m = j; m < i; ++m) s += sA[i * BW_MD + m] * sT[m * BW_MD + j];
+                t = -sB[i] * s;
+            }
+            sT[i * BW_MD + j] = t;
+            pr[BWP_T + i * BW_C + j] = t;
+        }
+    }
+}
+
+// Loads the chunk's decayed key operands and Tb into LDS (shared by states and dstate).
+__device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx& x, const float* pr, float* sKG,
+                                             float* sKH, float* sQG, float* sTB, int tid, int nthreads) {
+    for (int e = tid; e < BW_C * BW_D; e += nthreads) {
+        const int i = e >> 7, c = e & 127;
+        float kv = 0.f, qv = 0.f;
+        if (i < x.len) {
+            kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
+            if (sQG) qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
+        }
+        const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
+        const float eG = fexp(G);
+        sKG[i * BW_LD + c] = kv * eG;
+        sKH[i * BW_LD + c] = kv * fexp(Gl - G);
+        if (sQG) sQG[i * BW_LD + c] = p.scale * qv * eG;
+    }
+    for (int e = tid; e < BW_C * BW_C; e += nthreads) {
+        const int i = e >> 6, j = e & 63;
+        const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
+        sTB[i * BW_MD + j] = pr[BWP_T + e] * bj;
+    }
+}
+
+// ---------------------------------------------------------------- states
+// Work-group (b, hv, slice): thread t holds state rows c = t % 128, columns
+// 8 (t / 128) .. + 7 of the slice.
+__global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) {
+    __shared__ float sKG[BW_C * BW_LD], sKH[BW_C * BW_LD], sTB[BW_C * BW_MD];
+    __shared__ float sS[BW_D * BW_SD], sV[BW_C * BW_SD], sZ[BW_C * BW_SD], sVN[BW_C * BW_SD];
+    const int tid = threadIdx.x;
+    const int slice = blockIdx.x % BW_NSL;
+    const int64_t bh = blockIdx.x / BW_NSL;
+    const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
+    const int n0 = slice * BW_SL;
+    const int c = tid & 127, nb = (tid >> 7) * 8;
+    float S[8];
+    for (int e = 0; e < 8; ++e)
+        S[e] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
+    const int zn = tid & 15, zi = tid >> 4;   // Z / v_new: column zn, rows zi + 16 r
+    for (int ci = 0; ci < p.nc; ++ci) {
+        const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
+        float* hs = p.hs + x.ch * BW_STATE + c * BW_D + n0 + nb;
+        for (int e = 0; e < 8; ++e) {
+            hs[e] = S[e];
+            sS[c * BW_SD + nb + e] = S[e];
+        }
+        if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
+        const float* pr = p.prep + x.ch * BWP_FLOATS;
+        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, 256);
+        for (int e = tid; e < BW_C * BW_SL; e += 256) {
+            const int i = e >> 4, n = e & 15;
+            sV[i * BW_SD + n] = i < x.len ? bf2f(p.v[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
+        }
+        const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
+        __syncthreads();
+        for (int r = 0; r < 4; ++r) {
+            const int i = zi + 16 * r;
+            float z = sV[i * BW_SD + zn];
+            for (int cc = 0; cc < BW_D; ++cc) z -= sKG[i * BW_LD + cc] * sS[cc * BW_SD + zn];
+            sZ[i * BW_SD + zn] = z;
+        }
+        __syncthreads();
+        for (int r = 0; r < 4; ++r) {
+            const int i = zi + 16 * r;
+            float u = 0.f;
+            for (int j = 0; j <= i; ++j) u += sTB[i * BW_MD + j] * sZ[j * BW_SD + zn];
+            sVN[i * BW_SD + zn] = u;
+        }
+        __syncthreads();
+        for (int e = 0; e < 8; ++e) {
+            float s = gam * S[e];
+            for (int i = 0; i < BW_C; ++i) s += sKH[i * BW_LD + c] * sVN[i * BW_SD + nb + e];
+            S[e] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- dstate
+__global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) {
+    __shared__ float sQG[BW_C * BW_LD], sKG[BW_C * BW_LD], sKH[BW_C * BW_LD];
+    __shared__ float sAQ[BW_C * BW_MD], sTB[BW_C * BW_MD];
+    __shared__ float sDH[BW_D * BW_SD], sDO[BW_C * BW_SD], sDVN[BW_C * BW_SD], sDZ[BW_C * BW_SD];
+    const int tid = threadIdx.x;
+    const int slice = blockIdx.x % BW_NSL;
+    const int64_t bh = blockIdx.x / BW_NSL;
+    const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
+    const int n0 = slice * BW_SL;
+    const int c = tid & 127, nb = (tid >> 7) * 8;
+    float dh[8];
+    for (int e = 0; e < 8; ++e)
+        dh[e] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
+    const int zn = tid & 15, zi = tid >> 4;
+    for (int ci = p.nc - 1; ci >= 0; --ci) {
+        const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
+        float* ds = p.dhs + x.ch * BW_STATE + c * BW_D + n0 + nb;
+        for (int e = 0; e < 8; ++e) {
+            ds[e] = dh[e];
+            sDH[c * BW_SD + nb + e] = dh[e];
+        }
+        const float* pr = p.prep + x.ch * BWP_FLOATS;
+        load_key_ops(p, x, pr, sKG, sKH, sQG, sTB, tid, 256);
+        for (int e = tid; e < BW_C * BW_C; e += 256) sAQ[(e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
+        for (int e = tid; e < BW_C * BW_SL; e += 256) {
+            const int i = e >> 4, n = e & 15;
+            sDO[i * BW_SD + n] = i < x.len ? bf2f(p.dO[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
+        }
+        const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
+        __syncthreads();
+        for (int r = 0; r < 4; ++r) {   // dv_new = Aqk^T do + kh dh'
+            const int i = zi + 16 * r;
+            float u = 0.f;
+            for (int m = i; m < BW_C; ++m) u += sAQ[m * BW_MD + i] * sDO[m * BW_SD + zn];
+            for (int cc = 0; cc < BW_D; ++cc) u += sKH[i * BW_LD + cc] * sDH[cc * BW_SD + zn];
+            sDVN[i * BW_SD + zn] = u;
+        }
+        __syncthreads();
+        for (int r = 0; r < 4; ++r) {   // dZ = Tb^T dv_new
+            const int i = zi + 16 * r;
+            float z = 0.f;
+            for (int m = i; m < BW_C; ++m) z += sTB[m * BW_MD + i] * sDVN[m * BW_SD + zn];
+            sDZ[i * BW_SD + zn] = z;
+        }
+        __syncthreads();
+        for (int e = 0; e < 8; ++e) {   // dh = gam dh' + qg^T do - kg^T dZ
+            float s = gam * dh[e];
+            for (int i = 0; i < BW_C; ++i)
+                s += sQG[i * BW_LD + c] * sDO[i * BW_SD + nb + e] - sKG[i * BW_LD + c] * sDZ[i * BW_SD + nb + e];
+            dh[e] = s;
+        }
+        __syncthreads();
+    }
+    if (p.dh0)
+        for (int e = 0; e < 8; ++e) p.dh0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] = dh[e];
+}
+
+// ---------------------------------------------------------------- grad
+// LDS of the grad kernel, in floats.  Phase A (the loop over value slices):
+constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * BW_LD, GA_AQ = GA_KH + BW_C * BW_LD, GA_TB = GA_AQ + BW_C * BW_MD;
+constexpr int GA_H = GA_TB + BW_C * BW_MD, GA_DH = GA_H + BW_D * BW_SD, GA_DO = GA_DH + BW_D * BW_SD;
+constexpr int GA_V = GA_DO + BW_C * BW_SD, GA_Z = GA_V + BW_C * BW_SD, GA_VN = GA_Z + BW_C * BW_SD;
+constexpr int GA_DVN = GA_VN + BW_C * BW_SD, GA_DZ = GA_DVN + BW_C * BW_SD, GA_END = GA_DZ + BW_C * BW_SD;
+// Phase B (the inverse's gradient), then phase C (the pairwise terms):
+constexpr int GC_Q = 0, GC_K = GC_Q + BW_C * BW_LD, GC_G = GC_K + BW_C * BW_LD, GC_DAQ = GC_G + BW_C * BW_LD;
+constexpr int GC_DAB = GC_DAQ + BW_C * BW_MD, GC_END = GC_DAB + BW_C * BW_MD;
+constexpr int GB_M1 = 0, GB_M2 = GB_M1 + BW_C * BW_MD, GB_DA = GB_M2 + BW_C * BW_MD, GB_BETA = GB_DA + BW_C * BW_MD;
+constexpr int GB_T = GB_BETA + BW_C, GB_AB = GB_T + BW_C * BW_MD, GB_DTB = GC_END, GB_END = GB_DTB + BW_C * BW_MD;
+static_assert(GB_AB + BW_C * BW_MD <= GC_DAQ, "phase B temporaries must not overlap dAqk / dAbar");
+constexpr int G_LDS = GA_END > GB_END ? GA_END : GB_END;
+static_assert(G_LDS * 4 <= 160 * 1024, "grad kernel LDS");
+
+__global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
+    __shared__ float F[G_LDS];
+    const int tid = threadIdx.x;
+    const ChunkIdx x = chunk_of(p, blockIdx.x);
+    const float* pr = p.prep + x.ch * BWP_FLOATS;
+    const float* hs = p.hs + x.ch * BW_STATE;
+    const float* ds = p.dhs + x.ch * BW_STATE;
+    // element (i, c) accumulators: c = tid % 128, rows i = rg + 4 r
+    const int c = tid & 127, rg = tid >> 7;
+    // 64 x 64 accumulators: row ai = tid / 8, columns aj = tid % 8 + 8 s
+    const int ai = tid >> 3, aj = tid & 7;
+    float aQ[16], aKG[16], aKH[16], aAQ[8], aTB[8], dgam = 0.f;
+    for (int r = 0; r < 16; ++r) aQ[r] = aKG[r] = aKH[r] = 0.f;
+    for (int s = 0; s < 8; ++s) aAQ[s] = aTB[s] = 0.f;
+
+    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512);
+    for (int e = tid; e < BW_C * BW_C; e += 512) F[GA_AQ + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
+    const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
+    for (int sl = 0; sl < BW_NSL; ++sl) {
+        const int n0 = sl * BW_SL;
+        for (int e = tid; e < BW_D * BW_SL; e += 512) {
+            const int cc = e >> 4, n = e & 15;
+            F[GA_H + cc * BW_SD + n] = hs[cc * BW_D + n0 + n];
+            F[GA_DH + cc * BW_SD + n] = ds[cc * BW_D + n0 + n];
+        }
+        for (int e = tid; e < BW_C * BW_SL; e += 512) {
+            const int i = e >> 4, n = e & 15;
+            const bool in = i < x.len;
+            const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
+            F[GA_DO + i * BW_SD + n] = in ? bf2f(p.dO[o]) : 0.f;
+            F[GA_V + i * BW_SD + n] = in ? bf2f(p.v[o]) : 0.f;
+        }
+        __syncthreads();
+        for (int r = 0; r < 2; ++r) {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
+            const int i = zi + 32 * r;
+            float z = F[GA_V + i * BW_SD + zn], u = 0.f;
+            for (int cc = 0; cc < BW_D; ++cc) {
+                z -= F[GA_KG + i * BW_LD + cc] * F[GA_H + cc * BW_SD + zn];
+                u += F[GA_KH + i * BW_LD + cc] * F[GA_DH + cc * BW_SD + zn];
+            }
+            for (int m = i; m < BW_C; ++m) u += F[GA_AQ + m * BW_MD + i] * F[GA_DO + m * BW_SD + zn];
+            F[GA_Z + i * BW_SD + zn] = z;
+            F[GA_DVN + i * BW_SD + zn] = u;
+        }
+        __syncthreads();
+        for (int r = 0; r < 2; ++r) {   // v_new = Tb Z;  dZ = Tb^T dv_new = dv
+            const int i = zi + 32 * r;
+            float vn = 0.f, dz = 0.f;
+            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + j * BW_SD + zn];
+            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + m * BW_SD + zn];
+            F[GA_VN + i * BW_SD + zn] = vn;
+            F[GA_DZ + i * BW_SD + zn] = dz;
+            if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + zn] = dz;
+        }
+        __syncthreads();
+        for (int n = 0; n < BW_SL; ++n) {
+            const float h = F[GA_H + c * BW_SD + n], dhv = F[GA_DH + c * BW_SD + n];
+            for (int r = 0; r < 16; ++r) {
+                const int i = rg + 4 * r;
+                aQ[r] += F[GA_DO + i * BW_SD + n] * h;
+                aKG[r] -= F[GA_DZ + i * BW_SD + n] * h;
+                aKH[r] += F[GA_VN + i * BW_SD + n] * dhv;
+            }
+            if (rg == 0) dgam += dhv * h;
+            for (int s = 0; s < 8; ++s) {
+                const int j = aj + 8 * s;
+                aAQ[s] += F[GA_DO + ai * BW_SD + n] * F[GA_VN + j * BW_SD + n];
+                aTB[s] += F[GA_DVN + ai * BW_SD + n] * F[GA_Z + j * BW_SD + n];
+            }
+        }
+        __syncthreads();
+    }
+
+    // Phase B: dA = lower_strict(-T^T (dTb diag beta) T^T), dbeta, dAbar = diag(beta) dA.
+    for (int s = 0; s < 8; ++s) {
+        const int j = aj + 8 * s;
+        F[GB_DTB + ai * BW_MD + j] = aTB[s];
+        F[GC_DAQ + ai * BW_MD + j] = j <= ai ? aAQ[s] : 0.f;
+    }
+    for (int e = tid; e < BW_C * BW_C; e += 512) {
+        F[GB_T + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_T + e];
+        F[GB_AB + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_ABAR + e];
+    }
+    if (tid < BW_C)
+        F[GB_BETA + tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
+    __syncthreads();
+    for (int s = 0; s < 8; ++s) {
+        const int j = aj + 8 * s;
+        F[GB_M1 + ai * BW_MD + j] = F[GB_DTB + ai * BW_MD + j] * F[GB_BETA + j];
+    }
+    __syncthreads();
+    for (int s = 0; s < 8; ++s) {   // M2 = T^T M1
+        const int j = aj + 8 * s;
+        float a = 0.f;
+        for (int m = 0; m < BW_C; ++m) a += F[GB_T + m * BW_MD + ai] * F[GB_M1 + m * BW_MD + j];
+        F[GB_M2 + ai * BW_MD + j] = a;
+    }
+    __syncthreads();
+    for (int s = 0; s < 8; ++s) {   // dA = -M2 T^T, strictly lower
+        const int j = aj + 8 * s;
+        float a = 0.f;
+        if (j < ai)
+            for (int m = 0; m < BW_C; ++m) a -= F[GB_M2 + ai * BW_MD + m] * F[GB_T + j * BW_MD + m];
+        F[GB_DA + ai * BW_MD + j] = a;
+    }
+    __syncthreads();
+    if (tid < BW_C) {
+        const int j = tid;
+        float db = 0.f;
+        for (int i = 0; i < BW_C; ++i) db += F[GB_DTB + i * BW_MD + j] * F[GB_T + i * BW_MD + j];
+        for (int m = 0; m < BW_C; ++m) db += F[GB_DA + j * BW_MD + m] * F[GB_AB + j * BW_MD + m];
+        if (j < x.len) p.dbeta[((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv] = db;
+    }
+    for (int s = 0; s < 8; ++s) {
+        const int j = aj + 8 * s;
+        F[GC_DAB + ai * BW_MD + j] = F[GB_BETA + ai] * F[GB_DA + ai * BW_MD + j];
+    }
+    __syncthreads();
+
+    // Phase C: q, k and G of the chunk, then the pairwise terms per channel.
+    for (int e = tid; e < BW_C * BW_D; e += 512) {
+        const int i = e >> 7, cc = e & 127;
+        float qv = 0.f, kv = 0.f;
+        if (i < x.len) {
+            qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + cc]);
+            kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + cc]);
+        }
+        F[GC_Q + i * BW_LD + cc] = qv;
+        F[GC_K + i * BW_LD + cc] = kv;
+        F[GC_G + i * BW_LD + cc] = pr[BWP_G + e];
+    }
+    __syncthreads();
+    const float Gl = F[GC_G + (BW_C - 1) * BW_LD + c];
+    float oq[16], ok[16], oG[16], oP[16];
+    for (int r = 0; r < 16; ++r) {
+        const int i = rg + 4 * r;
+        const float Gi = F[GC_G + i * BW_LD + c], qi = F[GC_Q + i * BW_LD + c], ki = F[GC_K + i * BW_LD + c];
+        float Rq = 0.f, Rk = 0.f, Cq = 0.f, Ck = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const float kE = F[GC_K + j * BW_LD + c] * fexp(Gi - F[GC_G + j * BW_LD + c]);
+            Rq += F[GC_DAQ + i * BW_MD + j] * kE;
+            Rk += F[GC_DAB + i * BW_MD + j] * kE;   // zero on the diagonal
+        }
+        for (int m = i; m < BW_C; ++m) {
+            const float E = fexp(F[GC_G + m * BW_LD + c] - Gi);
+            Cq += F[GC_DAQ + m * BW_MD + i] * F[GC_Q + m * BW_LD + c] * E;
+            Ck += F[GC_DAB + m * BW_MD + i] * F[GC_K + m * BW_LD + c] * E;
+        }
+        const float eG = fexp(Gi), eH = fexp(Gl - Gi);
+        oq[r] = p.scale * (aQ[r] * eG + Rq);
+        ok[r] = aKG[r] * eG + aKH[r] * eH + p.scale * Cq + Ck + Rk;
+        oP[r] = aKH[r] * ki * eH;
+        oG[r] = p.scale * qi * Rq + ki * Rk - p.scale * ki * Cq - ki * Ck + aKG[r] * ki * eG +
+                p.scale * aQ[r] * qi * eG - oP[r];
+    }
+    for (int r = 0; r < 16; ++r) {
+        const int i = rg + 4 * r;
+        if (i < x.len) {
+            const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + c;
+            p.dqv[o] = oq[r];
+            p.dkv[o] = ok[r];
+        }
+    }
+    __syncthreads();   // q and k are no longer read: reuse them for dG and the kh terms
+    for (int r = 0; r < 16; ++r) {
+        const int i = rg + 4 * r;
+        F[GC_Q + i * BW_LD + c] = oG[r];
+        F[GC_K + i * BW_LD + c] = oP[r];
+    }
+    __syncthreads();
+    if (rg == 0) {
+        // G_last collects sum_t dkh * kh and dgam * gam; dg is the reverse cumsum of dG.
+        float tot = dgam * fexp(Gl);
+        for (int i = 0; i < BW_C; ++i) tot += F[GC_K + i * BW_LD + c];
+        float run = tot;
+        for (int i = BW_C - 1; i >= 0; --i) {
+            run += F[GC_Q + i * BW_LD + c];
+            if (i < x.len) p.dg[vh_off(p, x.b, x.t0 + i, x.hv) + c] = run;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- group
+__global__ void __launch_bounds__(256) kda_bwd_group_kernel(const BwdParams p, int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over [B * T, Hq, 128]
+    if (e >= total) return;
+    const int c = (int)(e & 127);
+    const int64_t rest = e >> 7;
+    const int hq = (int)(rest % p.Hq);
+    const int64_t tok = rest / p.Hq;
+    const int group = p.Hv / p.Hq;
+    float sq = 0.f, sk = 0.f;
+    for (int u = 0; u < group; ++u) {
+        const int64_t o = (tok * p.Hv + (int64_t)hq * group + u) * BW_D + c;
+        sq += p.dqv[o];
+        sk += p.dkv[o];
+    }
+    p.dq[e] = sq;
+    p.dk[e] = sk;
+}
+
+}  // namespace
+
+hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream) {
+    const int64_t chunks = (int64_t)p.B * p.nc * p.Hv;
+    const int64_t scans = (int64_t)p.B * p.Hv * BW_NSL;
+    if (chunks > 0) {
+        hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(kda_bwd_states_kernel, dim3((unsigned)scans), dim3(256), 0, stream, p);
+    }
+    if (scans > 0) hipLaunchKernelGGL(kda_bwd_dstate_kernel, dim3((unsigned)scans), dim3(256), 0, stream, p);
+    if (chunks > 0) {
+        hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)chunks), dim3(512), 0, stream, p);
+        if (p.Hv != p.Hq) {
+            const int64_t total = (int64_t)p.B * p.T * p.Hq * BW_D;
+            hipLaunchKernelGGL(kda_bwd_group_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
+                               total);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

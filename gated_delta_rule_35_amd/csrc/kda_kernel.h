@@ -62,6 +62,37 @@ struct DecodeParams {
 
 hipError_t launch_kda_decode(const DecodeParams& p, hipStream_t stream);
 
+// Backward pass over a fixed-length batch [B, T] (kda_bwd.hip).
+struct BwdParams {
+    const uint16_t* q;     // [B, T, Hq, 128] bf16 bits
+    const uint16_t* k;     // [B, T, Hq, 128] bf16 bits
+    const uint16_t* v;     // [B, T, Hv, 128] bf16 bits
+    const uint16_t* dO;    // [B, T, Hv, 128] bf16 bits: gradient of the output
+    const float* g;        // [B, T, Hv, 128]
+    const void* beta;      // [B, T, Hv] bf16 bits or fp32
+    const float* h0;       // [B, Hv, 128, 128] or nullptr (zero state)
+    const float* dhT;      // [B, Hv, 128, 128] gradient of the final state, or nullptr (zero)
+    float* dq;             // [B, T, Hq, 128]
+    float* dk;             // [B, T, Hq, 128]
+    float* dv;             // [B, T, Hv, 128]
+    float* dg;             // [B, T, Hv, 128]
+    float* dbeta;          // [B, T, Hv]
+    float* dh0;            // [B, Hv, 128, 128] or nullptr (not written)
+    float* prep;           // [B * nc * Hv][BWP_FLOATS]: G, Aqk, T, Abar of each chunk
+    float* hs;             // [B * nc * Hv][128 * 128]: state entering each chunk
+    float* dhs;            // [B * nc * Hv][128 * 128]: gradient of the state leaving each chunk
+    float* dqv;            // [B, T, Hv, 128]: dq per value head (equals dq when Hq == Hv)
+    float* dkv;            // [B, T, Hv, 128]: dk per value head (equals dk when Hq == Hv)
+    int64_t T;
+    int32_t B, Hq, Hv, nc;  // nc = ceil(T / 64) chunks per row
+    int32_t beta_f32;
+    float scale;
+};
+constexpr int BWP_G = 0, BWP_AQK = 64 * 128, BWP_T = BWP_AQK + 64 * 64, BWP_ABAR = BWP_T + 64 * 64;
+constexpr int BWP_FLOATS = BWP_ABAR + 64 * 64;
+
+hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream);
+
 // Workspace bytes for the given sizes (one record per chunk slot and value head).
 int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
 

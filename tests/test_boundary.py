@@ -356,3 +356,76 @@ def test_cp_plan(lib):
         assert plan(lib, *bad) == (0, 0, 0)
     # NULL outputs are allowed
     assert lib.kda_fwd_cp_plan(1, 65536, 8, 256, None, None) == 1
+
+
+# ---- kda_bwd ----
+
+def good_bwd(B=2, T_=100, Hq=2, Hv=4, beta_dtype=binding.KDA_F32, h0=True, dh0=True):
+    F = binding.KDA_F32
+    return dict(q=T([B, T_, Hq, 128]), k=T([B, T_, Hq, 128]), v=T([B, T_, Hv, 128]), g=T([B, T_, Hv, 128], F),
+                beta=T([B, T_, Hv], beta_dtype), h0=T([B, Hv, 128, 128], F) if h0 else None,
+                do=T([B, T_, Hv, 128]), dhT=T([B, Hv, 128, 128], F), dq=T([B, T_, Hq, 128], F),
+                dk=T([B, T_, Hq, 128], F), dv=T([B, T_, Hv, 128], F), dg=T([B, T_, Hv, 128], F),
+                dbeta=T([B, T_, Hv], F), dh0=T([B, Hv, 128, 128], F) if dh0 else None)
+
+
+BWD_ARGS = ("q", "k", "v", "g", "beta")
+BWD_REST = ("h0", "do", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def call_bwd(lib, a, scale=0.088, ws=None, ws_size=0):
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    return lib.kda_bwd(*[r(a.get(n)) for n in BWD_ARGS], scale, *[r(a.get(n)) for n in BWD_REST], ws, ws_size,
+                       None)
+
+
+def expect_bwd(lib, a, name, **kw):
+    st = call_bwd(lib, a, **kw)
+    assert binding.STATUS_NAMES[st] == name, (binding.STATUS_NAMES[st], name)
+
+
+def test_bwd_workspace_size(lib):
+    unit = 20480 * 4 + 2 * 128 * 128 * 4
+    assert lib.kda_bwd_workspace_size(2, 8192, 64, 64) == 2 * 128 * 64 * unit
+    # grouped value heads add dq and dk per value head; partial chunks count whole
+    assert lib.kda_bwd_workspace_size(1, 100, 2, 4) == 2 * 4 * unit + 2 * 100 * 4 * 512
+    assert lib.kda_bwd_workspace_size(3, 0, 1, 1) == 0
+    assert lib.kda_bwd_workspace_size(-1, 10, 1, 1) == -1
+    assert lib.kda_bwd_workspace_size(1, 10, 0, 1) == -1
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    for key in BWD_ARGS + ("do", "dq", "dk", "dv", "dg", "dbeta"):
+        a = good_bwd()
+        a[key] = None
+        expect_bwd(lib, a, "KDA_ERR_NULL")
+    for key in ("dq", "dv", "dg", "dbeta", "dh0", "dhT", "h0"):   # fp32 only
+        a = good_bwd()
+        a[key].dtype = binding.KDA_BF16
+        expect_bwd(lib, a, "KDA_ERR_DTYPE")
+    a = good_bwd()
+    a["do"].dtype = binding.KDA_F32
+    expect_bwd(lib, a, "KDA_ERR_DTYPE")
+    for key, shape in (("dq", [2, 100, 4, 128]), ("dv", [2, 100, 2, 128]), ("dg", [2, 99, 4, 128]),
+                       ("dbeta", [2, 100, 2]), ("do", [2, 100, 4, 64]), ("dh0", [2, 4, 128, 64]),
+                       ("dhT", [1, 4, 128, 128]), ("h0", [2, 2, 128, 128])):
+        a = good_bwd()
+        a[key] = T(shape, a[key].dtype)
+        expect_bwd(lib, a, "KDA_ERR_SHAPE")
+    expect_bwd(lib, good_bwd(Hq=3, Hv=4), "KDA_ERR_UNSUPPORTED")
+    a = good_bwd()
+    a["dv"] = T([2, 100, 4, 128], binding.KDA_F32, data=FAKE + 8)
+    expect_bwd(lib, a, "KDA_ERR_LAYOUT")
+    for s in (0.0, -1.0, float("inf")):
+        expect_bwd(lib, good_bwd(), "KDA_ERR_VALUE", scale=s)
+    need = lib.kda_bwd_workspace_size(2, 100, 2, 4)
+    expect_bwd(lib, good_bwd(), "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
+    expect_bwd(lib, good_bwd(), "KDA_ERR_WORKSPACE", ws=FAKE + 16, ws_size=need)
+
+
+def test_bwd_empty_problem_needs_no_launch(lib):
+    for a in (good_bwd(B=0), good_bwd(T_=0, dh0=False)):
+        for key in a:
+            if a[key] is not None and a[key].shape[0] * a[key].shape[1] == 0:
+                a[key].data = None
+        expect_bwd(lib, a, "KDA_OK")

@@ -1,0 +1,145 @@
+"""GPU parity of the backward (kda_bwd, through the C ABI) against the fp64
+chunk-form gradients of the oracle (oracle/grad.py), which are themselves pinned
+to autograd and finite differences on the CPU.
+
+Tolerance: the kernels work in fp32 throughout, so each gradient is a chain of a
+few fp32 products of length at most 192 (128 channels plus 64 tokens); with unit
+roundoff 6e-8 that bounds the relative error of each product near 1.2e-5, and a
+chain of four of them near 5e-5.  The test asks for a relative Frobenius error of
+at most 1e-4 per gradient and per value head.
+
+Each test prints the case it is about to launch before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_35_amd import kda_bwd, kda_bwd_workspace_size, load_library
+from gated_delta_rule_35_amd.inputs import make_inputs
+from oracle import grad as og
+from tests.kda_check import head_subset, to_device
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 128 ** -0.5
+TOL = 1e-4
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    load_library()  # fails loudly if the HIP library is not built
+    yield
+
+
+def _case(B, T, Hq, Hv, seed, h0=True, dhT=True, beta_dtype=torch.float32):
+    x = make_inputs(B, T, Hq, Hv, beta_dtype, h0, seed=seed)
+    gen = torch.Generator("cpu").manual_seed(seed + 1000)
+    x["do"] = torch.randn(B, T, Hv, 128, generator=gen).to(torch.bfloat16)
+    x["dhT"] = torch.randn(B, Hv, 128, 128, generator=gen) if dhT else None
+    return x
+
+
+def _gpu_grads(x, want_dh0=True, workspace=None):
+    d = to_device(x)
+    g = kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, d["do"], initial_state=d["h0"],
+                d_final_state=d["dhT"], d_initial_state=want_dh0, workspace=workspace)
+    torch.cuda.synchronize()
+    return {n: (None if t is None else t.cpu().numpy().astype(np.float64)) for n, t in g.items()}
+
+
+def _f64(t):
+    return None if t is None else t.float().numpy().astype(np.float64)
+
+
+def _oracle(x):
+    # with no initial state the gradient is still taken at the zero state
+    B, Hv = x["v"].shape[0], x["v"].shape[2]
+    h0 = _f64(x["h0"]) if x["h0"] is not None else np.zeros((B, Hv, 128, 128))
+    return og.chunked_grads(_f64(x["q"]), _f64(x["k"]), _f64(x["v"]), _f64(x["g"]), _f64(x["beta"]), SCALE,
+                            h0, _f64(x["do"]), _f64(x["dhT"]), chunk=64)
+
+
+def _rel_per_head(a, b, head_axis):
+    a, b = np.moveaxis(a, head_axis, 0), np.moveaxis(b, head_axis, 0)
+    out = []
+    for h in range(a.shape[0]):
+        den = np.linalg.norm(b[h])
+        out.append(np.linalg.norm(a[h] - b[h]) / den if den > 0 else np.linalg.norm(a[h]))
+    return max(out) if out else 0.0
+
+
+def _compare(got, ref, label):
+    for n in NAMES:
+        if ref[n] is None:
+            assert got[n] is None, n
+            continue
+        axis = 1 if n == "dh0" else 2
+        err = _rel_per_head(got[n], ref[n], axis)
+        _say(f"{label} {n}: rel frob {err:.2e}")
+        assert err <= TOL, (label, n, err)
+
+
+@pytest.mark.parametrize("B,T,Hq,Hv,h0,dhT,beta_dtype", [
+    (2, 150, 2, 4, True, True, torch.float32),      # several chunks, ragged tail, grouped value heads
+    (1, 64, 1, 1, False, False, torch.bfloat16),    # one full chunk, zero state, bf16 beta
+    (1, 1, 2, 2, True, True, torch.float32),        # a single token
+    (3, 200, 4, 4, True, False, torch.float32),     # MHA, three rows
+])
+def test_bwd_matches_oracle(B, T, Hq, Hv, h0, dhT, beta_dtype):
+    x = _case(B, T, Hq, Hv, seed=B * 1000 + T, h0=h0, dhT=dhT, beta_dtype=beta_dtype)
+    _say(f"kda_bwd B={B} T={T} Hq={Hq} Hv={Hv} h0={h0} dhT={dhT} beta={beta_dtype}")
+    got = _gpu_grads(x)
+    _compare(got, _oracle(x), f"B{B} T{T}")
+
+
+def test_bwd_empty_sequence_passes_the_state_gradient_through():
+    x = _case(2, 0, 1, 2, seed=5)
+    _say("kda_bwd T=0")
+    got = _gpu_grads(x)
+    assert np.array_equal(got["dh0"], _f64(x["dhT"]))
+    assert got["dq"].size == 0 and got["dbeta"].size == 0
+
+
+def test_bwd_without_initial_state_gradient_and_with_caller_workspace():
+    x = _case(1, 130, 2, 4, seed=6)
+    need = kda_bwd_workspace_size(1, 130, 2, 4)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _say("kda_bwd B=1 T=130 caller workspace, no dh0")
+    a = _gpu_grads(x, want_dh0=False, workspace=ws)
+    b = _gpu_grads(x, want_dh0=True)
+    assert a["dh0"] is None
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.array_equal(a[n], b[n]), n          # same kernels, same order: bitwise equal
+
+
+def test_bwd_is_reproducible():
+    x = _case(2, 300, 2, 2, seed=7)
+    _say("kda_bwd B=2 T=300 twice")
+    a, b = _gpu_grads(x), _gpu_grads(x)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_bwd_full_size_sampled_heads():
+    # the 2 x 8192 token, 64-head batch the forward is measured on; two heads checked
+    B, T, H = 2, 8192, 64
+    x = _case(B, T, H, H, seed=8, h0=False, dhT=False)
+    _say(f"kda_bwd B={B} T={T} H={H}")
+    got = _gpu_grads(x, want_dh0=False)
+    heads = [0, 37]
+    sub = head_subset(x, heads, H, H)
+    sub["do"] = x["do"][:, :, heads]
+    sub["dhT"] = None
+    ref = _oracle(sub)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        err = _rel_per_head(got[n][:, :, heads], ref[n], 2)
+        _say(f"full size {n}: rel frob {err:.2e}")
+        assert err <= TOL, (n, err)
+        assert np.isfinite(got[n]).all(), n
