@@ -178,6 +178,106 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def bwd_macs_per_chunk(C=64, d=128):
+    """Multiply-adds of the chunk-form backward per (64-token chunk, value head),
+    each product of the equations counted once: the operands (Aqk, Abar, the
+    inverse), the forward walk (Z, v_new, h'), the backward walk (dv_new, dZ, dh)
+    and the chunk-parallel gradients (d(qg), d(kg), d(kh), dAqk, dTb, the inverse's
+    gradient and the four pairwise sums per channel)."""
+    tri = C * (C + 1) // 2
+    prep = 2 * tri * d + C * (C - 1) * (C + 1) // 6
+    fwd = C * d * d + tri * d + d * C * d
+    bwd = (tri * d + C * d * d) + tri * d + 2 * C * d * d
+    grad = 3 * C * d * d + (tri + C * C) * d + 2 * C ** 3 + 4 * tri * d
+    return prep + fwd + bwd + grad
+
+
+def bench_bwd(args):
+    """kda_bwd on --workload (fixed-length rows): HIP events around each call on
+    its stream, with a caller workspace so no allocation is timed."""
+    import torch
+    from gated_delta_rule_35_amd import kda_bwd, kda_bwd_workspace_size
+    from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
+    if args.gpus != 1:
+        print("bench.py measures one GPU only", file=sys.stderr, flush=True)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    if w.varlen_total:
+        raise SystemExit("the backward takes fixed-length rows only")
+    log(f"generating inputs for {args.workload}")
+    x, _ = workload_inputs(w)
+    B, T = w.B, w.T
+    gen = torch.Generator("cpu").manual_seed(1)
+    do = torch.randn(B, T, w.Hv, 128, generator=gen).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    do_d = do.to(dev)
+    ws = torch.empty(kda_bwd_workspace_size(B, T, w.Hq, w.Hv), dtype=torch.uint8, device=dev)
+    grads = None
+
+    def one():
+        nonlocal grads
+        grads = kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, do_d, initial_state=d["h0"],
+                        grads=grads, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        one()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    t = sum(ms) / len(ms) / 1e3
+    n_tok = B * T
+    units = B * ((T + 63) // 64) * w.Hv
+    flops = 2 * bwd_macs_per_chunk() * units
+    tf = flops / t / 1e12
+    log(f"backward {args.workload}: call avg {t * 1e3:.3f} ms (min {min(ms):.3f}), {n_tok / t / 1e6:.2f} M tok/s, "
+        f"{tf:.1f} TFLOP/s algorithmic")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import grad as og
+        heads = list(range(min(2, w.Hv)))
+        group = w.Hv // w.Hq
+        f64 = lambda a: a.float().numpy().astype("float64")  # noqa: E731
+        sub = [f64(x["q"][:, :, [h // group for h in heads]]), f64(x["k"][:, :, [h // group for h in heads]]),
+               f64(x["v"][:, :, heads]), f64(x["g"][:, :, heads]), f64(x["beta"][:, :, heads])]
+        h0 = f64(x["h0"][:, heads]) if x["h0"] is not None else None
+        dos = f64(do[:, :, heads])
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            og.chunked_grads(*sub, w.scale, h0, dos, None, chunk=64)
+            reps += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - c0
+        tok_s = n_tok * len(heads) / w.Hv * reps / el
+        cpu = {"value": round(tok_s, 1), "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+               "sample": f"fp64 chunk-form gradients (numpy) on value heads {heads} of the full batch, "
+                         f"{reps} run(s) in {el:.1f} s, scaled to all {w.Hv} heads"}
+        log(f"cpu oracle: {tok_s:.1f} tok/s")
+    rec = {"metric": "KDA backward tokens/s (gradients of q, k, v, g, beta)", "value": round(n_tok / t, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": args.workload, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128},
+           "call_ms_avg": round(t * 1e3, 4), "algorithmic_flops_per_call": flops,
+           "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                        "scope": "the whole kda_bwd call (five kernels): algorithmic fp32 flops over its duration"},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def oracle_cpu_baseline(x, cu, w, N, n_tok, scale, seconds, heads):
     """The fp64 oracle (token recurrence) on value heads 0 .. heads-1 of the
     workload, run repeatedly for at least `seconds`; tokens/s scaled to all heads."""
@@ -310,6 +410,8 @@ def main():
                          "(0: the library's suggestion) against kda_fwd")
     ap.add_argument("--cp-first", type=int, default=0, metavar="L0",
                     help="with --cp L: chunks of the first segment (default L)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="instead of the forward, time the backward kda_bwd on --workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the benchmark, run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -324,6 +426,9 @@ def main():
         return
     if args.decode:
         bench_decode(args)
+        return
+    if args.bwd:
+        bench_bwd(args)
         return
     if args.cp >= 0:
         bench_cp(args)
