@@ -24,7 +24,7 @@
 //
 // Five kernels, all fp32 on the vector ALUs with LDS tiles:
 //   prep    one work-group per (chunk, value head): G, Aqk, Abar and T
-//   states  one per (sequence, value head, 16 value columns): walks the chunks
+//   states  one per (sequence, value head, 32 value columns): walks the chunks
 //           forward and stores each chunk's entering state h
 //   dstate  the same grid, walking the chunks backward: stores each chunk's dh'
 //           and writes the initial state's gradient
@@ -42,9 +42,13 @@ constexpr int BW_C = 64;      // chunk length
 constexpr int BW_D = 128;     // head dimension
 constexpr int BW_LD = 129;    // row stride of [64][128] LDS tiles: odd, so a column read across rows spreads over banks
 constexpr int BW_MD = 65;     // row stride of [64][64] LDS tiles
-constexpr int BW_SL = 16;     // value columns per scan work-group
-constexpr int BW_SD = 17;     // row stride of [*][16] LDS tiles
+constexpr int BW_SL = 32;     // value columns per scan work-group
+constexpr int BW_SD = 33;     // row stride of [*][32] LDS tiles
 constexpr int BW_NSL = BW_D / BW_SL;
+constexpr int BW_ST = 512;    // threads of a scan work-group: row c = t % 128, columns 8 (t / 128) .. + 7
+constexpr int GSL = 16;       // value columns per step of the grad kernel's slice loop
+constexpr int GSD = 17;       // row stride of [*][16] LDS tiles
+constexpr int GNSL = BW_D / GSL;
 constexpr int64_t BW_STATE = (int64_t)BW_D * BW_D;
 
 __device__ __forceinline__ float ld_beta(const BwdParams& p, int64_t idx) {
@@ -146,8 +150,10 @@ __global__ void __launch_bounds__(256) kda_bwd_prep_kernel(const BwdParams p) {
 }
 
 // Loads the chunk's decayed key operands and Tb into LDS (shared by states and dstate).
+// Any of sKG, sKH, sQG, sTB may be null (not loaded).
 __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx& x, const float* pr, float* sKG,
                                              float* sKH, float* sQG, float* sTB, int tid, int nthreads) {
+    if (sKG || sKH || sQG)
     for (int e = tid; e < BW_C * BW_D; e += nthreads) {
         const int i = e >> 7, c = e & 127;
         float kv = 0.f, qv = 0.f;
@@ -157,10 +163,11 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
         }
         const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
         const float eG = fexp(G);
-        sKG[i * BW_LD + c] = kv * eG;
-        sKH[i * BW_LD + c] = kv * fexp(Gl - G);
+        if (sKG) sKG[i * BW_LD + c] = kv * eG;
+        if (sKH) sKH[i * BW_LD + c] = kv * fexp(Gl - G);
         if (sQG) sQG[i * BW_LD + c] = p.scale * qv * eG;
     }
+    if (sTB)
     for (int e = tid; e < BW_C * BW_C; e += nthreads) {
         const int i = e >> 6, j = e & 63;
         const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
@@ -169,9 +176,9 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
 }
 
 // ---------------------------------------------------------------- states
-// Work-group (b, hv, slice): thread t holds state rows c = t % 128, columns
-// 8 (t / 128) .. + 7 of the slice.
-__global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) {
+// Work-group (b, hv, slice of 32 value columns), 512 threads: thread t holds
+// state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.
+__global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p) {
     __shared__ float sKG[BW_C * BW_LD], sKH[BW_C * BW_LD], sTB[BW_C * BW_MD];
     __shared__ float sS[BW_D * BW_SD], sV[BW_C * BW_SD], sZ[BW_C * BW_SD], sVN[BW_C * BW_SD];
     const int tid = threadIdx.x;
@@ -183,7 +190,7 @@ __global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) 
     float S[8];
     for (int e = 0; e < 8; ++e)
         S[e] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
-    const int zn = tid & 15, zi = tid >> 4;   // Z / v_new: column zn, rows zi + 16 r
+    const int zn = tid & 31, zi = tid >> 5;   // Z / v_new: column zn, rows zi + 16 r
     for (int ci = 0; ci < p.nc; ++ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
         float* hs = p.hs + x.ch * BW_STATE + c * BW_D + n0 + nb;
@@ -193,9 +200,9 @@ __global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) 
         }
         if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
         const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, 256);
-        for (int e = tid; e < BW_C * BW_SL; e += 256) {
-            const int i = e >> 4, n = e & 15;
+        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, BW_ST);
+        for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
+            const int i = e >> 5, n = e & 31;
             sV[i * BW_SD + n] = i < x.len ? bf2f(p.v[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
         }
         const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
@@ -203,6 +210,7 @@ __global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) 
         for (int r = 0; r < 4; ++r) {
             const int i = zi + 16 * r;
             float z = sV[i * BW_SD + zn];
+#pragma unroll 8
             for (int cc = 0; cc < BW_D; ++cc) z -= sKG[i * BW_LD + cc] * sS[cc * BW_SD + zn];
             sZ[i * BW_SD + zn] = z;
         }
@@ -216,6 +224,7 @@ __global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) 
         __syncthreads();
         for (int e = 0; e < 8; ++e) {
             float s = gam * S[e];
+#pragma unroll 8
             for (int i = 0; i < BW_C; ++i) s += sKH[i * BW_LD + c] * sVN[i * BW_SD + nb + e];
             S[e] = s;
         }
@@ -224,8 +233,11 @@ __global__ void __launch_bounds__(256) kda_bwd_states_kernel(const BwdParams p) 
 }
 
 // ---------------------------------------------------------------- dstate
-__global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) {
-    __shared__ float sQG[BW_C * BW_LD], sKG[BW_C * BW_LD], sKH[BW_C * BW_LD];
+// Same grid and thread layout as states.  kh is needed only for dv_new and qg
+// only for the state update, so they share one LDS tile: qg is loaded once
+// dv_new is done.
+__global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p) {
+    __shared__ float sKG[BW_C * BW_LD], sKQ[BW_C * BW_LD];   // kg; kh, then qg
     __shared__ float sAQ[BW_C * BW_MD], sTB[BW_C * BW_MD];
     __shared__ float sDH[BW_D * BW_SD], sDO[BW_C * BW_SD], sDVN[BW_C * BW_SD], sDZ[BW_C * BW_SD];
     const int tid = threadIdx.x;
@@ -237,7 +249,7 @@ __global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) 
     float dh[8];
     for (int e = 0; e < 8; ++e)
         dh[e] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
-    const int zn = tid & 15, zi = tid >> 4;
+    const int zn = tid & 31, zi = tid >> 5;
     for (int ci = p.nc - 1; ci >= 0; --ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
         float* ds = p.dhs + x.ch * BW_STATE + c * BW_D + n0 + nb;
@@ -246,10 +258,10 @@ __global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) 
             sDH[c * BW_SD + nb + e] = dh[e];
         }
         const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKH, sQG, sTB, tid, 256);
-        for (int e = tid; e < BW_C * BW_C; e += 256) sAQ[(e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
-        for (int e = tid; e < BW_C * BW_SL; e += 256) {
-            const int i = e >> 4, n = e & 15;
+        load_key_ops(p, x, pr, sKG, sKQ, nullptr, sTB, tid, BW_ST);
+        for (int e = tid; e < BW_C * BW_C; e += BW_ST) sAQ[(e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
+        for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
+            const int i = e >> 5, n = e & 31;
             sDO[i * BW_SD + n] = i < x.len ? bf2f(p.dO[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
         }
         const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
@@ -258,10 +270,11 @@ __global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) 
             const int i = zi + 16 * r;
             float u = 0.f;
             for (int m = i; m < BW_C; ++m) u += sAQ[m * BW_MD + i] * sDO[m * BW_SD + zn];
-            for (int cc = 0; cc < BW_D; ++cc) u += sKH[i * BW_LD + cc] * sDH[cc * BW_SD + zn];
+            for (int cc = 0; cc < BW_D; ++cc) u += sKQ[i * BW_LD + cc] * sDH[cc * BW_SD + zn];
             sDVN[i * BW_SD + zn] = u;
         }
         __syncthreads();
+        load_key_ops(p, x, pr, nullptr, nullptr, sKQ, nullptr, tid, BW_ST);   // kh is done with: qg replaces it
         for (int r = 0; r < 4; ++r) {   // dZ = Tb^T dv_new
             const int i = zi + 16 * r;
             float z = 0.f;
@@ -272,7 +285,7 @@ __global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) 
         for (int e = 0; e < 8; ++e) {   // dh = gam dh' + qg^T do - kg^T dZ
             float s = gam * dh[e];
             for (int i = 0; i < BW_C; ++i)
-                s += sQG[i * BW_LD + c] * sDO[i * BW_SD + nb + e] - sKG[i * BW_LD + c] * sDZ[i * BW_SD + nb + e];
+                s += sKQ[i * BW_LD + c] * sDO[i * BW_SD + nb + e] - sKG[i * BW_LD + c] * sDZ[i * BW_SD + nb + e];
             dh[e] = s;
         }
         __syncthreads();
@@ -284,9 +297,9 @@ __global__ void __launch_bounds__(256) kda_bwd_dstate_kernel(const BwdParams p) 
 // ---------------------------------------------------------------- grad
 // LDS of the grad kernel, in floats.  Phase A (the loop over value slices):
 constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * BW_LD, GA_AQ = GA_KH + BW_C * BW_LD, GA_TB = GA_AQ + BW_C * BW_MD;
-constexpr int GA_H = GA_TB + BW_C * BW_MD, GA_DH = GA_H + BW_D * BW_SD, GA_DO = GA_DH + BW_D * BW_SD;
-constexpr int GA_V = GA_DO + BW_C * BW_SD, GA_Z = GA_V + BW_C * BW_SD, GA_VN = GA_Z + BW_C * BW_SD;
-constexpr int GA_DVN = GA_VN + BW_C * BW_SD, GA_DZ = GA_DVN + BW_C * BW_SD, GA_END = GA_DZ + BW_C * BW_SD;
+constexpr int GA_H = GA_TB + BW_C * BW_MD, GA_DH = GA_H + BW_D * GSD, GA_DO = GA_DH + BW_D * GSD;
+constexpr int GA_V = GA_DO + BW_C * GSD, GA_Z = GA_V + BW_C * GSD, GA_VN = GA_Z + BW_C * GSD;
+constexpr int GA_DVN = GA_VN + BW_C * GSD, GA_DZ = GA_DVN + BW_C * GSD, GA_END = GA_DZ + BW_C * GSD;
 // Phase B (the inverse's gradient), then phase C (the pairwise terms):
 constexpr int GC_Q = 0, GC_K = GC_Q + BW_C * BW_LD, GC_G = GC_K + BW_C * BW_LD, GC_DAQ = GC_G + BW_C * BW_LD;
 constexpr int GC_DAB = GC_DAQ + BW_C * BW_MD, GC_END = GC_DAB + BW_C * BW_MD;
@@ -314,56 +327,56 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512);
     for (int e = tid; e < BW_C * BW_C; e += 512) F[GA_AQ + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
     const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
-    for (int sl = 0; sl < BW_NSL; ++sl) {
-        const int n0 = sl * BW_SL;
-        for (int e = tid; e < BW_D * BW_SL; e += 512) {
+    for (int sl = 0; sl < GNSL; ++sl) {
+        const int n0 = sl * GSL;
+        for (int e = tid; e < BW_D * GSL; e += 512) {
             const int cc = e >> 4, n = e & 15;
-            F[GA_H + cc * BW_SD + n] = hs[cc * BW_D + n0 + n];
-            F[GA_DH + cc * BW_SD + n] = ds[cc * BW_D + n0 + n];
+            F[GA_H + cc * GSD + n] = hs[cc * BW_D + n0 + n];
+            F[GA_DH + cc * GSD + n] = ds[cc * BW_D + n0 + n];
         }
-        for (int e = tid; e < BW_C * BW_SL; e += 512) {
+        for (int e = tid; e < BW_C * GSL; e += 512) {
             const int i = e >> 4, n = e & 15;
             const bool in = i < x.len;
             const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
-            F[GA_DO + i * BW_SD + n] = in ? bf2f(p.dO[o]) : 0.f;
-            F[GA_V + i * BW_SD + n] = in ? bf2f(p.v[o]) : 0.f;
+            F[GA_DO + i * GSD + n] = in ? bf2f(p.dO[o]) : 0.f;
+            F[GA_V + i * GSD + n] = in ? bf2f(p.v[o]) : 0.f;
         }
         __syncthreads();
         for (int r = 0; r < 2; ++r) {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
             const int i = zi + 32 * r;
-            float z = F[GA_V + i * BW_SD + zn], u = 0.f;
+            float z = F[GA_V + i * GSD + zn], u = 0.f;
             for (int cc = 0; cc < BW_D; ++cc) {
-                z -= F[GA_KG + i * BW_LD + cc] * F[GA_H + cc * BW_SD + zn];
-                u += F[GA_KH + i * BW_LD + cc] * F[GA_DH + cc * BW_SD + zn];
+                z -= F[GA_KG + i * BW_LD + cc] * F[GA_H + cc * GSD + zn];
+                u += F[GA_KH + i * BW_LD + cc] * F[GA_DH + cc * GSD + zn];
             }
-            for (int m = i; m < BW_C; ++m) u += F[GA_AQ + m * BW_MD + i] * F[GA_DO + m * BW_SD + zn];
-            F[GA_Z + i * BW_SD + zn] = z;
-            F[GA_DVN + i * BW_SD + zn] = u;
+            for (int m = i; m < BW_C; ++m) u += F[GA_AQ + m * BW_MD + i] * F[GA_DO + m * GSD + zn];
+            F[GA_Z + i * GSD + zn] = z;
+            F[GA_DVN + i * GSD + zn] = u;
         }
         __syncthreads();
         for (int r = 0; r < 2; ++r) {   // v_new = Tb Z;  dZ = Tb^T dv_new = dv
             const int i = zi + 32 * r;
             float vn = 0.f, dz = 0.f;
-            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + j * BW_SD + zn];
-            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + m * BW_SD + zn];
-            F[GA_VN + i * BW_SD + zn] = vn;
-            F[GA_DZ + i * BW_SD + zn] = dz;
+            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + j * GSD + zn];
+            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + m * GSD + zn];
+            F[GA_VN + i * GSD + zn] = vn;
+            F[GA_DZ + i * GSD + zn] = dz;
             if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + zn] = dz;
         }
         __syncthreads();
-        for (int n = 0; n < BW_SL; ++n) {
-            const float h = F[GA_H + c * BW_SD + n], dhv = F[GA_DH + c * BW_SD + n];
+        for (int n = 0; n < GSL; ++n) {
+            const float h = F[GA_H + c * GSD + n], dhv = F[GA_DH + c * GSD + n];
             for (int r = 0; r < 16; ++r) {
                 const int i = rg + 4 * r;
-                aQ[r] += F[GA_DO + i * BW_SD + n] * h;
-                aKG[r] -= F[GA_DZ + i * BW_SD + n] * h;
-                aKH[r] += F[GA_VN + i * BW_SD + n] * dhv;
+                aQ[r] += F[GA_DO + i * GSD + n] * h;
+                aKG[r] -= F[GA_DZ + i * GSD + n] * h;
+                aKH[r] += F[GA_VN + i * GSD + n] * dhv;
             }
             if (rg == 0) dgam += dhv * h;
             for (int s = 0; s < 8; ++s) {
                 const int j = aj + 8 * s;
-                aAQ[s] += F[GA_DO + ai * BW_SD + n] * F[GA_VN + j * BW_SD + n];
-                aTB[s] += F[GA_DVN + ai * BW_SD + n] * F[GA_Z + j * BW_SD + n];
+                aAQ[s] += F[GA_DO + ai * GSD + n] * F[GA_VN + j * GSD + n];
+                aTB[s] += F[GA_DVN + ai * GSD + n] * F[GA_Z + j * GSD + n];
             }
         }
         __syncthreads();
@@ -504,9 +517,9 @@ hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream) {
     const int64_t scans = (int64_t)p.B * p.Hv * BW_NSL;
     if (chunks > 0) {
         hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, stream, p);
-        hipLaunchKernelGGL(kda_bwd_states_kernel, dim3((unsigned)scans), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(kda_bwd_states_kernel, dim3((unsigned)scans), dim3(BW_ST), 0, stream, p);
     }
-    if (scans > 0) hipLaunchKernelGGL(kda_bwd_dstate_kernel, dim3((unsigned)scans), dim3(256), 0, stream, p);
+    if (scans > 0) hipLaunchKernelGGL(kda_bwd_dstate_kernel, dim3((unsigned)scans), dim3(BW_ST), 0, stream, p);
     if (chunks > 0) {
         hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)chunks), dim3(512), 0, stream, p);
         if (p.Hv != p.Hq) {
