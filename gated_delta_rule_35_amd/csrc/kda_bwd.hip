@@ -152,7 +152,8 @@ __global__ void __launch_bounds__(256) kda_bwd_prep_kernel(const BwdParams p) {
 // Loads the chunk's decayed key operands and Tb into LDS (shared by states and dstate).
 // Any of sKG, sKH, sQG, sTB may be null (not loaded).
 __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx& x, const float* pr, float* sKG,
-                                             float* sKH, float* sQG, float* sTB, int tid, int nthreads) {
+                                             float* sKH, float* sQG, float* sTB, int tid, int nthreads,
+                                             int ld = BW_LD) {
     if (sKG || sKH || sQG)
     for (int e = tid; e < BW_C * BW_D; e += nthreads) {
         const int i = e >> 7, c = e & 127;
@@ -163,9 +164,9 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
         }
         const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
         const float eG = fexp(G);
-        if (sKG) sKG[i * BW_LD + c] = kv * eG;
-        if (sKH) sKH[i * BW_LD + c] = kv * fexp(Gl - G);
-        if (sQG) sQG[i * BW_LD + c] = p.scale * qv * eG;
+        if (sKG) sKG[i * ld + c] = kv * eG;
+        if (sKH) sKH[i * ld + c] = kv * fexp(Gl - G);
+        if (sQG) sQG[i * ld + c] = p.scale * qv * eG;
     }
     if (sTB)
     for (int e = tid; e < BW_C * BW_C; e += nthreads) {
@@ -295,11 +296,19 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
 }
 
 // ---------------------------------------------------------------- grad
+// One 512-thread work-group per (chunk, value head).  The value columns are
+// taken 16 at a time; the tiles of one such slice that are read along the
+// token index (do, v, Z, v_new, dv_new, dZ) are stored transposed, [16][68], so
+// that a thread reads four consecutive tokens with one 16-byte LDS load.
+constexpr int GLD = 132;   // row stride of the kg / kh tiles: a multiple of 4 for 16-byte reads
+constexpr int GTS = 68;    // row stride of the transposed slice tiles
 // LDS of the grad kernel, in floats.  Phase A (the loop over value slices):
-constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * BW_LD, GA_AQ = GA_KH + BW_C * BW_LD, GA_TB = GA_AQ + BW_C * BW_MD;
+constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * GLD, GA_AQ = GA_KH + BW_C * GLD, GA_TB = GA_AQ + BW_C * BW_MD;
 constexpr int GA_H = GA_TB + BW_C * BW_MD, GA_DH = GA_H + BW_D * GSD, GA_DO = GA_DH + BW_D * GSD;
-constexpr int GA_V = GA_DO + BW_C * GSD, GA_Z = GA_V + BW_C * GSD, GA_VN = GA_Z + BW_C * GSD;
-constexpr int GA_DVN = GA_VN + BW_C * GSD, GA_DZ = GA_DVN + BW_C * GSD, GA_END = GA_DZ + BW_C * GSD;
+constexpr int GA_V = GA_DO + GSL * GTS, GA_Z = GA_V + GSL * GTS, GA_VN = GA_Z + GSL * GTS;
+constexpr int GA_DVN = GA_VN + GSL * GTS, GA_DZ = GA_DVN + GSL * GTS, GA_END = GA_DZ + GSL * GTS;
+static_assert(GA_H % 4 == 0 && GA_DO % 4 == 0 && GA_V % 4 == 0 && GA_Z % 4 == 0 && GA_VN % 4 == 0 &&
+              GA_DVN % 4 == 0 && GA_DZ % 4 == 0 && GA_KH % 4 == 0, "16-byte aligned tiles");
 // Phase B (the inverse's gradient), then phase C (the pairwise terms):
 constexpr int GC_Q = 0, GC_K = GC_Q + BW_C * BW_LD, GC_G = GC_K + BW_C * BW_LD, GC_DAQ = GC_G + BW_C * BW_LD;
 constexpr int GC_DAB = GC_DAQ + BW_C * BW_MD, GC_END = GC_DAB + BW_C * BW_MD;
@@ -309,24 +318,27 @@ static_assert(GB_AB + BW_C * BW_MD <= GC_DAQ, "phase B temporaries must not over
 constexpr int G_LDS = GA_END > GB_END ? GA_END : GB_END;
 static_assert(G_LDS * 4 <= 160 * 1024, "grad kernel LDS");
 
+__device__ __forceinline__ f32x4 lds4(const float* a) { return *reinterpret_cast<const f32x4*>(a); }
+
 __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
-    __shared__ float F[G_LDS];
+    __shared__ __attribute__((aligned(16))) float F[G_LDS];
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
     const float* pr = p.prep + x.ch * BWP_FLOATS;
     const float* hs = p.hs + x.ch * BW_STATE;
     const float* ds = p.dhs + x.ch * BW_STATE;
-    // element (i, c) accumulators: c = tid % 128, rows i = rg + 4 r
-    const int c = tid & 127, rg = tid >> 7;
-    // 64 x 64 accumulators: row ai = tid / 8, columns aj = tid % 8 + 8 s
-    const int ai = tid >> 3, aj = tid & 7;
+    // element (i, c) accumulators: c = tid % 128, rows i = 16 rg + r
+    const int c = tid & 127, rg = tid >> 7, i0 = 16 * rg;
+    // 64 x 64 accumulators: row ai = tid / 8, columns 8 aj .. + 7
+    const int ai = tid >> 3, aj = (tid & 7) * 8;
     float aQ[16], aKG[16], aKH[16], aAQ[8], aTB[8], dgam = 0.f;
     for (int r = 0; r < 16; ++r) aQ[r] = aKG[r] = aKH[r] = 0.f;
     for (int s = 0; s < 8; ++s) aAQ[s] = aTB[s] = 0.f;
 
-    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512);
+    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512, GLD);
     for (int e = tid; e < BW_C * BW_C; e += 512) F[GA_AQ + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
     const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
+#pragma unroll 1
     for (int sl = 0; sl < GNSL; ++sl) {
         const int n0 = sl * GSL;
         for (int e = tid; e < BW_D * GSL; e += 512) {
@@ -338,45 +350,64 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
             const int i = e >> 4, n = e & 15;
             const bool in = i < x.len;
             const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
-            F[GA_DO + i * GSD + n] = in ? bf2f(p.dO[o]) : 0.f;
-            F[GA_V + i * GSD + n] = in ? bf2f(p.v[o]) : 0.f;
+            F[GA_DO + n * GTS + i] = in ? bf2f(p.dO[o]) : 0.f;
+            F[GA_V + n * GTS + i] = in ? bf2f(p.v[o]) : 0.f;
         }
         __syncthreads();
-        for (int r = 0; r < 2; ++r) {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
-            const int i = zi + 32 * r;
-            float z = F[GA_V + i * GSD + zn], u = 0.f;
-            for (int cc = 0; cc < BW_D; ++cc) {
-                z -= F[GA_KG + i * BW_LD + cc] * F[GA_H + cc * GSD + zn];
-                u += F[GA_KH + i * BW_LD + cc] * F[GA_DH + cc * GSD + zn];
+        {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
+            float z0 = F[GA_V + zn * GTS + zi], z1 = F[GA_V + zn * GTS + zi + 32], u0 = 0.f, u1 = 0.f;
+#pragma unroll 2
+            for (int cc = 0; cc < BW_D; cc += 4) {
+                const f32x4 g0 = lds4(F + GA_KG + zi * GLD + cc), g1 = lds4(F + GA_KG + (zi + 32) * GLD + cc);
+                const f32x4 k0 = lds4(F + GA_KH + zi * GLD + cc), k1 = lds4(F + GA_KH + (zi + 32) * GLD + cc);
+                for (int e = 0; e < 4; ++e) {
+                    const float h = F[GA_H + (cc + e) * GSD + zn], d = F[GA_DH + (cc + e) * GSD + zn];
+                    z0 -= g0[e] * h;
+                    z1 -= g1[e] * h;
+                    u0 += k0[e] * d;
+                    u1 += k1[e] * d;
+                }
             }
-            for (int m = i; m < BW_C; ++m) u += F[GA_AQ + m * BW_MD + i] * F[GA_DO + m * GSD + zn];
-            F[GA_Z + i * GSD + zn] = z;
-            F[GA_DVN + i * GSD + zn] = u;
+            for (int m = zi; m < BW_C; ++m) u0 += F[GA_AQ + m * BW_MD + zi] * F[GA_DO + zn * GTS + m];
+            for (int m = zi + 32; m < BW_C; ++m) u1 += F[GA_AQ + m * BW_MD + zi + 32] * F[GA_DO + zn * GTS + m];
+            F[GA_Z + zn * GTS + zi] = z0;
+            F[GA_Z + zn * GTS + zi + 32] = z1;
+            F[GA_DVN + zn * GTS + zi] = u0;
+            F[GA_DVN + zn * GTS + zi + 32] = u1;
         }
         __syncthreads();
         for (int r = 0; r < 2; ++r) {   // v_new = Tb Z;  dZ = Tb^T dv_new = dv
             const int i = zi + 32 * r;
             float vn = 0.f, dz = 0.f;
-            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + j * GSD + zn];
-            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + m * GSD + zn];
-            F[GA_VN + i * GSD + zn] = vn;
-            F[GA_DZ + i * GSD + zn] = dz;
+            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + zn * GTS + j];
+            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + zn * GTS + m];
+            F[GA_VN + zn * GTS + i] = vn;
+            F[GA_DZ + zn * GTS + i] = dz;
             if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + zn] = dz;
         }
         __syncthreads();
+#pragma unroll 1
         for (int n = 0; n < GSL; ++n) {
             const float h = F[GA_H + c * GSD + n], dhv = F[GA_DH + c * GSD + n];
-            for (int r = 0; r < 16; ++r) {
-                const int i = rg + 4 * r;
-                aQ[r] += F[GA_DO + i * GSD + n] * h;
-                aKG[r] -= F[GA_DZ + i * GSD + n] * h;
-                aKH[r] += F[GA_VN + i * GSD + n] * dhv;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o4 = lds4(F + GA_DO + n * GTS + i0 + 4 * q4);
+                const f32x4 z4 = lds4(F + GA_DZ + n * GTS + i0 + 4 * q4);
+                const f32x4 v4 = lds4(F + GA_VN + n * GTS + i0 + 4 * q4);
+                for (int e = 0; e < 4; ++e) {
+                    aQ[4 * q4 + e] += o4[e] * h;
+                    aKG[4 * q4 + e] -= z4[e] * h;
+                    aKH[4 * q4 + e] += v4[e] * dhv;
+                }
             }
             if (rg == 0) dgam += dhv * h;
-            for (int s = 0; s < 8; ++s) {
-                const int j = aj + 8 * s;
-                aAQ[s] += F[GA_DO + ai * GSD + n] * F[GA_VN + j * GSD + n];
-                aTB[s] += F[GA_DVN + ai * GSD + n] * F[GA_Z + j * GSD + n];
+            const float oa = F[GA_DO + n * GTS + ai], va = F[GA_DVN + n * GTS + ai];
+            const f32x4 vA = lds4(F + GA_VN + n * GTS + aj), vB = lds4(F + GA_VN + n * GTS + aj + 4);
+            const f32x4 zA = lds4(F + GA_Z + n * GTS + aj), zB = lds4(F + GA_Z + n * GTS + aj + 4);
+            for (int e = 0; e < 4; ++e) {
+                aAQ[e] += oa * vA[e];
+                aAQ[4 + e] += oa * vB[e];
+                aTB[e] += va * zA[e];
+                aTB[4 + e] += va * zB[e];
             }
         }
         __syncthreads();
@@ -384,7 +415,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
 
     // Phase B: dA = lower_strict(-T^T (dTb diag beta) T^T), dbeta, dAbar = diag(beta) dA.
     for (int s = 0; s < 8; ++s) {
-        const int j = aj + 8 * s;
+        const int j = aj + s;
         F[GB_DTB + ai * BW_MD + j] = aTB[s];
         F[GC_DAQ + ai * BW_MD + j] = j <= ai ? aAQ[s] : 0.f;
     }
@@ -396,19 +427,19 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
         F[GB_BETA + tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
     __syncthreads();
     for (int s = 0; s < 8; ++s) {
-        const int j = aj + 8 * s;
+        const int j = aj + s;
         F[GB_M1 + ai * BW_MD + j] = F[GB_DTB + ai * BW_MD + j] * F[GB_BETA + j];
     }
     __syncthreads();
     for (int s = 0; s < 8; ++s) {   // M2 = T^T M1
-        const int j = aj + 8 * s;
+        const int j = aj + s;
         float a = 0.f;
         for (int m = 0; m < BW_C; ++m) a += F[GB_T + m * BW_MD + ai] * F[GB_M1 + m * BW_MD + j];
         F[GB_M2 + ai * BW_MD + j] = a;
     }
     __syncthreads();
     for (int s = 0; s < 8; ++s) {   // dA = -M2 T^T, strictly lower
-        const int j = aj + 8 * s;
+        const int j = aj + s;
         float a = 0.f;
         if (j < ai)
             for (int m = 0; m < BW_C; ++m) a -= F[GB_M2 + ai * BW_MD + m] * F[GB_T + j * BW_MD + m];
@@ -423,7 +454,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
         if (j < x.len) p.dbeta[((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv] = db;
     }
     for (int s = 0; s < 8; ++s) {
-        const int j = aj + 8 * s;
+        const int j = aj + s;
         F[GC_DAB + ai * BW_MD + j] = F[GB_BETA + ai] * F[GB_DA + ai * BW_MD + j];
     }
     __syncthreads();
@@ -444,7 +475,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     const float Gl = F[GC_G + (BW_C - 1) * BW_LD + c];
     float oq[16], ok[16], oG[16], oP[16];
     for (int r = 0; r < 16; ++r) {
-        const int i = rg + 4 * r;
+        const int i = i0 + r;
         const float Gi = F[GC_G + i * BW_LD + c], qi = F[GC_Q + i * BW_LD + c], ki = F[GC_K + i * BW_LD + c];
         float Rq = 0.f, Rk = 0.f, Cq = 0.f, Ck = 0.f;
         for (int j = 0; j <= i; ++j) {
@@ -465,7 +496,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
                 p.scale * aQ[r] * qi * eG - oP[r];
     }
     for (int r = 0; r < 16; ++r) {
-        const int i = rg + 4 * r;
+        const int i = i0 + r;
         if (i < x.len) {
             const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + c;
             p.dqv[o] = oq[r];
@@ -474,7 +505,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     }
     __syncthreads();   // q and k are no longer read: reuse them for dG and the kh terms
     for (int r = 0; r < 16; ++r) {
-        const int i = rg + 4 * r;
+        const int i = i0 + r;
         F[GC_Q + i * BW_LD + c] = oG[r];
         F[GC_K + i * BW_LD + c] = oP[r];
     }
