@@ -42,14 +42,17 @@ constexpr int BW_C = 64;      // chunk length
 constexpr int BW_D = 128;     // head dimension
 constexpr int BW_LD = 129;    // row stride of [64][128] LDS tiles: odd, so a column read across rows spreads over banks
 constexpr int BW_MD = 65;     // row stride of [64][64] LDS tiles
+constexpr int GLD = 132;      // row stride of [64][128] tiles read along rows with 16-byte loads
 constexpr int BW_SL = 32;     // value columns per scan work-group
-constexpr int BW_SD = 33;     // row stride of [*][32] LDS tiles
+constexpr int BW_SD = 36;     // row stride of [*][32] LDS tiles: a multiple of 4 for 16-byte reads
 constexpr int BW_NSL = BW_D / BW_SL;
 constexpr int BW_ST = 512;    // threads of a scan work-group: row c = t % 128, columns 8 (t / 128) .. + 7
 constexpr int GSL = 16;       // value columns per step of the grad kernel's slice loop
 constexpr int GSD = 17;       // row stride of [*][16] LDS tiles
 constexpr int GNSL = BW_D / GSL;
 constexpr int64_t BW_STATE = (int64_t)BW_D * BW_D;
+
+__device__ __forceinline__ f32x4 lds4(const float* a) { return *reinterpret_cast<const f32x4*>(a); }
 
 __device__ __forceinline__ float ld_beta(const BwdParams& p, int64_t idx) {
     return p.beta_f32 ? static_cast<const float*>(p.beta)[idx] : bf2f(static_cast<const uint16_t*>(p.beta)[idx]);
@@ -83,12 +86,16 @@ __device__ __forceinline__ int64_t vh_off(const BwdParams& p, int b, int64_t t, 
 }
 
 // ---------------------------------------------------------------- prep
-__global__ void __launch_bounds__(256) kda_bwd_prep_kernel(const BwdParams p) {
-    __shared__ float sQ[BW_C * BW_LD], sK[BW_C * BW_LD], sG[BW_C * BW_LD];
+constexpr int BW_PT = 512;   // threads of the prep work-group
+
+__global__ void __launch_bounds__(BW_PT) kda_bwd_prep_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) float sQ[BW_C * GLD];
+    __shared__ __attribute__((aligned(16))) float sK[BW_C * GLD];
+    __shared__ __attribute__((aligned(16))) float sG[BW_C * GLD];
     __shared__ float sA[BW_C * BW_MD], sT[BW_C * BW_MD], sB[BW_C];
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
-    for (int e = tid; e < BW_C * BW_D; e += 256) {
+    for (int e = tid; e < BW_C * BW_D; e += BW_PT) {
         const int i = e >> 7, c = e & 127;
         float qv = 0.f, kv = 0.f, gv = 0.f;   // rows past the sequence's end: q = k = 0, g = 0
         if (i < x.len) {
@@ -97,31 +104,36 @@ __global__ void __launch_bounds__(256) kda_bwd_prep_kernel(const BwdParams p) {
             kv = bf2f(p.k[qk_off(p, x.b, t, x.hq) + c]);
             gv = p.g[vh_off(p, x.b, t, x.hv) + c];
         }
-        sQ[i * BW_LD + c] = qv;
-        sK[i * BW_LD + c] = kv;
-        sG[i * BW_LD + c] = gv;
+        sQ[i * GLD + c] = qv;
+        sK[i * GLD + c] = kv;
+        sG[i * GLD + c] = gv;
     }
     if (tid < BW_C) sB[tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
     __syncthreads();
     if (tid < BW_D) {   // chunk-local inclusive cumsum; padded rows repeat the last valid G
         float run = 0.f;
         for (int i = 0; i < BW_C; ++i) {
-            run += sG[i * BW_LD + tid];
-            sG[i * BW_LD + tid] = run;
+            run += sG[i * GLD + tid];
+            sG[i * GLD + tid] = run;
         }
     }
     __syncthreads();
     float* pr = p.prep + x.ch * BWP_FLOATS;
-    for (int e = tid; e < BW_C * BW_D; e += 256) pr[BWP_G + e] = sG[(e >> 7) * BW_LD + (e & 127)];
-    // Aqk (j <= i) and Abar (j < i): one wave per row i, lane j.
-    for (int e = tid; e < BW_C * BW_C; e += 256) {
+    for (int e = tid; e < BW_C * BW_D; e += BW_PT) pr[BWP_G + e] = sG[(e >> 7) * GLD + (e & 127)];
+    // Aqk (j <= i) and Abar (j < i): one wave per row i, lane j, four channels per LDS read.
+    for (int e = tid; e < BW_C * BW_C; e += BW_PT) {
         const int i = e >> 6, j = e & 63;
         float aq = 0.f, ak = 0.f;
         if (j <= i) {
-            for (int c = 0; c < BW_D; ++c) {
-                const float d = fexp(sG[i * BW_LD + c] - sG[j * BW_LD + c]) * sK[j * BW_LD + c];
-                aq += sQ[i * BW_LD + c] * d;
-                ak += sK[i * BW_LD + c] * d;
+#pragma unroll 4
+            for (int c = 0; c < BW_D; c += 4) {
+                const f32x4 gi = lds4(sG + i * GLD + c), gj = lds4(sG + j * GLD + c), kj = lds4(sK + j * GLD + c);
+                const f32x4 qi = lds4(sQ + i * GLD + c), ki = lds4(sK + i * GLD + c);
+                for (int u = 0; u < 4; ++u) {
+                    const float d = fexp(gi[u] - gj[u]) * kj[u];
+                    aq += qi[u] * d;
+                    ak += ki[u] * d;
+                }
             }
             if (j == i) ak = 0.f;
         }
@@ -178,10 +190,16 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
 
 // ---------------------------------------------------------------- states
 // Work-group (b, hv, slice of 32 value columns), 512 threads: thread t holds
-// state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.
+// state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.  For the
+// chunk-sized products thread t takes column zn = t % 32 of rows zi + 16 r.
 __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p) {
-    __shared__ float sKG[BW_C * BW_LD], sKH[BW_C * BW_LD], sTB[BW_C * BW_MD];
-    __shared__ float sS[BW_D * BW_SD], sV[BW_C * BW_SD], sZ[BW_C * BW_SD], sVN[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sKG[BW_C * GLD];
+    __shared__ __attribute__((aligned(16))) float sKH[BW_C * GLD];
+    __shared__ __attribute__((aligned(16))) float sTB[BW_C * BW_MD];
+    __shared__ __attribute__((aligned(16))) float sS[BW_D * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sV[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sZ[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sVN[BW_C * BW_SD];
     const int tid = threadIdx.x;
     const int slice = blockIdx.x % BW_NSL;
     const int64_t bh = blockIdx.x / BW_NSL;
@@ -191,7 +209,8 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
     float S[8];
     for (int e = 0; e < 8; ++e)
         S[e] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
-    const int zn = tid & 31, zi = tid >> 5;   // Z / v_new: column zn, rows zi + 16 r
+    const int zn = tid & 31, zi = tid >> 5;
+#pragma unroll 1
     for (int ci = 0; ci < p.nc; ++ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
         float* hs = p.hs + x.ch * BW_STATE + c * BW_D + n0 + nb;
@@ -201,33 +220,44 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
         }
         if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
         const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, BW_ST);
+        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, BW_ST, GLD);
         for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
             const int i = e >> 5, n = e & 31;
             sV[i * BW_SD + n] = i < x.len ? bf2f(p.v[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
         }
         const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
         __syncthreads();
-        for (int r = 0; r < 4; ++r) {
-            const int i = zi + 16 * r;
-            float z = sV[i * BW_SD + zn];
-#pragma unroll 8
-            for (int cc = 0; cc < BW_D; ++cc) z -= sKG[i * BW_LD + cc] * sS[cc * BW_SD + zn];
-            sZ[i * BW_SD + zn] = z;
+        {   // Z = v - kg h
+            float z[4];
+            for (int r = 0; r < 4; ++r) z[r] = sV[(zi + 16 * r) * BW_SD + zn];
+#pragma unroll 2
+            for (int cc = 0; cc < BW_D; cc += 4) {
+                const float h0 = sS[cc * BW_SD + zn], h1 = sS[(cc + 1) * BW_SD + zn];
+                const float h2 = sS[(cc + 2) * BW_SD + zn], h3 = sS[(cc + 3) * BW_SD + zn];
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4 g4 = lds4(sKG + (zi + 16 * r) * GLD + cc);
+                    z[r] -= g4[0] * h0 + g4[1] * h1 + g4[2] * h2 + g4[3] * h3;
+                }
+            }
+            for (int r = 0; r < 4; ++r) sZ[(zi + 16 * r) * BW_SD + zn] = z[r];
         }
         __syncthreads();
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r) {   // v_new = Tb Z
             const int i = zi + 16 * r;
             float u = 0.f;
             for (int j = 0; j <= i; ++j) u += sTB[i * BW_MD + j] * sZ[j * BW_SD + zn];
             sVN[i * BW_SD + zn] = u;
         }
         __syncthreads();
-        for (int e = 0; e < 8; ++e) {
-            float s = gam * S[e];
-#pragma unroll 8
-            for (int i = 0; i < BW_C; ++i) s += sKH[i * BW_LD + c] * sVN[i * BW_SD + nb + e];
-            S[e] = s;
+        for (int e = 0; e < 8; ++e) S[e] *= gam;
+#pragma unroll 2
+        for (int i = 0; i < BW_C; ++i) {   // h' = gam h + kh^T v_new
+            const float kh = sKH[i * GLD + c];
+            const f32x4 a4 = lds4(sVN + i * BW_SD + nb), b4 = lds4(sVN + i * BW_SD + nb + 4);
+            for (int e = 0; e < 4; ++e) {
+                S[e] += kh * a4[e];
+                S[4 + e] += kh * b4[e];
+            }
         }
         __syncthreads();
     }
@@ -238,9 +268,14 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
 // only for the state update, so they share one LDS tile: qg is loaded once
 // dv_new is done.
 __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p) {
-    __shared__ float sKG[BW_C * BW_LD], sKQ[BW_C * BW_LD];   // kg; kh, then qg
-    __shared__ float sAQ[BW_C * BW_MD], sTB[BW_C * BW_MD];
-    __shared__ float sDH[BW_D * BW_SD], sDO[BW_C * BW_SD], sDVN[BW_C * BW_SD], sDZ[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sKG[BW_C * GLD];
+    __shared__ __attribute__((aligned(16))) float sKQ[BW_C * GLD];   // kh, then qg
+    __shared__ __attribute__((aligned(16))) float sAQ[BW_C * BW_MD];
+    __shared__ __attribute__((aligned(16))) float sTB[BW_C * BW_MD];
+    __shared__ __attribute__((aligned(16))) float sDH[BW_D * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sDO[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sDVN[BW_C * BW_SD];
+    __shared__ __attribute__((aligned(16))) float sDZ[BW_C * BW_SD];
     const int tid = threadIdx.x;
     const int slice = blockIdx.x % BW_NSL;
     const int64_t bh = blockIdx.x / BW_NSL;
@@ -251,6 +286,7 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
     for (int e = 0; e < 8; ++e)
         dh[e] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
     const int zn = tid & 31, zi = tid >> 5;
+#pragma unroll 1
     for (int ci = p.nc - 1; ci >= 0; --ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
         float* ds = p.dhs + x.ch * BW_STATE + c * BW_D + n0 + nb;
@@ -259,7 +295,7 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
             sDH[c * BW_SD + nb + e] = dh[e];
         }
         const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKQ, nullptr, sTB, tid, BW_ST);
+        load_key_ops(p, x, pr, sKG, sKQ, nullptr, sTB, tid, BW_ST, GLD);
         for (int e = tid; e < BW_C * BW_C; e += BW_ST) sAQ[(e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
         for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
             const int i = e >> 5, n = e & 31;
@@ -267,27 +303,46 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
         }
         const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
         __syncthreads();
-        for (int r = 0; r < 4; ++r) {   // dv_new = Aqk^T do + kh dh'
-            const int i = zi + 16 * r;
-            float u = 0.f;
-            for (int m = i; m < BW_C; ++m) u += sAQ[m * BW_MD + i] * sDO[m * BW_SD + zn];
-            for (int cc = 0; cc < BW_D; ++cc) u += sKQ[i * BW_LD + cc] * sDH[cc * BW_SD + zn];
-            sDVN[i * BW_SD + zn] = u;
+        {   // dv_new = Aqk^T do + kh dh'
+            float u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int cc = 0; cc < BW_D; cc += 4) {
+                const float d0 = sDH[cc * BW_SD + zn], d1 = sDH[(cc + 1) * BW_SD + zn];
+                const float d2 = sDH[(cc + 2) * BW_SD + zn], d3 = sDH[(cc + 3) * BW_SD + zn];
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4 k4 = lds4(sKQ + (zi + 16 * r) * GLD + cc);
+                    u[r] += k4[0] * d0 + k4[1] * d1 + k4[2] * d2 + k4[3] * d3;
+                }
+            }
+            for (int m = zi; m < BW_C; ++m) {
+                const float o = sDO[m * BW_SD + zn];
+                for (int r = 0; r < 4; ++r)
+                    if (zi + 16 * r <= m) u[r] += sAQ[m * BW_MD + zi + 16 * r] * o;
+            }
+            for (int r = 0; r < 4; ++r) sDVN[(zi + 16 * r) * BW_SD + zn] = u[r];
         }
         __syncthreads();
-        load_key_ops(p, x, pr, nullptr, nullptr, sKQ, nullptr, tid, BW_ST);   // kh is done with: qg replaces it
-        for (int r = 0; r < 4; ++r) {   // dZ = Tb^T dv_new
-            const int i = zi + 16 * r;
-            float z = 0.f;
-            for (int m = i; m < BW_C; ++m) z += sTB[m * BW_MD + i] * sDVN[m * BW_SD + zn];
-            sDZ[i * BW_SD + zn] = z;
+        load_key_ops(p, x, pr, nullptr, nullptr, sKQ, nullptr, tid, BW_ST, GLD);   // kh is done with: qg replaces it
+        {   // dZ = Tb^T dv_new
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int m = zi; m < BW_C; ++m) {
+                const float d = sDVN[m * BW_SD + zn];
+                for (int r = 0; r < 4; ++r)
+                    if (zi + 16 * r <= m) z[r] += sTB[m * BW_MD + zi + 16 * r] * d;
+            }
+            for (int r = 0; r < 4; ++r) sDZ[(zi + 16 * r) * BW_SD + zn] = z[r];
         }
         __syncthreads();
-        for (int e = 0; e < 8; ++e) {   // dh = gam dh' + qg^T do - kg^T dZ
-            float s = gam * dh[e];
-            for (int i = 0; i < BW_C; ++i)
-                s += sKQ[i * BW_LD + c] * sDO[i * BW_SD + nb + e] - sKG[i * BW_LD + c] * sDZ[i * BW_SD + nb + e];
-            dh[e] = s;
+        for (int e = 0; e < 8; ++e) dh[e] *= gam;
+#pragma unroll 2
+        for (int i = 0; i < BW_C; ++i) {   // dh = gam dh' + qg^T do - kg^T dZ
+            const float qg = sKQ[i * GLD + c], kg = sKG[i * GLD + c];
+            const f32x4 o0 = lds4(sDO + i * BW_SD + nb), o1 = lds4(sDO + i * BW_SD + nb + 4);
+            const f32x4 z0 = lds4(sDZ + i * BW_SD + nb), z1 = lds4(sDZ + i * BW_SD + nb + 4);
+            for (int e = 0; e < 4; ++e) {
+                dh[e] += qg * o0[e] - kg * z0[e];
+                dh[4 + e] += qg * o1[e] - kg * z1[e];
+            }
         }
         __syncthreads();
     }
@@ -300,7 +355,6 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
 // taken 16 at a time; the tiles of one such slice that are read along the
 // token index (do, v, Z, v_new, dv_new, dZ) are stored transposed, [16][68], so
 // that a thread reads four consecutive tokens with one 16-byte LDS load.
-constexpr int GLD = 132;   // row stride of the kg / kh tiles: a multiple of 4 for 16-byte reads
 constexpr int GTS = 68;    // row stride of the transposed slice tiles
 // LDS of the grad kernel, in floats.  Phase A (the loop over value slices):
 constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * GLD, GA_AQ = GA_KH + BW_C * GLD, GA_TB = GA_AQ + BW_C * BW_MD;
@@ -317,8 +371,6 @@ constexpr int GB_T = GB_BETA + BW_C, GB_AB = GB_T + BW_C * BW_MD, GB_DTB = GC_EN
 static_assert(GB_AB + BW_C * BW_MD <= GC_DAQ, "phase B temporaries must not overlap dAqk / dAbar");
 constexpr int G_LDS = GA_END > GB_END ? GA_END : GB_END;
 static_assert(G_LDS * 4 <= 160 * 1024, "grad kernel LDS");
-
-__device__ __forceinline__ f32x4 lds4(const float* a) { return *reinterpret_cast<const f32x4*>(a); }
 
 __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float F[G_LDS];
@@ -547,7 +599,7 @@ hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream) {
     const int64_t chunks = (int64_t)p.B * p.nc * p.Hv;
     const int64_t scans = (int64_t)p.B * p.Hv * BW_NSL;
     if (chunks > 0) {
-        hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)chunks), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)chunks), dim3(BW_PT), 0, stream, p);
         hipLaunchKernelGGL(kda_bwd_states_kernel, dim3((unsigned)scans), dim3(BW_ST), 0, stream, p);
     }
     if (scans > 0) hipLaunchKernelGGL(kda_bwd_dstate_kernel, dim3((unsigned)scans), dim3(BW_ST), 0, stream, p);
