@@ -265,8 +265,41 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
 
 // ---------------------------------------------------------------- dstate
 // Same grid and thread layout as states.  kh is needed only for dv_new and qg
-// only for the state update, so they share one LDS tile: qg is loaded once
-// dv_new is done.
+// only for the state update, so they share one LDS tile: qg is written once
+// dv_new is done.  The walk is bound by the latency of each chunk's loads, so
+// the raw inputs of the next chunk (k, q, G, T, beta, Aqk, do) are fetched into
+// registers while the current chunk computes dZ and the state update.  Thread t loads elements
+// e = t + 512 u of the [64][128] tiles (channel c = t % 128 for all of them) and
+// of the [64][64] tiles (column t % 64).
+struct DstateRaw {
+    uint16_t k[16], q[16];
+    float G[16], T[8], A[8], dO[4];
+    float Gl, beta;
+};
+
+__device__ __forceinline__ void dstate_fetch(const BwdParams& p, const ChunkIdx& x, int tid, int n0, DstateRaw& r) {
+    const float* pr = p.prep + x.ch * BWP_FLOATS;
+    const int c = tid & 127;
+    for (int u = 0; u < 16; ++u) {
+        const int i = (tid + BW_ST * u) >> 7;
+        const bool in = i < x.len;
+        r.k[u] = in ? p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
+        r.q[u] = in ? p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
+        r.G[u] = pr[BWP_G + tid + BW_ST * u];
+    }
+    r.Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
+    for (int u = 0; u < 8; ++u) {
+        r.T[u] = pr[BWP_T + tid + BW_ST * u];
+        r.A[u] = pr[BWP_AQK + tid + BW_ST * u];
+    }
+    const int j = tid & 63;
+    r.beta = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + BW_ST * u, i = e >> 5, n = e & 31;
+        r.dO[u] = i < x.len ? bf2f(p.dO[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n]) : 0.f;
+    }
+}
+
 __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sKG[BW_C * GLD];
     __shared__ __attribute__((aligned(16))) float sKQ[BW_C * GLD];   // kh, then qg
@@ -286,6 +319,8 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
     for (int e = 0; e < 8; ++e)
         dh[e] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
     const int zn = tid & 31, zi = tid >> 5;
+    DstateRaw raw;
+    if (p.nc > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + p.nc - 1) * p.Hv + hv), tid, n0, raw);
 #pragma unroll 1
     for (int ci = p.nc - 1; ci >= 0; --ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
@@ -294,35 +329,46 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
             ds[e] = dh[e];
             sDH[c * BW_SD + nb + e] = dh[e];
         }
-        const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKQ, nullptr, sTB, tid, BW_ST, GLD);
-        for (int e = tid; e < BW_C * BW_C; e += BW_ST) sAQ[(e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
-        for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
-            const int i = e >> 5, n = e & 31;
-            sDO[i * BW_SD + n] = i < x.len ? bf2f(p.dO[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
+        // this chunk's operands, from the registers fetched during the previous step
+        for (int u = 0; u < 16; ++u) {
+            const int i = (tid + BW_ST * u) >> 7;
+            const float kv = bf2f(raw.k[u]);
+            sKG[i * GLD + c] = kv * fexp(raw.G[u]);
+            sKQ[i * GLD + c] = kv * fexp(raw.Gl - raw.G[u]);
         }
-        const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + BW_ST * u, i = e >> 6, j = e & 63;
+            sTB[i * BW_MD + j] = raw.T[u] * raw.beta;
+            sAQ[i * BW_MD + j] = raw.A[u];
+        }
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + BW_ST * u;
+            sDO[(e >> 5) * BW_SD + (e & 31)] = raw.dO[u];
+        }
+        const float gam = fexp(raw.Gl);
         __syncthreads();
         {   // dv_new = Aqk^T do + kh dh'
-            float u[4] = {0.f, 0.f, 0.f, 0.f};
+            float u4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
             for (int cc = 0; cc < BW_D; cc += 4) {
                 const float d0 = sDH[cc * BW_SD + zn], d1 = sDH[(cc + 1) * BW_SD + zn];
                 const float d2 = sDH[(cc + 2) * BW_SD + zn], d3 = sDH[(cc + 3) * BW_SD + zn];
                 for (int r = 0; r < 4; ++r) {
                     const f32x4 k4 = lds4(sKQ + (zi + 16 * r) * GLD + cc);
-                    u[r] += k4[0] * d0 + k4[1] * d1 + k4[2] * d2 + k4[3] * d3;
+                    u4[r] += k4[0] * d0 + k4[1] * d1 + k4[2] * d2 + k4[3] * d3;
                 }
             }
             for (int m = zi; m < BW_C; ++m) {
                 const float o = sDO[m * BW_SD + zn];
                 for (int r = 0; r < 4; ++r)
-                    if (zi + 16 * r <= m) u[r] += sAQ[m * BW_MD + zi + 16 * r] * o;
+                    if (zi + 16 * r <= m) u4[r] += sAQ[m * BW_MD + zi + 16 * r] * o;
             }
-            for (int r = 0; r < 4; ++r) sDVN[(zi + 16 * r) * BW_SD + zn] = u[r];
+            for (int r = 0; r < 4; ++r) sDVN[(zi + 16 * r) * BW_SD + zn] = u4[r];
         }
         __syncthreads();
-        load_key_ops(p, x, pr, nullptr, nullptr, sKQ, nullptr, tid, BW_ST, GLD);   // kh is done with: qg replaces it
+        for (int u = 0; u < 16; ++u)   // kh is done with: qg replaces it
+            sKQ[((tid + BW_ST * u) >> 7) * GLD + c] = p.scale * bf2f(raw.q[u]) * fexp(raw.G[u]);
+        if (ci > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci - 1) * p.Hv + hv), tid, n0, raw);
         {   // dZ = Tb^T dv_new
             float z[4] = {0.f, 0.f, 0.f, 0.f};
             for (int m = zi; m < BW_C; ++m) {
@@ -336,12 +382,12 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
         for (int e = 0; e < 8; ++e) dh[e] *= gam;
 #pragma unroll 2
         for (int i = 0; i < BW_C; ++i) {   // dh = gam dh' + qg^T do - kg^T dZ
-            const float qg = sKQ[i * GLD + c], kg = sKG[i * GLD + c];
+            const float q1 = sKQ[i * GLD + c], k1 = sKG[i * GLD + c];
             const f32x4 o0 = lds4(sDO + i * BW_SD + nb), o1 = lds4(sDO + i * BW_SD + nb + 4);
             const f32x4 z0 = lds4(sDZ + i * BW_SD + nb), z1 = lds4(sDZ + i * BW_SD + nb + 4);
             for (int e = 0; e < 4; ++e) {
-                dh[e] += qg * o0[e] - kg * z0[e];
-                dh[4 + e] += qg * o1[e] - kg * z1[e];
+                dh[e] += q1 * o0[e] - k1 * z0[e];
+                dh[4 + e] += q1 * o1[e] - k1 * z1[e];
             }
         }
         __syncthreads();
