@@ -192,6 +192,32 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
 // Work-group (b, hv, slice of 32 value columns), 512 threads: thread t holds
 // state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.  For the
 // chunk-sized products thread t takes column zn = t % 32 of rows zi + 16 r.
+// The next chunk's raw inputs are fetched into registers while this one computes.
+struct StatesRaw {
+    uint16_t k[16];
+    float G[16], T[8], v[4];
+    float Gl, beta;
+};
+
+// Raw inputs of one chunk for thread t (the element layout of DstateRaw).
+__device__ __forceinline__ void states_fetch(const BwdParams& p, const ChunkIdx& x, int tid, int n0, StatesRaw& r) {
+    const float* pr = p.prep + x.ch * BWP_FLOATS;
+    const int c = tid & 127;
+    for (int u = 0; u < 16; ++u) {
+        const int i = (tid + BW_ST * u) >> 7;
+        r.k[u] = i < x.len ? p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
+        r.G[u] = pr[BWP_G + tid + BW_ST * u];
+    }
+    r.Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
+    for (int u = 0; u < 8; ++u) r.T[u] = pr[BWP_T + tid + BW_ST * u];
+    const int j = tid & 63;
+    r.beta = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + BW_ST * u, i = e >> 5, n = e & 31;
+        r.v[u] = i < x.len ? bf2f(p.v[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n]) : 0.f;
+    }
+}
+
 __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sKG[BW_C * GLD];
     __shared__ __attribute__((aligned(16))) float sKH[BW_C * GLD];
@@ -210,6 +236,8 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
     for (int e = 0; e < 8; ++e)
         S[e] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
     const int zn = tid & 31, zi = tid >> 5;
+    StatesRaw raw;
+    if (p.nc > 1) states_fetch(p, chunk_of(p, (int64_t)b * p.nc * p.Hv + hv), tid, n0, raw);
 #pragma unroll 1
     for (int ci = 0; ci < p.nc; ++ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
@@ -219,13 +247,22 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
             sS[c * BW_SD + nb + e] = S[e];
         }
         if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
-        const float* pr = p.prep + x.ch * BWP_FLOATS;
-        load_key_ops(p, x, pr, sKG, sKH, nullptr, sTB, tid, BW_ST, GLD);
-        for (int e = tid; e < BW_C * BW_SL; e += BW_ST) {
-            const int i = e >> 5, n = e & 31;
-            sV[i * BW_SD + n] = i < x.len ? bf2f(p.v[vh_off(p, b, x.t0 + i, hv) + n0 + n]) : 0.f;
+        for (int u = 0; u < 16; ++u) {
+            const int i = (tid + BW_ST * u) >> 7;
+            const float kv = bf2f(raw.k[u]);
+            sKG[i * GLD + c] = kv * fexp(raw.G[u]);
+            sKH[i * GLD + c] = kv * fexp(raw.Gl - raw.G[u]);
         }
-        const float gam = fexp(pr[BWP_G + (BW_C - 1) * BW_D + c]);
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + BW_ST * u;
+            sTB[(e >> 6) * BW_MD + (e & 63)] = raw.T[u] * raw.beta;
+        }
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + BW_ST * u;
+            sV[(e >> 5) * BW_SD + (e & 31)] = raw.v[u];
+        }
+        const float gam = fexp(raw.Gl);
+        if (ci + 1 < p.nc - 1) states_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci + 1) * p.Hv + hv), tid, n0, raw);
         __syncthreads();
         {   // Z = v - kg h
             float z[4];
@@ -436,21 +473,39 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512, GLD);
     for (int e = tid; e < BW_C * BW_C; e += 512) F[GA_AQ + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
     const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
+    // a slice's inputs for thread t: h and dh' elements t + 512 u (u < 4) of the
+    // [128][16] slice, do and v elements t + 512 u (u < 2) of the [64][16] slice;
+    // the next slice's are fetched while this one computes
+    float rH[4], rDH[4], rDO[2], rV[2];
+    auto fetch = [&](int n0) {
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 512 * u, cc = e >> 4, n = e & 15;
+            rH[u] = hs[cc * BW_D + n0 + n];
+            rDH[u] = ds[cc * BW_D + n0 + n];
+        }
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + 512 * u, i = e >> 4, n = e & 15;
+            const bool in = i < x.len;
+            const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
+            rDO[u] = in ? bf2f(p.dO[o]) : 0.f;
+            rV[u] = in ? bf2f(p.v[o]) : 0.f;
+        }
+    };
+    fetch(0);
 #pragma unroll 1
     for (int sl = 0; sl < GNSL; ++sl) {
         const int n0 = sl * GSL;
-        for (int e = tid; e < BW_D * GSL; e += 512) {
-            const int cc = e >> 4, n = e & 15;
-            F[GA_H + cc * GSD + n] = hs[cc * BW_D + n0 + n];
-            F[GA_DH + cc * GSD + n] = ds[cc * BW_D + n0 + n];
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 512 * u, cc = e >> 4, n = e & 15;
+            F[GA_H + cc * GSD + n] = rH[u];
+            F[GA_DH + cc * GSD + n] = rDH[u];
         }
-        for (int e = tid; e < BW_C * GSL; e += 512) {
-            const int i = e >> 4, n = e & 15;
-            const bool in = i < x.len;
-            const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
-            F[GA_DO + n * GTS + i] = in ? bf2f(p.dO[o]) : 0.f;
-            F[GA_V + n * GTS + i] = in ? bf2f(p.v[o]) : 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + 512 * u, i = e >> 4, n = e & 15;
+            F[GA_DO + n * GTS + i] = rDO[u];
+            F[GA_V + n * GTS + i] = rV[u];
         }
+        if (sl + 1 < GNSL) fetch(n0 + GSL);
         __syncthreads();
         {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
             float z0 = F[GA_V + zn * GTS + zi], z1 = F[GA_V + zn * GTS + zi + 32], u0 = 0.f, u1 = 0.f;
