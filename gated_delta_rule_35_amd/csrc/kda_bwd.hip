@@ -161,30 +161,32 @@ __global__ void __launch_bounds__(BW_PT) kda_bwd_prep_kernel(const BwdParams p) 
     }
 }
 
-// Loads the chunk's decayed key operands and Tb into LDS (shared by states and dstate).
+// Loads the chunk's decayed key operands, and optionally Tb, into LDS.
 // Any of sKG, sKH, sQG, sTB may be null (not loaded).
 __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx& x, const float* pr, float* sKG,
                                              float* sKH, float* sQG, float* sTB, int tid, int nthreads,
                                              int ld = BW_LD) {
-    if (sKG || sKH || sQG)
-    for (int e = tid; e < BW_C * BW_D; e += nthreads) {
-        const int i = e >> 7, c = e & 127;
-        float kv = 0.f, qv = 0.f;
-        if (i < x.len) {
-            kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
-            if (sQG) qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
+    if (sKG || sKH || sQG) {
+        for (int e = tid; e < BW_C * BW_D; e += nthreads) {
+            const int i = e >> 7, c = e & 127;
+            float kv = 0.f, qv = 0.f;
+            if (i < x.len) {
+                if (sKG || sKH) kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
+                if (sQG) qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
+            }
+            const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
+            const float eG = fexp(G);
+            if (sKG) sKG[i * ld + c] = kv * eG;
+            if (sKH) sKH[i * ld + c] = kv * fexp(Gl - G);
+            if (sQG) sQG[i * ld + c] = p.scale * qv * eG;
         }
-        const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
-        const float eG = fexp(G);
-        if (sKG) sKG[i * ld + c] = kv * eG;
-        if (sKH) sKH[i * ld + c] = kv * fexp(Gl - G);
-        if (sQG) sQG[i * ld + c] = p.scale * qv * eG;
     }
-    if (sTB)
-    for (int e = tid; e < BW_C * BW_C; e += nthreads) {
-        const int i = e >> 6, j = e & 63;
-        const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
-        sTB[i * BW_MD + j] = pr[BWP_T + e] * bj;
+    if (sTB) {
+        for (int e = tid; e < BW_C * BW_C; e += nthreads) {
+            const int i = e >> 6, j = e & 63;
+            const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
+            sTB[i * BW_MD + j] = pr[BWP_T + e] * bj;
+        }
     }
 }
 
@@ -439,13 +441,14 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
 // token index (do, v, Z, v_new, dv_new, dZ) are stored transposed, [16][68], so
 // that a thread reads four consecutive tokens with one 16-byte LDS load.
 constexpr int GTS = 68;    // row stride of the transposed slice tiles
+constexpr int GMD = 68;    // row stride of the grad kernel's Tb tile (16-byte rows)
 // LDS of the grad kernel, in floats.  Phase A (the loop over value slices):
 constexpr int GA_KG = 0, GA_KH = GA_KG + BW_C * GLD, GA_AQ = GA_KH + BW_C * GLD, GA_TB = GA_AQ + BW_C * BW_MD;
-constexpr int GA_H = GA_TB + BW_C * BW_MD, GA_DH = GA_H + BW_D * GSD, GA_DO = GA_DH + BW_D * GSD;
+constexpr int GA_H = GA_TB + BW_C * GMD, GA_DH = GA_H + BW_D * GSD, GA_DO = GA_DH + BW_D * GSD;
 constexpr int GA_V = GA_DO + GSL * GTS, GA_Z = GA_V + GSL * GTS, GA_VN = GA_Z + GSL * GTS;
 constexpr int GA_DVN = GA_VN + GSL * GTS, GA_DZ = GA_DVN + GSL * GTS, GA_END = GA_DZ + GSL * GTS;
 static_assert(GA_H % 4 == 0 && GA_DO % 4 == 0 && GA_V % 4 == 0 && GA_Z % 4 == 0 && GA_VN % 4 == 0 &&
-              GA_DVN % 4 == 0 && GA_DZ % 4 == 0 && GA_KH % 4 == 0, "16-byte aligned tiles");
+              GA_DVN % 4 == 0 && GA_DZ % 4 == 0 && GA_KH % 4 == 0 && GA_TB % 4 == 0, "16-byte aligned tiles");
 // Phase B (the inverse's gradient), then phase C (the pairwise terms):
 constexpr int GC_Q = 0, GC_K = GC_Q + BW_C * BW_LD, GC_G = GC_K + BW_C * BW_LD, GC_DAQ = GC_G + BW_C * BW_LD;
 constexpr int GC_DAB = GC_DAQ + BW_C * BW_MD, GC_END = GC_DAB + BW_C * BW_MD;
@@ -470,8 +473,15 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     for (int r = 0; r < 16; ++r) aQ[r] = aKG[r] = aKH[r] = 0.f;
     for (int s = 0; s < 8; ++s) aAQ[s] = aTB[s] = 0.f;
 
-    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, F + GA_TB, tid, 512, GLD);
-    for (int e = tid; e < BW_C * BW_C; e += 512) F[GA_AQ + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_AQK + e];
+    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, nullptr, tid, 512, GLD);
+    {
+        const int j = tid & 63;   // the same column for every element this thread loads
+        const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
+        for (int e = tid; e < BW_C * BW_C; e += 512) {
+            F[GA_AQ + (e >> 6) * BW_MD + j] = pr[BWP_AQK + e];
+            F[GA_TB + (e >> 6) * GMD + j] = pr[BWP_T + e] * bj;
+        }
+    }
     const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
     // a slice's inputs for thread t: h and dh' elements t + 512 u (u < 4) of the
     // [128][16] slice, do and v elements t + 512 u (u < 2) of the [64][16] slice;
@@ -521,8 +531,14 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
                     u1 += k1[e] * d;
                 }
             }
-            for (int m = zi; m < BW_C; ++m) u0 += F[GA_AQ + m * BW_MD + zi] * F[GA_DO + zn * GTS + m];
-            for (int m = zi + 32; m < BW_C; ++m) u1 += F[GA_AQ + m * BW_MD + zi + 32] * F[GA_DO + zn * GTS + m];
+            // Aqk is zero above the diagonal, so the sums may start at a multiple of 4
+            for (int m = zi & ~3; m < BW_C; m += 4) {
+                const f32x4 o4 = lds4(F + GA_DO + zn * GTS + m);
+                for (int e = 0; e < 4; ++e) {
+                    u0 += F[GA_AQ + (m + e) * BW_MD + zi] * o4[e];
+                    if (m >= 32) u1 += F[GA_AQ + (m + e) * BW_MD + zi + 32] * o4[e];
+                }
+            }
             F[GA_Z + zn * GTS + zi] = z0;
             F[GA_Z + zn * GTS + zi + 32] = z1;
             F[GA_DVN + zn * GTS + zi] = u0;
@@ -532,8 +548,15 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
         for (int r = 0; r < 2; ++r) {   // v_new = Tb Z;  dZ = Tb^T dv_new = dv
             const int i = zi + 32 * r;
             float vn = 0.f, dz = 0.f;
-            for (int j = 0; j <= i; ++j) vn += F[GA_TB + i * BW_MD + j] * F[GA_Z + zn * GTS + j];
-            for (int m = i; m < BW_C; ++m) dz += F[GA_TB + m * BW_MD + i] * F[GA_DVN + zn * GTS + m];
+            // Tb is zero above the diagonal: whole groups of 4 cover the triangle
+            for (int j = 0; j <= i; j += 4) {
+                const f32x4 t4 = lds4(F + GA_TB + i * GMD + j), z4 = lds4(F + GA_Z + zn * GTS + j);
+                vn += t4[0] * z4[0] + t4[1] * z4[1] + t4[2] * z4[2] + t4[3] * z4[3];
+            }
+            for (int m = i & ~3; m < BW_C; m += 4) {
+                const f32x4 d4 = lds4(F + GA_DVN + zn * GTS + m);
+                for (int e = 0; e < 4; ++e) dz += F[GA_TB + (m + e) * GMD + i] * d4[e];
+            }
             F[GA_VN + zn * GTS + i] = vn;
             F[GA_DZ + zn * GTS + i] = dz;
             if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + zn] = dz;

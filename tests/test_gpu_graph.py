@@ -1,5 +1,5 @@
 """The library's launches under HIP graph capture (torch.cuda.graph): kda_fwd,
-kda_fwd_cp and kda_decode are captured once with caller-owned outputs and
+kda_fwd_cp, kda_decode and kda_bwd are captured once with caller-owned outputs and
 workspaces (nothing is allocated and no memset is recorded), then replayed
 several times with eager work and synchronisation in between; every replay
 must reproduce the eager result bit for bit."""
@@ -85,3 +85,22 @@ def test_kda_decode_in_a_graph():
     o_ref, n_ref = kda_decode(*args, new_state=torch.empty_like(state))
     out, new = torch.empty_like(o_ref), torch.empty_like(n_ref)
     capture_and_replay(lambda: kda_decode(*args, out=out, new_state=new), (out, new), (o_ref, n_ref))
+
+
+def test_kda_bwd_in_a_graph():
+    _say("graph: kda_bwd B=2 T=150 Hq=2 Hv=4 with h0, dhT and dh0")
+    from gated_delta_rule_35_amd import kda_bwd, kda_bwd_workspace_size
+    x = make_inputs(2, 150, 2, 4, torch.float32, h0=True, seed=302)
+    d = to_device(x)
+    gen = torch.Generator("cpu").manual_seed(303)
+    do = torch.randn(2, 150, 4, 128, generator=gen).to(torch.bfloat16).cuda()
+    dhT = torch.randn(2, 4, 128, 128, generator=gen).cuda()
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, do)
+    ref = kda_bwd(*args, initial_state=d["h0"], d_final_state=dhT, d_initial_state=True)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+    outs = {n: torch.empty_like(ref[n]) for n in names}
+    ws = torch.empty(kda_bwd_workspace_size(2, 150, 2, 4), dtype=torch.uint8, device="cuda")
+    capture_and_replay(lambda: kda_bwd(*args, initial_state=d["h0"], d_final_state=dhT, grads=outs,
+                                       d_initial_state=outs["dh0"], workspace=ws),
+                       [outs[n] for n in names], [ref[n] for n in names])
