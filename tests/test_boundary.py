@@ -429,3 +429,16 @@ def test_bwd_empty_problem_needs_no_launch(lib):
             if a[key] is not None and a[key].shape[0] * a[key].shape[1] == 0:
                 a[key].data = None
         expect_bwd(lib, a, "KDA_OK")
+
+
+def test_binding_refuses_host_tensors():
+    # no CPU fallback: host tensors are rejected before the library is called
+    import torch
+    from gated_delta_rule_35_amd import kda_bwd, kda_decode
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 4, 1, 128)
+    beta = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        kda_bwd(q, q, q, g, beta, 0.1, q)
+    with pytest.raises(ValueError):
+        kda_decode(q[:, 0], q[:, 0], q[:, 0], g[:, 0], beta[:, 0], 0.1, None)

@@ -99,6 +99,21 @@ def test_bwd_matches_oracle(B, T, Hq, Hv, h0, dhT, beta_dtype):
     _compare(got, _oracle(x), f"B{B} T{T}")
 
 
+def test_bwd_strong_decay():
+    # g near -3 per token and channel: e^G underflows within a chunk, the regime where
+    # the forward needs its exact diagonal path; every factor here is exp of a
+    # non-positive difference, so nothing overflows
+    x = make_inputs(2, 140, 2, 2, torch.float32, True, seed=9, g_shift=-3.0)
+    gen = torch.Generator("cpu").manual_seed(1009)
+    x["do"] = torch.randn(2, 140, 2, 128, generator=gen).to(torch.bfloat16)
+    x["dhT"] = torch.randn(2, 2, 128, 128, generator=gen)
+    _say("kda_bwd B=2 T=140 strong decay (g_shift -3)")
+    got = _gpu_grads(x)
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    _compare(got, _oracle(x), "strong decay")
+
+
 def test_bwd_empty_sequence_passes_the_state_gradient_through():
     x = _case(2, 0, 1, 2, seed=5)
     _say("kda_bwd T=0")
