@@ -86,49 +86,70 @@ __device__ __forceinline__ int64_t vh_off(const BwdParams& p, int b, int64_t t, 
 }
 
 // ---------------------------------------------------------------- prep
+// q and k stay bf16 in LDS (exact: they are bf16 inputs), and Abar and T reuse
+// their space once the pairwise products are done, so that two work-groups fit
+// on a CU.
 constexpr int BW_PT = 512;   // threads of the prep work-group
+constexpr int PQ_LD = 136;   // row stride (bf16 elements) of the q / k tiles: 8-byte aligned rows
+struct PrepLds {
+    union {
+        struct {
+            uint16_t q[BW_C * PQ_LD], k[BW_C * PQ_LD];
+        } in;
+        struct {
+            float A[BW_C * BW_MD], T[BW_C * BW_MD];
+        } out;
+    } u;
+    float G[BW_C * GLD];
+    float beta[BW_C];
+};
 
-__global__ void __launch_bounds__(BW_PT) kda_bwd_prep_kernel(const BwdParams p) {
-    __shared__ __attribute__((aligned(16))) float sQ[BW_C * GLD];
-    __shared__ __attribute__((aligned(16))) float sK[BW_C * GLD];
-    __shared__ __attribute__((aligned(16))) float sG[BW_C * GLD];
-    __shared__ float sA[BW_C * BW_MD], sT[BW_C * BW_MD], sB[BW_C];
+__device__ __forceinline__ f32x4 lds_bf4(const uint16_t* a) {
+    const uint2 w = *reinterpret_cast<const uint2*>(a);
+    return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+}
+
+__global__ void __launch_bounds__(BW_PT, 2) kda_bwd_prep_kernel(const BwdParams p) {
+    __shared__ __attribute__((aligned(16))) PrepLds L;
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
     for (int e = tid; e < BW_C * BW_D; e += BW_PT) {
         const int i = e >> 7, c = e & 127;
-        float qv = 0.f, kv = 0.f, gv = 0.f;   // rows past the sequence's end: q = k = 0, g = 0
+        uint16_t qv = 0, kv = 0;   // rows past the sequence's end: q = k = 0, g = 0
+        float gv = 0.f;
         if (i < x.len) {
             const int64_t t = x.t0 + i;
-            qv = bf2f(p.q[qk_off(p, x.b, t, x.hq) + c]);
-            kv = bf2f(p.k[qk_off(p, x.b, t, x.hq) + c]);
+            qv = p.q[qk_off(p, x.b, t, x.hq) + c];
+            kv = p.k[qk_off(p, x.b, t, x.hq) + c];
             gv = p.g[vh_off(p, x.b, t, x.hv) + c];
         }
-        sQ[i * GLD + c] = qv;
-        sK[i * GLD + c] = kv;
-        sG[i * GLD + c] = gv;
+        L.u.in.q[i * PQ_LD + c] = qv;
+        L.u.in.k[i * PQ_LD + c] = kv;
+        L.G[i * GLD + c] = gv;
     }
-    if (tid < BW_C) sB[tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
+    if (tid < BW_C) L.beta[tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
     __syncthreads();
     if (tid < BW_D) {   // chunk-local inclusive cumsum; padded rows repeat the last valid G
         float run = 0.f;
         for (int i = 0; i < BW_C; ++i) {
-            run += sG[i * GLD + tid];
-            sG[i * GLD + tid] = run;
+            run += L.G[i * GLD + tid];
+            L.G[i * GLD + tid] = run;
         }
     }
     __syncthreads();
     float* pr = p.prep + x.ch * BWP_FLOATS;
-    for (int e = tid; e < BW_C * BW_D; e += BW_PT) pr[BWP_G + e] = sG[(e >> 7) * GLD + (e & 127)];
+    for (int e = tid; e < BW_C * BW_D; e += BW_PT) pr[BWP_G + e] = L.G[(e >> 7) * GLD + (e & 127)];
     // Aqk (j <= i) and Abar (j < i): one wave per row i, lane j, four channels per LDS read.
-    for (int e = tid; e < BW_C * BW_C; e += BW_PT) {
-        const int i = e >> 6, j = e & 63;
+    float abar[BW_C * BW_C / BW_PT];
+    for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
+        const int e = tid + BW_PT * s, i = e >> 6, j = e & 63;
         float aq = 0.f, ak = 0.f;
         if (j <= i) {
 #pragma unroll 4
             for (int c = 0; c < BW_D; c += 4) {
-                const f32x4 gi = lds4(sG + i * GLD + c), gj = lds4(sG + j * GLD + c), kj = lds4(sK + j * GLD + c);
-                const f32x4 qi = lds4(sQ + i * GLD + c), ki = lds4(sK + i * GLD + c);
+                const f32x4 gi = lds4(L.G + i * GLD + c), gj = lds4(L.G + j * GLD + c);
+                const f32x4 kj = lds_bf4(L.u.in.k + j * PQ_LD + c);
+                const f32x4 qi = lds_bf4(L.u.in.q + i * PQ_LD + c), ki = lds_bf4(L.u.in.k + i * PQ_LD + c);
                 for (int u = 0; u < 4; ++u) {
                     const float d = fexp(gi[u] - gj[u]) * kj[u];
                     aq += qi[u] * d;
@@ -139,7 +160,12 @@ __global__ void __launch_bounds__(BW_PT) kda_bwd_prep_kernel(const BwdParams p) 
         }
         pr[BWP_AQK + e] = p.scale * aq;
         pr[BWP_ABAR + e] = ak;
-        sA[i * BW_MD + j] = ak;
+        abar[s] = ak;
+    }
+    __syncthreads();   // q and k are dead: Abar and T take their space
+    for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
+        const int e = tid + BW_PT * s;
+        L.u.out.A[(e >> 6) * BW_MD + (e & 63)] = abar[s];
     }
     __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution: lane j owns column j,
@@ -152,10 +178,10 @@ __global__ void __launch_bounds__(BW_PT) kda_bwd_prep_kernel(const BwdParams p) 
                 t = 1.f;
             } else if (i > j) {
                 float s = 0.f;
-                for (int m = j; m < i; ++m) s += sA[i * BW_MD + m] * sT[m * BW_MD + j];
-                t = -sB[i] * s;
+                for (int m = j; m < i; ++m) s += L.u.out.A[i * BW_MD + m] * L.u.out.T[m * BW_MD + j];
+                t = -L.beta[i] * s;
             }
-            sT[i * BW_MD + j] = t;
+            L.u.out.T[i * BW_MD + j] = t;
             pr[BWP_T + i * BW_C + j] = t;
         }
     }
