@@ -527,7 +527,8 @@ kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
     const int64_t nc = (T + 63) / 64;
     if (B * nc * Hv > kMaxBlocks || B * Hv * 8 > kMaxBlocks || B > (int64_t(1) << 24) || Hv > (int64_t(1) << 16))
         return KDA_ERR_UNSUPPORTED;
-    if (B * T * Hq * kHeadDim > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
+    // the group kernel's grid, (B T Hq 128) / 256 work-groups, must fit 32 bits
+    if (B * T * Hq * kHeadDim > (int64_t(1) << 39)) return KDA_ERR_UNSUPPORTED;
     const BwdLayout L = bwd_layout(B, T, Hq, Hv);
     if (workspace && (workspace_size < L.total || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
         return KDA_ERR_WORKSPACE;
