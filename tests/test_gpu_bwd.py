@@ -158,3 +158,33 @@ def test_bwd_full_size_sampled_heads():
         _say(f"full size {n}: rel frob {err:.2e}")
         assert err <= TOL, (n, err)
         assert np.isfinite(got[n]).all(), n
+
+
+def test_bwd_full_size_gva_group():
+    # the 1 x 4096 token batch with 16 q/k heads and 64 value heads: the four value heads of
+    # q/k head 5 checked; dq and dk of that head are the sums over its group
+    from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["gva_b1_hq16_hv64_t4096"]
+    x, _ = workload_inputs(w)
+    gen = torch.Generator("cpu").manual_seed(1010)
+    x["do"] = torch.randn(w.B, w.T, w.Hv, 128, generator=gen).to(torch.bfloat16)
+    x["dhT"] = None
+    _say(f"kda_bwd GVA B={w.B} T={w.T} Hq={w.Hq} Hv={w.Hv}")
+    got = _gpu_grads(x, want_dh0=x["h0"] is not None)
+    group = w.Hv // w.Hq
+    hq = 5
+    heads = list(range(hq * group, (hq + 1) * group))
+    sub = head_subset(x, heads, w.Hq, w.Hv)
+    sub["do"] = x["do"][:, :, heads]
+    sub["dhT"] = None
+    ref = _oracle(sub)
+    for n in ("dv", "dg", "dbeta"):
+        err = _rel_per_head(got[n][:, :, heads], ref[n], 2)
+        _say(f"GVA {n}: rel frob {err:.2e}")
+        assert err <= TOL, (n, err)
+    for n in ("dq", "dk"):
+        g = got[n][:, :, hq]
+        r = ref[n].sum(axis=2)
+        err = np.linalg.norm(g - r) / np.linalg.norm(r)
+        _say(f"GVA {n} (group sum): rel frob {err:.2e}")
+        assert err <= TOL, (n, err)
