@@ -294,6 +294,10 @@ int64_t kda_bwd_workspace_size(int64_t batch, int64_t seq_len, int64_t num_qk_he
  * finished; NULL makes the library allocate it with hipMallocAsync on `stream`
  * and release it with hipFreeAsync.  Checks, error codes, stream semantics and
  * reproducibility are those of kda_fwd; the call does not synchronise.
+ * Sequences of different lengths: pad them to a common T with q = k = v = 0,
+ * g = 0, beta = 0 and d_out = 0.  Such tokens neither decay nor write the
+ * state, so each row's gradients are those of its own sequence; the pads get
+ * zero dq, dk, dv and dbeta.
  */
 kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                      const kda_tensor_t* g, const kda_tensor_t* beta, float scale,

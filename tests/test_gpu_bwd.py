@@ -188,3 +188,27 @@ def test_bwd_full_size_gva_group():
         err = np.linalg.norm(g - r) / np.linalg.norm(r)
         _say(f"GVA {n} (group sum): rel frob {err:.2e}")
         assert err <= TOL, (n, err)
+
+
+def test_bwd_padded_rows_equal_separate_sequences():
+    # sequences of different lengths as equal-length rows: the tail of the shorter row is
+    # padded with q = k = v = 0, g = 0, beta = 0 and zero output gradient, tokens that
+    # neither decay nor write the state, so each row's gradients are its sequence's own
+    T, lens = 100, (100, 37)
+    x = _case(2, T, 2, 2, seed=11)
+    for key in ("q", "k", "v", "g", "beta", "do"):
+        x[key][1, lens[1]:] = 0
+    _say("kda_bwd padded rows: lengths 100 and 37")
+    got = _gpu_grads(x)
+    for b, L in enumerate(lens):
+        row = {k: (v[b:b + 1, :L] if k in ("q", "k", "v", "g", "beta", "do") else
+                   (v[b:b + 1] if v is not None else None)) for k, v in x.items()}
+        ref = _oracle(row)
+        for n in NAMES:
+            g = got[n][b:b + 1] if n == "dh0" else got[n][b:b + 1, :L]
+            err = _rel_per_head(g, ref[n], 1 if n == "dh0" else 2)
+            _say(f"row {b} (length {L}) {n}: rel frob {err:.2e}")
+            assert err <= TOL, (b, n, err)
+        if L < T:
+            for n in ("dq", "dk", "dv", "dbeta"):
+                assert not np.any(got[n][b, L:]), n   # pads get no gradient
