@@ -494,6 +494,25 @@ def main():
     log(f"{ms_per_step:.4f} ms/step (wall); intra kernel avg {t_intra * 1e3:.4f} ms (min {min(intra_ms):.4f}), "
         f"scan kernel avg {t_scan * 1e3:.4f} ms (min {min(scan_ms):.4f}); {tokens_per_s / 1e6:.2f} M tokens/s")
 
+    # The 11-argument kda_fwd on the same inputs: its device memory beyond the
+    # caller's tensors comes from hipMallocAsync / hipFreeAsync on the stream,
+    # inside the call (HIP events around each whole call).
+    from gated_delta_rule_35_amd import kda_fwd
+    for _ in range(2):
+        kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                out=out, final_state=hT)
+    torch.cuda.synchronize()
+    ev11 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev11:
+        e[0].record(stream)
+        kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                out=out, final_state=hT)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    call11 = [e[0].elapsed_time(e[1]) for e in ev11]
+    t_call11 = sum(call11) / len(call11) / 1e3
+    log(f"kda_fwd (11 arguments) avg {t_call11 * 1e3:.4f} ms per call")
+
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
     n_ch = chunk_heads(lengths, w.Hv)
@@ -544,6 +563,7 @@ def main():
                    "dv_slices": kda_dv_slices(N, w.Hv), "mfma_operands": "f16", "accumulate": "f32",
                    "io": "bf16 q/k/v/o, f32 g/state"},
         "kernel_ms_avg": round(t_kern * 1e3, 5),
+        "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
         "algorithmic_bytes_per_step": nbytes,
         "roofline": roofline,
         "mfma": mfma,

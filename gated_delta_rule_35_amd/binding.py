@@ -1,13 +1,12 @@
 """ctypes binding of libkda.so (argument marshalling only).
 
-Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_intra, kda_fwd_scan,
-kda_fwd_trace, kda_fwd_cp, kda_decode, kda_fwd_workspace_size,
-kda_fwd_cp_workspace_size, kda_status_string, kda_dv_slices.  Tensors are passed
-as kda_tensor_t descriptors built from torch tensors (data pointer, dtype,
-shape, strides); the stream is torch's current HIP stream unless one is given.
-The workspace is a uint8 device tensor from torch's caching allocator unless
-the caller passes one (or `workspace=False`, which lets the library allocate
-it in stream order).
+Names follow the C ABI in include/kda.h: kda_fwd, kda_fwd_ws, kda_fwd_intra,
+ kda_fwd_scan, kda_fwd_trace, kda_fwd_cp, kda_decode, kda_bwd and
+their size queries, kda_status_string, kda_dv_slices.  Tensors are passed as
+kda_tensor_t descriptors built from torch tensors (data pointer, dtype, shape,
+strides); the stream is torch's current HIP stream unless one is given.  Where
+an entry point takes a workspace, it is a uint8 device tensor the caller passes
+or one taken here from torch's caching allocator.
 """
 import ctypes
 import os
@@ -22,9 +21,10 @@ KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
-EXPORTED = ["kda_fwd", "kda_fwd_intra", "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode",
-            "kda_bwd", "kda_fwd_workspace_size", "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan",
-            "kda_bwd_workspace_size", "kda_status_string", "kda_dv_slices"]
+EXPORTED = ["kda_fwd", "kda_fwd_ws", "kda_fwd_intra",
+            "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode", "kda_bwd", "kda_fwd_workspace_size",
+            "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_bwd_workspace_size", "kda_status_string",
+            "kda_dv_slices"]
 
 
 class KdaTensor(ctypes.Structure):
@@ -58,11 +58,13 @@ def load_library(path=None):
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(p)
     tp = ctypes.POINTER(KdaTensor)
-    lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p, ctypes.c_int64,
-                            ctypes.c_void_p]
+    lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_ws.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_void_p]
+    lib.kda_fwd_ws.restype = ctypes.c_int
     for name in ("kda_fwd_intra", "kda_fwd_scan"):
-        getattr(lib, name).argtypes = lib.kda_fwd.argtypes
+        getattr(lib, name).argtypes = lib.kda_fwd_ws.argtypes
         getattr(lib, name).restype = ctypes.c_int
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
@@ -137,40 +139,43 @@ def kda_fwd_workspace_size(total_tokens, num_sequences, num_value_heads):
 
 
 def _workspace(workspace, q, v, cu_seqlens, stream):
-    """(tensor, pointer, size) of the workspace argument: a given uint8 tensor,
-    NULL for workspace=False (the library allocates in stream order), else a
-    fresh tensor of the size the library asks for.  A fresh tensor is marked as
-    used on an explicitly given stream, so the caching allocator does not hand
-    it out again before that stream's work on it is done."""
-    if workspace is False:
-        return None, None, 0
+    """(tensor, pointer, size) of a workspace argument: the given uint8 tensor, or
+    a fresh one from torch's caching allocator of the size the library asks for.
+    A fresh tensor is marked as used on an explicitly given stream, so the
+    caching allocator does not hand it out again before that stream's work on it
+    is done."""
     if workspace is None:
         if q.dim() != 4 or v.dim() != 4:
             return None, None, 0   # the C library rejects the shapes
-        if stream is not None and not isinstance(stream, torch.cuda.Stream):
-            return None, None, 0   # a raw stream handle: let the library allocate on it
         n = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
         size = kda_fwd_workspace_size(q.shape[0] * q.shape[1], max(n, 0), v.shape[2])
         if size <= 0:
             return None, None, 0
         workspace = torch.empty(size, dtype=torch.uint8, device=v.device)
-        if stream is not None:
+        if stream is not None and isinstance(stream, torch.cuda.Stream):
             workspace.record_stream(stream)
     return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace,
-          entry="kda_fwd"):
+          entry):
+    """One forward entry point.  Entries with a workspace argument (kda_fwd_ws,
+    the stage calls, kda_fwd_trace) get `workspace` (None: allocated here);
+    kda_fwd takes none."""
     lib = load_library()
     tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
     for t in tensors:
         if t is not None and not t.is_cuda:
-            raise ValueError("kda_fwd needs every tensor on the GPU")
+            raise ValueError(f"{entry} needs every tensor on the GPU")
     descs = [describe(t) for t in tensors]
     s = _stream_handle(stream, tensors)
-    _ws, ws_ptr, ws_size = _workspace(workspace, q, v, cu_seqlens, stream)
     args = [_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]), float(scale),
-            _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8]), ws_ptr, ws_size]
+            _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8])]
+    if entry == "kda_fwd":
+        _check(lib, getattr(lib, entry)(*args, s))
+        return
+    _ws, ws_ptr, ws_size = _workspace(workspace, q, v, cu_seqlens, stream)
+    args += [ws_ptr, ws_size]
     if trace is None:
         _check(lib, getattr(lib, entry)(*args, s))
     else:
@@ -178,19 +183,34 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
         _check(lib, lib.kda_fwd_trace(*args, ctypes.byref(tr), s))
 
 
-def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
-            stream=None, workspace=None):
-    """KDA forward.  Returns (out, final_state); allocates them when not given
-    (final_state is allocated only when `final_state=True` is passed).
-    `workspace`: a uint8 device tensor of at least kda_fwd_workspace_size() bytes,
-    None (allocated here from torch's caching allocator) or False (the library
-    allocates it in stream order)."""
+def _outputs(q, v, cu_seqlens, out, final_state):
     if out is None:
         out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
     if final_state is True:
         n = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
         final_state = torch.empty((n, v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=v.device)
-    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace)
+    return out, final_state
+
+
+def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+            stream=None, workspace=None):
+    """KDA forward.  Returns (out, final_state); allocates them when not given
+    (final_state is allocated only when `final_state=True` is passed).
+    Without `workspace` this is the C kda_fwd; with a uint8 device tensor of at
+    least kda_fwd_workspace_size() bytes it is kda_fwd_ws on that workspace."""
+    out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
+    entry = "kda_fwd" if workspace is None else "kda_fwd_ws"
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace, entry)
+    return out, final_state
+
+
+def kda_fwd_ws(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+               stream=None, workspace=None):
+    """The two-pass forward with a caller workspace (C kda_fwd_ws); `workspace`
+    None takes one from torch's caching allocator.  Returns (out, final_state)."""
+    out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace,
+          "kda_fwd_ws")
     return out, final_state
 
 
@@ -214,9 +234,9 @@ def kda_fwd_trace(q, k, v, g, beta, scale, trace, cu_seqlens=None, initial_state
                   final_state=None, stream=None, workspace=None):
     """kda_fwd that also fills the fp32 intermediate dumps in `trace`, a dict with
     any of the keys G, Aqk, Akk, T, W, U, v_new, h (see include/kda.h)."""
-    if out is None:
-        out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
-    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace)
+    out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, trace, workspace,
+          "kda_fwd_trace")
     return out, final_state
 
 

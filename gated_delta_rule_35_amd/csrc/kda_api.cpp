@@ -232,7 +232,16 @@ int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int6
 kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                      const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
                      const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
-                     void* workspace, int64_t workspace_size, void* stream) {
+                     void* stream) {
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, nullptr, 0, nullptr, kBoth,
+               stream);
+}
+
+kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                        const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
+                        const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
+                        void* workspace, int64_t workspace_size, void* stream) {
+    if (!workspace) return KDA_ERR_WORKSPACE;
     return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
                nullptr, kBoth, stream);
 }
@@ -582,7 +591,8 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported configuration";
         case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scale must be finite and positive";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
-        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_fwd_workspace_size or misaligned";
+        case KDA_ERR_WORKSPACE:
+            return "KDA_ERR_WORKSPACE: workspace missing, smaller than the entry point's workspace size or misaligned";
     }
     return "KDA: unknown status";
 }

@@ -76,15 +76,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 5, /* head dim != 128, Hv % Hq != 0, B != 1 with cu_seqlens, grid too large */
     KDA_ERR_VALUE = 6,       /* scale not finite or not > 0 */
     KDA_ERR_HIP = 7,         /* the HIP runtime reported an error at launch or allocation */
-    KDA_ERR_WORKSPACE = 8    /* workspace smaller than kda_fwd_workspace_size() or not 16-byte aligned */
+    KDA_ERR_WORKSPACE = 8    /* entry points with a workspace: missing, too small or misaligned */
 } kda_status_t;
-
-/*
- * kda_fwd_workspace_size -- bytes of device workspace kda_fwd needs for a call
- * with `total_tokens` = B * T tokens, N sequences and Hv value heads:
- * (ceil(total_tokens / 64) + N) * Hv * 61952.  Returns -1 for a negative size.
- */
-int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads);
 
 /*
  * kda_fwd -- the KDA forward pass over a batch.
@@ -98,11 +91,9 @@ int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int6
  * initial_state may alias final_state (each state tile is read before it is
  * written, by the same work-group); a partial overlap of the two returns
  * KDA_ERR_LAYOUT.
- * workspace: device memory of at least kda_fwd_workspace_size() bytes,
- * 16-byte aligned, owned by the caller and not used by anything else until the
- * call's work on `stream` has finished; its contents need no initialisation.
- * With workspace == NULL the library allocates it with hipMallocAsync on
- * `stream` and releases it with hipFreeAsync after the two launches.
+ * Device memory beyond the caller's tensors, if the call needs any, is
+ * allocated with hipMallocAsync on `stream` and released with hipFreeAsync on
+ * it, so calls on different streams never share it.
  * cu_seqlens must be non-decreasing with cu_seqlens[0] = 0 and
  * cu_seqlens[N] <= T.  That is a precondition the host cannot check without a
  * device read; the kernel clamps every sequence to [0, T) so that malformed
@@ -118,8 +109,33 @@ int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int6
 kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                      const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                      const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
-                     const kda_tensor_t* out, const kda_tensor_t* final_state,
-                     void* workspace, int64_t workspace_size, void* stream);
+                     const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
+
+/*
+ * kda_fwd_workspace_size -- bytes of device workspace kda_fwd_ws needs for a
+ * call with `total_tokens` = B * T tokens, N sequences and Hv value heads:
+ * (ceil(total_tokens / 64) + N) * Hv * 61952.  Returns -1 for a negative size.
+ */
+int64_t kda_fwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads);
+
+/*
+ * kda_fwd_ws -- the two-pass form of the forward with a caller-owned workspace:
+ * an intra-chunk kernel over every chunk at once writes one record per chunk
+ * and value head to `workspace`, and a scan kernel walks each sequence's chunks
+ * in order, reading them.  Same arguments, checks, results and semantics as
+ * kda_fwd, plus:
+ * workspace: device memory of at least kda_fwd_workspace_size() bytes,
+ * 16-byte aligned, owned by the caller and not used by anything else until the
+ * call's work on `stream` has finished; its contents need no initialisation.
+ * NULL, a smaller size or a misaligned pointer return KDA_ERR_WORKSPACE.
+ * The call allocates nothing and records no memset, so it can be captured into
+ * a HIP graph.
+ */
+kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                        const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                        const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                        const kda_tensor_t* out, const kda_tensor_t* final_state,
+                        void* workspace, int64_t workspace_size, void* stream);
 
 /*
  * kda_fwd_cp -- kda_fwd for fixed-length batches, with each sequence cut into
@@ -257,7 +273,6 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
                         const kda_tensor_t* state_in, const kda_tensor_t* state_out,
                         const kda_tensor_t* out, void* stream);
 
-/* Human-readable name of a status code (static storage; never NULL). */
 /*
  * kda_bwd_workspace_size -- bytes of device workspace kda_bwd needs for a
  * fixed-length batch of B rows of T tokens with Hq query/key heads and Hv value
@@ -307,6 +322,7 @@ kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
                      const kda_tensor_t* d_initial_state, void* workspace, int64_t workspace_size,
                      void* stream);
 
+/* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status_t status);
 
 /* Number of dv slices (scan work-groups per sequence and value head) that

@@ -56,10 +56,15 @@ def good(B=1, T_=64, Hq=2, Hv=2, beta_dtype=binding.KDA_F32):
                 out=T([B, T_, Hv, 128]))
 
 
-def call(lib, a, scale=0.088, cu=None, h0=None, hT=None, ws=None, ws_size=0):
+def call(lib, a, scale=0.088, cu=None, h0=None, hT=None, ws=None, ws_size=None, entry="kda_fwd"):
+    """One forward call: the 11-argument kda_fwd, or, when a workspace size is
+    given, kda_fwd_ws."""
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
-    return lib.kda_fwd(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")),
-                       scale, r(cu), r(h0), r(a.get("out")), r(hT), ws, ws_size, None)
+    args = (r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale, r(cu), r(h0),
+            r(a.get("out")), r(hT))
+    if ws_size is not None:
+        return lib.kda_fwd_ws(*args, ws, ws_size, None)
+    return getattr(lib, entry)(*args, None)
 
 
 def expect(lib, a, name, **kw):
@@ -178,6 +183,17 @@ def test_dv_slices(lib):
         assert lib.kda_dv_slices(n, hv) == 2
 
 
+def test_kda_fwd_has_the_eleven_argument_signature(lib):
+    # q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream
+    assert len(lib.kda_fwd.argtypes) == 11
+    assert len(lib.kda_fwd_ws.argtypes) == 13
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decl = re.search(r"kda_status_t\s+kda_fwd\s*\((.*?)\);", text, flags=re.S).group(1)
+    names = [p.strip().split()[-1].lstrip("*") for p in decl.split(",")]
+    assert names == ["q", "k", "v", "g", "beta", "scale", "cu_seqlens", "initial_state", "out", "final_state",
+                     "stream"]
+
+
 def test_trace_requires_descriptor(lib):
     a = good()
     r = ctypes.byref
@@ -205,6 +221,7 @@ def test_workspace_checked_before_launch(lib):
     need = lib.kda_fwd_workspace_size(200, 2, 4)
     expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
     expect(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE + 8, ws_size=need)
+    expect(lib, a, "KDA_ERR_WORKSPACE", ws=None, ws_size=need)   # kda_fwd_ws requires one
     # a lone stage needs the caller's workspace
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
     for entry in (lib.kda_fwd_intra, lib.kda_fwd_scan):

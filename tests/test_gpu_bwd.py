@@ -97,6 +97,11 @@ def test_bwd_matches_oracle(B, T, Hq, Hv, h0, dhT, beta_dtype):
     _say(f"kda_bwd B={B} T={T} Hq={Hq} Hv={Hv} h0={h0} dhT={dhT} beta={beta_dtype}")
     got = _gpu_grads(x)
     _compare(got, _oracle(x), f"B{B} T{T}")
+    # and against autograd through the token recurrence itself (no chunk structure)
+    Bv, Hvv = x["v"].shape[0], x["v"].shape[2]
+    h0 = x["h0"] if x["h0"] is not None else torch.zeros(Bv, Hvv, 128, 128)
+    rec = og.grads(x["q"], x["k"], x["v"], x["g"], x["beta"], SCALE, h0, x["do"], x["dhT"])
+    _compare(got, rec, f"B{B} T{T} vs recurrence")
 
 
 def test_bwd_strong_decay():
@@ -143,18 +148,22 @@ def test_bwd_is_reproducible():
 
 
 def test_bwd_full_size_sampled_heads():
-    # the 2 x 8192 token, 64-head batch the forward is measured on; two heads checked
+    # the 2 x 8192 token, 64-head batch the forward is measured on, with its initial
+    # state ~ 0.1 N(0, 1), a random final-state gradient and the initial-state
+    # gradient: 128 chunks of carried state gradient; two heads checked
     B, T, H = 2, 8192, 64
-    x = _case(B, T, H, H, seed=8, h0=False, dhT=False)
-    _say(f"kda_bwd B={B} T={T} H={H}")
-    got = _gpu_grads(x, want_dh0=False)
+    x = _case(B, T, H, H, seed=8, h0=True, dhT=True)
+    _say(f"kda_bwd B={B} T={T} H={H} with h0, dhT and dh0")
+    got = _gpu_grads(x, want_dh0=True)
     heads = [0, 37]
     sub = head_subset(x, heads, H, H)
     sub["do"] = x["do"][:, :, heads]
-    sub["dhT"] = None
+    sub["dhT"] = x["dhT"][:, heads]
     ref = _oracle(sub)
-    for n in ("dq", "dk", "dv", "dg", "dbeta"):
-        err = _rel_per_head(got[n][:, :, heads], ref[n], 2)
+    for n in NAMES:
+        axis = 1 if n == "dh0" else 2
+        g = got[n][:, heads] if n == "dh0" else got[n][:, :, heads]
+        err = _rel_per_head(g, ref[n], axis)
         _say(f"full size {n}: rel frob {err:.2e}")
         assert err <= TOL, (n, err)
         assert np.isfinite(got[n]).all(), n
