@@ -246,6 +246,27 @@ kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
                nullptr, kBoth, stream);
 }
 
+int64_t kda_fwd_noalloc_max_bytes(void) { return kda::NOALLOC_SCRATCH_BYTES; }
+
+kda_status_t kda_fwd_noalloc(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                             const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                             const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                             const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream) {
+    // Every host check first (as kda_fwd_ws), then the size limit; only then is the
+    // device touched, to look up the scratch address.
+    kda::KdaParams p;
+    int64_t B, T, N;
+    kda_status_t st = prepare(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, p, B, T, N);
+    if (st != KDA_OK) return st;
+    const int64_t need = kda::workspace_bytes(B * T, N, p.Hv);
+    if (need > kda::NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    if (N == 0 || (T == 0 && !final_state)) return KDA_OK;
+    void* ws = nullptr;
+    if (kda::noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, ws,
+               kda::NOALLOC_SCRATCH_BYTES, nullptr, kBoth, stream);
+}
+
 kda_status_t kda_fwd_intra(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                            const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
                            const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
@@ -592,7 +613,8 @@ const char* kda_status_string(kda_status_t s) {
         case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scale must be finite and positive";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
         case KDA_ERR_WORKSPACE:
-            return "KDA_ERR_WORKSPACE: workspace missing, smaller than the entry point's workspace size or misaligned";
+            return "KDA_ERR_WORKSPACE: workspace missing, smaller than the entry point's workspace size or misaligned "
+                   "(kda_fwd_noalloc: the call needs more than its static scratch)";
     }
     return "KDA: unknown status";
 }

@@ -93,6 +93,11 @@ constexpr int BWP_FLOATS = BWP_ABAR + 64 * 64;
 
 hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream);
 
+// Size of the static device scratch behind kda_fwd_noalloc (64 MiB), and its
+// device address on the current device (looked up once per device).
+constexpr int64_t NOALLOC_SCRATCH_BYTES = int64_t(64) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Workspace bytes for the given sizes (one record per chunk slot and value head).
 int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
 

@@ -138,6 +138,28 @@ kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
                         void* workspace, int64_t workspace_size, void* stream);
 
 /*
+ * kda_fwd_noalloc -- kda_fwd_ws without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The records live in a static device array of kda_fwd_noalloc_max_bytes()
+ * bytes (64 MiB) that each GPU the library runs on holds from module load
+ * until the process ends.  A call whose kda_fwd_workspace_size() exceeds it
+ * returns KDA_ERR_WORKSPACE before any HIP call.  Results are bitwise those of
+ * kda_fwd_ws.  Every call on one GPU uses that GPU's array, which keeps the
+ * last call's contents (no call relies on them: every record a call reads it
+ * writes first): calls that overlap on one GPU (two streams or two host
+ * threads) race and must not be made.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) with that device current.
+ */
+kda_status_t kda_fwd_noalloc(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                             const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                             const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                             const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
+/* Size of kda_fwd_noalloc's static scratch per GPU, in bytes. */
+int64_t kda_fwd_noalloc_max_bytes(void);
+
+/*
  * kda_fwd_cp -- kda_fwd for fixed-length batches, with each sequence cut into
  * segments that the scan walks side by side (context parallelism inside one
  * GPU), for batches whose B * Hv is too small to fill the chip.

@@ -57,8 +57,8 @@ def good(B=1, T_=64, Hq=2, Hv=2, beta_dtype=binding.KDA_F32):
 
 
 def call(lib, a, scale=0.088, cu=None, h0=None, hT=None, ws=None, ws_size=None, entry="kda_fwd"):
-    """One forward call: the 11-argument kda_fwd, or, when a workspace size is
-    given, kda_fwd_ws."""
+    """One forward call: the 11-argument kda_fwd (or kda_fwd_noalloc), or, when a
+    workspace size is given, kda_fwd_ws."""
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
     args = (r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale, r(cu), r(h0),
             r(a.get("out")), r(hT))
@@ -186,12 +186,37 @@ def test_dv_slices(lib):
 def test_kda_fwd_has_the_eleven_argument_signature(lib):
     # q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream
     assert len(lib.kda_fwd.argtypes) == 11
+    assert len(lib.kda_fwd_noalloc.argtypes) == 11
     assert len(lib.kda_fwd_ws.argtypes) == 13
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     decl = re.search(r"kda_status_t\s+kda_fwd\s*\((.*?)\);", text, flags=re.S).group(1)
     names = [p.strip().split()[-1].lstrip("*") for p in decl.split(",")]
     assert names == ["q", "k", "v", "g", "beta", "scale", "cu_seqlens", "initial_state", "out", "final_state",
                      "stream"]
+
+
+def test_noalloc_limit_checked_on_the_host(lib):
+    # 64 MiB of static scratch: a call whose workspace would exceed it is refused
+    # before any HIP call; the tensor checks come first
+    cap = lib.kda_fwd_noalloc_max_bytes()
+    assert cap == 64 << 20
+    rec = 61952
+    assert lib.kda_fwd_workspace_size(2 * 8192, 2, 64) > cap
+    a = good(B=2, T_=8192, Hq=64, Hv=64)
+    expect(lib, a, "KDA_ERR_WORKSPACE", entry="kda_fwd_noalloc")
+    # largest fitting: (ceil(T / 64) + 1) * Hv records for one sequence
+    hv = cap // (rec * (128 + 1))
+    assert lib.kda_fwd_workspace_size(8192, 1, hv) <= cap < lib.kda_fwd_workspace_size(8192, 1, hv + 1)
+    b = good(B=1, T_=8192, Hq=hv + 1, Hv=hv + 1)
+    expect(lib, b, "KDA_ERR_WORKSPACE", entry="kda_fwd_noalloc")
+    b["q"] = T([1, 8192, hv + 1, 64])
+    expect(lib, b, "KDA_ERR_UNSUPPORTED", entry="kda_fwd_noalloc")
+    expect(lib, good(), "KDA_ERR_VALUE", scale=-1.0, entry="kda_fwd_noalloc")
+    # an empty problem needs no scratch and no launch
+    c = good(B=1, T_=0)
+    for key in ("q", "k", "v", "g", "beta", "out"):
+        c[key].data = None
+    expect(lib, c, "KDA_OK", entry="kda_fwd_noalloc")
 
 
 def test_trace_requires_descriptor(lib):
