@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("kda_intra.hip", "kda_scan.hip", "kda_compose.hip", "kda_decode.hip", "kda_bwd.hip", "kda_scratch.hip",
+           for f in ("kda_fused.hip", "kda_intra.hip", "kda_scan.hip", "kda_compose.hip", "kda_decode.hip", "kda_bwd.hip", "kda_scratch.hip",
               "kda_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -101,6 +101,10 @@ hipError_t noalloc_scratch(void** out);
 // Workspace bytes for the given sizes (one record per chunk slot and value head).
 int64_t workspace_bytes(int64_t total_tokens, int64_t N, int64_t Hv);
 
+// Fused forward: one work-group per (sequence, value head, 64-wide dv slice),
+// N * Hv * 2 in all; no workspace.
+hipError_t launch_kda_fused(const KdaParams& p, hipStream_t stream);
+
 // Intra-chunk kernel: one work-group per (chunk slot, value head), nslots * Hv in all.
 hipError_t launch_kda_intra(const KdaParams& p, bool trace, hipStream_t stream);
 

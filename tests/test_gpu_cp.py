@@ -74,11 +74,12 @@ def test_segmented_long_sequence():
     check_cp(x, 64, "cp T=65536")
 
 
-def test_two_segments_or_fewer_is_kda_fwd_bitwise():
-    _say("kda_fwd_cp with 2 segments vs kda_fwd, B=2 T=256 H=2")
+def test_two_segments_or_fewer_is_kda_fwd_ws_bitwise():
+    from gated_delta_rule_35_amd import kda_fwd_ws
+    _say("kda_fwd_cp with 2 segments vs kda_fwd_ws, B=2 T=256 H=2")
     x = make_inputs(2, 256, 2, 2, torch.float32, h0=True, seed=202)
     d = to_device(x)
-    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o1, h1 = kda_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
     o2, h2 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 2, initial_state=d["h0"],
                         final_state=True)
     o3, h3 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 1, 3, initial_state=d["h0"],
