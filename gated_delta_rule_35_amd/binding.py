@@ -21,7 +21,7 @@ KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
-EXPORTED = ["kda_fwd", "kda_fwd_ws", "kda_fwd_noalloc", "kda_fwd_noalloc_max_bytes", "kda_fwd_intra",
+EXPORTED = ["kda_fwd", "kda_fwd_fused", "kda_fwd_ws", "kda_fwd_noalloc", "kda_fwd_noalloc_max_bytes", "kda_fwd_intra",
             "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode", "kda_bwd", "kda_fwd_workspace_size",
             "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_bwd_workspace_size", "kda_status_string",
             "kda_dv_slices"]
@@ -60,6 +60,8 @@ def load_library(path=None):
     tp = ctypes.POINTER(KdaTensor)
     lib.kda_fwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_fused.argtypes = lib.kda_fwd.argtypes
+    lib.kda_fwd_fused.restype = ctypes.c_int
     lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_fwd_noalloc_max_bytes.argtypes = []
@@ -165,7 +167,7 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
           entry):
     """One forward entry point.  Entries with a workspace argument (kda_fwd_ws,
     the stage calls, kda_fwd_trace) get `workspace` (None: allocated here);
-    kda_fwd and kda_fwd_noalloc take none."""
+    kda_fwd, kda_fwd_fused and kda_fwd_noalloc take none."""
     lib = load_library()
     tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
     for t in tensors:
@@ -175,7 +177,7 @@ def _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, 
     s = _stream_handle(stream, tensors)
     args = [_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]), float(scale),
             _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8])]
-    if entry in ("kda_fwd", "kda_fwd_noalloc"):
+    if entry in ("kda_fwd", "kda_fwd_fused", "kda_fwd_noalloc"):
         _check(lib, getattr(lib, entry)(*args, s))
         return
     _ws, ws_ptr, ws_size = _workspace(workspace, q, v, cu_seqlens, stream)
@@ -205,6 +207,16 @@ def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=No
     out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
     entry = "kda_fwd" if workspace is None else "kda_fwd_ws"
     _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace, entry)
+    return out, final_state
+
+
+def kda_fwd_fused(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+                  stream=None):
+    """The single-pass forward (C kda_fwd_fused).  Returns (out, final_state); out
+    and final_state=True are allocated here when not given."""
+    out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
+    _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, None,
+          "kda_fwd_fused")
     return out, final_state
 
 

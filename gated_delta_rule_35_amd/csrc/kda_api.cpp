@@ -237,6 +237,20 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
                stream);
 }
 
+kda_status_t kda_fwd_fused(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream) {
+    kda::KdaParams p;
+    int64_t B, T, N;
+    kda_status_t st = prepare(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, p, B, T, N);
+    if (st != KDA_OK) return st;
+    if (N * p.Hv * 2 > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || (T == 0 && !final_state)) return KDA_OK;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_kda_fused(p, hs), hs);
+}
+
 kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                         const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
                         const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,

@@ -112,6 +112,28 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
                      const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
 
 /*
+ * kda_fwd_fused -- the single-pass form of the forward ("cuLA PR #131: SM100/SM103
+ * KDA forward to pure CuTeDSL", Summary: chunk intra, FP32 Akk inversion,
+ * recompute W/U; "cuLA REPO_LAYOUT.md", ops/: chunk delta-H and forward output,
+ * and the fused-forward entries): one persistent work-group per (sequence, value
+ * head, 64-wide dv slice) builds each chunk's operands, Aqk and T in LDS while it
+ * scans the previous chunk, so nothing but q, k, v, g, beta, the states and o
+ * crosses HBM.  Same arguments, checks, results semantics and reproducibility as
+ * kda_fwd, and it allocates nothing (it can be captured into a HIP graph).
+ * Precision: as kda_fwd's, except that the decay anchor is per 64-token chunk:
+ * a chunk whose total decay exceeds exp(-16) on some channel takes an exact fp32
+ * path (Aqk and Akk element by element, operands with every factor <= 1).
+ * It runs N * Hv * 2 work-groups of 512 threads with about 158 KB of LDS each,
+ * one per CU: it is meant for batches with at least that many (sequence, head)
+ * pairs; with fewer, kda_fwd is faster.  More than 2^31 - 1 work-groups return
+ * KDA_ERR_UNSUPPORTED.
+ */
+kda_status_t kda_fwd_fused(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                           const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                           const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                           const kda_tensor_t* out, const kda_tensor_t* final_state, void* stream);
+
+/*
  * kda_fwd_workspace_size -- bytes of device workspace kda_fwd_ws needs for a
  * call with `total_tokens` = B * T tokens, N sequences and Hv value heads:
  * (ceil(total_tokens / 64) + N) * Hv * 61952.  Returns -1 for a negative size.

@@ -1,12 +1,12 @@
-"""The library's launches under HIP graph capture (torch.cuda.graph): kda_fwd_ws,
-kda_fwd_cp, kda_decode and kda_bwd are captured once with caller-owned outputs and
+"""The library's launches under HIP graph capture (torch.cuda.graph): kda_fwd_fused,
+kda_fwd_ws, kda_fwd_cp, kda_decode and kda_bwd are captured once with caller-owned outputs and
 workspaces (nothing is allocated and no memset is recorded), then replayed
 several times with eager work and synchronisation in between; every replay
 must reproduce the eager result bit for bit."""
 import pytest
 import torch
 
-from gated_delta_rule_35_amd import (kda_decode, kda_fwd, kda_fwd_cp, kda_fwd_cp_workspace_size,
+from gated_delta_rule_35_amd import (kda_decode, kda_fwd, kda_fwd_cp, kda_fwd_cp_workspace_size, kda_fwd_fused,
                                      kda_fwd_workspace_size, kda_fwd_ws, load_library)
 from gated_delta_rule_35_amd.inputs import make_inputs
 from tests.kda_check import to_device
@@ -52,14 +52,25 @@ def capture_and_replay(call, outputs, reference):
             assert torch.equal(t.view(bits), ref.view(bits)), f"replay {r}"
 
 
+def test_kda_fwd_fused_in_a_graph():
+    _say("graph: kda_fwd_fused (nothing allocated) B=2 T=300 Hq=2 Hv=4 with h0")
+    x = make_inputs(2, 300, 2, 4, torch.float32, h0=True, seed=302)
+    d = to_device(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE)
+    o_ref, h_ref = kda_fwd_fused(*args, initial_state=d["h0"], final_state=True)
+    out, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    capture_and_replay(lambda: kda_fwd_fused(*args, initial_state=d["h0"], out=out, final_state=hT), (out, hT),
+                       (o_ref, h_ref))
+
+
 def test_kda_fwd_ws_in_a_graph():
     _say("graph: kda_fwd_ws B=2 T=300 Hq=2 Hv=4 with h0")
     x = make_inputs(2, 300, 2, 4, torch.float32, h0=True, seed=300)
     d = to_device(x)
     args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE)
-    o_ref, h_ref = kda_fwd(*args, initial_state=d["h0"], final_state=True)
-    out, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
     ws = torch.empty(kda_fwd_workspace_size(600, 2, 4), dtype=torch.uint8, device="cuda")
+    o_ref, h_ref = kda_fwd_ws(*args, initial_state=d["h0"], final_state=True, workspace=ws)
+    out, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
     capture_and_replay(lambda: kda_fwd_ws(*args, initial_state=d["h0"], out=out, final_state=hT, workspace=ws),
                        (out, hT), (o_ref, h_ref))
 

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gated_delta_rule_35_amd import kda_fwd, kda_fwd_trace, load_library
+from gated_delta_rule_35_amd import kda_fwd, kda_fwd_fused, kda_fwd_trace, load_library
 from gated_delta_rule_35_amd.inputs import WORKLOADS, make_inputs, workload_inputs, cu_from_lengths
 from tests.kda_check import (O_MAX_ABS, O_REL_F, STATE_REL_F, head_subset, rel_frob_per_head, seq_slices,
                              state_rel_frob, to_device)
@@ -21,6 +21,24 @@ def _say(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
+# Every forward test runs on both forms of the forward: kda_fwd (the two-pass
+# kernels) and kda_fwd_fused (the single-pass kernel).  Tests of one form's own
+# machinery (stage traces, workspaces, stage calls) carry the two_pass_only mark.
+ENTRIES = {"kda_fwd": kda_fwd, "kda_fwd_fused": kda_fwd_fused}
+FWD = kda_fwd
+
+
+@pytest.fixture(autouse=True, params=list(ENTRIES))
+def entry(request):
+    global FWD
+    if request.param != "kda_fwd" and request.node.get_closest_marker("two_pass_only"):
+        pytest.skip("a test of the two-pass form's own machinery")
+    FWD = ENTRIES[request.param]
+    _say(f"entry point {request.param}")
+    yield request.param
+    FWD = kda_fwd
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -32,7 +50,7 @@ def _gpu():
 def run_gpu(x, cu=None, scale=SCALE, want_state=True):
     d = to_device(x)
     cu_d = cu.to("cuda") if cu is not None else None
-    o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+    o, hT = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
                     final_state=True if want_state else None)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), (hT.cpu().numpy() if hT is not None else None)
@@ -154,11 +172,12 @@ def test_zero_length_batch_passes_the_state_through():
     assert o.shape == (2, 0, 3, 128)
     assert np.array_equal(hT, x["h0"].numpy())
     d = to_device(x)
-    _, hT0 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, final_state=True)
+    _, hT0 = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, final_state=True)
     torch.cuda.synchronize()
     assert not torch.any(hT0)   # no initial state: a zero final state
 
 
+@pytest.mark.two_pass_only
 def test_stage_intermediates_match_oracle_chunked_form():
     """Stage-by-stage parity (gate cumsum, Aqk, Akk, T, W, U, v_new, chunk states)
     against the oracle's chunked form on a small case with tails."""
@@ -189,7 +208,7 @@ def test_repeat_runs_are_bitwise_identical():
     d = to_device(x)
     outs = []
     for _ in range(3):
-        o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+        o, hT = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
         outs.append((o.view(torch.int16).clone(), hT.view(torch.int32).clone()))
     torch.cuda.synchronize()
     for o, h in outs[1:]:
@@ -200,10 +219,10 @@ def test_gva_equals_repeated_mha_bitwise():
     _say("GVA vs repeated MHA, B=1 Hq=4 Hv=16 T=200")
     x = make_inputs(1, 200, 4, 16, torch.bfloat16, h0=True, seed=41)
     d = to_device(x)
-    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o1, h1 = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
     qr = d["q"].repeat_interleave(4, dim=2).contiguous()
     kr = d["k"].repeat_interleave(4, dim=2).contiguous()
-    o2, h2 = kda_fwd(qr, kr, d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o2, h2 = FWD(qr, kr, d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
@@ -216,11 +235,11 @@ def test_packed_equals_separate_calls_bitwise():
     H = 130
     x = make_inputs(1, int(cu[-1]), H, H, torch.float32, h0=True, N=len(lens), seed=51)
     d = to_device(x)
-    o, hT = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(),
+    o, hT = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(),
                     initial_state=d["h0"], final_state=True)
     for n, s in enumerate(seq_slices(cu)):
         sl = {k: d[k][:, s].contiguous() for k in ("q", "k", "v", "g", "beta")}
-        on, hn = kda_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], SCALE,
+        on, hn = FWD(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], SCALE,
                          initial_state=d["h0"][n:n + 1].contiguous(), final_state=True)
         torch.cuda.synchronize()
         assert torch.equal(on.view(torch.int16), o[:, s].view(torch.int16)), n
@@ -237,7 +256,7 @@ def test_sequence_isolation_and_poisoned_outputs():
     d = to_device(x)
     out = torch.full_like(d["v"], float("nan"))
     hT = torch.full((3, 4, 128, 128), float("nan"), device="cuda")
-    kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(), initial_state=d["h0"],
+    FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(), initial_state=d["h0"],
             out=out, final_state=hT)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.isfinite(hT).all()
@@ -247,7 +266,7 @@ def test_sequence_isolation_and_poisoned_outputs():
         d2[name][:, s1] = float("nan")
     out2 = torch.empty_like(out)
     hT2 = torch.empty_like(hT)
-    kda_fwd(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], SCALE, cu_seqlens=cu.cuda(),
+    FWD(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], SCALE, cu_seqlens=cu.cuda(),
             initial_state=d2["h0"], out=out2, final_state=hT2)
     torch.cuda.synchronize()
     for n, s in enumerate(seq_slices(cu)):
@@ -261,9 +280,9 @@ def test_initial_state_may_alias_final_state():
     _say("aliased initial/final state B=2 H=2 T=100")
     x = make_inputs(2, 100, 2, 2, torch.float32, h0=True, seed=71)
     d = to_device(x)
-    o1, h1 = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
+    o1, h1 = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=d["h0"], final_state=True)
     state = d["h0"].clone()
-    o2, _ = kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=state, final_state=state)
+    o2, _ = FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, initial_state=state, final_state=state)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(h1.view(torch.int32), state.view(torch.int32))
@@ -273,17 +292,17 @@ def test_two_streams_match_serial_runs():
     _say("two streams, B=2 H=64 T=256")
     xa = to_device(make_inputs(2, 256, 64, 64, torch.float32, h0=True, seed=81))
     xb = to_device(make_inputs(2, 256, 64, 64, torch.bfloat16, h0=False, seed=82))
-    ra = kda_fwd(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"], final_state=True)
-    rb = kda_fwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
+    ra = FWD(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"], final_state=True)
+    rb = FWD(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
     torch.cuda.synchronize()
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for _ in range(3):
         with torch.cuda.stream(sa):
-            oa = kda_fwd(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"],
+            oa = FWD(xa["q"], xa["k"], xa["v"], xa["g"], xa["beta"], SCALE, initial_state=xa["h0"],
                          final_state=True)
         with torch.cuda.stream(sb):
-            ob = kda_fwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
+            ob = FWD(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], SCALE, final_state=True)
         outs.append((oa, ob))
     torch.cuda.synchronize()
     for oa, ob in outs:
@@ -293,6 +312,7 @@ def test_two_streams_match_serial_runs():
         assert torch.equal(ob[1].view(torch.int32), rb[1].view(torch.int32))
 
 
+@pytest.mark.two_pass_only
 def test_workspace_choices_are_bitwise_identical():
     """The two-pass form kda_fwd_ws with a fresh workspace, twice, and with an
     oversized dirty one: the same bits."""
@@ -312,6 +332,7 @@ def test_workspace_choices_are_bitwise_identical():
         assert torch.equal(h.view(torch.int32), h1.view(torch.int32))
 
 
+@pytest.mark.two_pass_only
 def test_stage_calls_equal_kda_fwd_ws_bitwise():
     """kda_fwd_intra then kda_fwd_scan = kda_fwd_ws (the two-pass form)."""
     from gated_delta_rule_35_amd import kda_fwd_intra, kda_fwd_scan, kda_fwd_workspace_size, kda_fwd_ws
@@ -380,7 +401,7 @@ def test_full_size_workloads_every_head(name):
     out = torch.full_like(d["v"], float("nan"))
     hT = torch.full((N, w.Hv, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
     _say(f"full workload {name}: kda_fwd into NaN-filled outputs")
-    kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, cu_seqlens=cu_d, initial_state=d["h0"], out=out,
+    FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, cu_seqlens=cu_d, initial_state=d["h0"], out=out,
             final_state=hT)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
@@ -397,6 +418,7 @@ def test_full_size_workloads_every_head(name):
     assert rel <= O_REL_F and mx <= O_MAX_ABS and srel <= STATE_REL_F
 
 
+@pytest.mark.two_pass_only
 @pytest.mark.parametrize("name", ["mha_b2_h64_t8192", "varlen_h64_16k"])
 def test_full_size_two_pass_form_agrees(name):
     """kda_fwd_ws (the two-pass form with a caller workspace) and its two stage
