@@ -42,7 +42,7 @@ MAC_PER_CHUNK_HEAD = 4_512_416
 # The forward kernels' sources and the build script that holds their compiler
 # flags: counters taken on other code than these are not reported.
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_35_amd", "csrc", f)
-                  for f in ("kda_intra.hip", "kda_scan.hip", "kda_device.h", "kda_kernel.h")] + \
+                  for f in ("kda_intra.hip", "kda_scan.hip", "kda_fused.hip", "kda_device.h", "kda_kernel.h")] + \
                  [os.path.join(ROOT, "gated_delta_rule_35_amd", "build.py")]
 RECORD_BYTES = 61952   # workspace record per (chunk, value head)
 # The pages' own time for this exact workload ("cuLA PR #131: SM100/SM103 KDA
@@ -303,7 +303,58 @@ def oracle_cpu_baseline(x, cu, w, N, n_tok, scale, seconds, heads):
            "sample": f"fp64 token recurrence over value heads 0..{len(hs) - 1} of {w.Hv} (all {N} sequences, "
                      f"{n_tok} tokens each head), {reps} runs in {cpu_s:.1f} s, scaled to {w.Hv} heads"}
     log(f"cpu baseline {cpu_tok:.1f} tokens/s on {cpu['cores']} threads ({reps} runs, {cpu_s:.1f} s)")
+    # the same oracle on one OpenMP thread (value head 0 only, for about a quarter
+    # of the time), and the host CPU's model name
+    one = one_thread_oracle(sub, cu, w, N, n_tok, scale, max(seconds / 4, 2.0))
+    if one is not None:
+        cpu["one_thread"] = one
+    cpu["cpu_model"] = cpu_model_name()
     return cpu
+
+
+def cpu_model_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def one_thread_oracle(sub, cu, w, N, n_tok, scale, seconds):
+    """tokens/s of the oracle on one OpenMP thread over value head 0 (scaled to all
+    heads), or None when the OpenMP runtime cannot be reached."""
+    import ctypes
+    import numpy as np
+    import oracle
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    before = oracle.threads()
+    # value head 0 and its q/k head (index 0 of each head axis)
+    one = {k: (np.ascontiguousarray(v[:, :, 0:1]) if v is not None else None) for k, v in sub.items() if k != "h0"}
+    one["h0"] = np.ascontiguousarray(sub["h0"][:, 0:1]) if sub.get("h0") is not None else None
+    gomp.omp_set_num_threads(1)
+    try:
+        if oracle.threads() != 1:
+            return None
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.recurrence(one["q"], one["k"], one["v"], one["g"], one["beta"], scale, cu_seqlens=cu,
+                              h0=one["h0"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        gomp.omp_set_num_threads(before)
+    tok = n_tok / w.Hv * reps / el
+    log(f"cpu baseline, one thread: {tok:.1f} tokens/s ({reps} runs of value head 0, {el:.1f} s)")
+    return {"value": round(tok, 1), "unit": "tokens/s", "cores": 1,
+            "sample": f"value head 0 of {w.Hv} (all {N} sequences), {reps} runs in {el:.1f} s, scaled to {w.Hv} heads"}
 
 
 def bench_cp(args):
@@ -513,6 +564,24 @@ def main():
     t_call11 = sum(call11) / len(call11) / 1e3
     log(f"kda_fwd (11 arguments) avg {t_call11 * 1e3:.4f} ms per call")
 
+    # kda_fwd_fused, the single-pass kernel, on the same inputs (HIP events around
+    # each call: one launch of kda_fused_kernel)
+    from gated_delta_rule_35_amd import kda_fwd_fused
+    for _ in range(2):
+        kda_fwd_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                      out=out, final_state=hT)
+    torch.cuda.synchronize()
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evf:
+        e[0].record(stream)
+        kda_fwd_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                      out=out, final_state=hT)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    callf = [e[0].elapsed_time(e[1]) for e in evf]
+    t_fused = sum(callf) / len(callf) / 1e3
+    log(f"kda_fwd_fused avg {t_fused * 1e3:.4f} ms per call (min {min(callf):.4f})")
+
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
     n_ch = chunk_heads(lengths, w.Hv)
@@ -533,6 +602,12 @@ def main():
                 "scope": "whole forward: algorithmic bytes of the forward over the summed average durations of "
                          "kda_intra_kernel and kda_scan_kernel",
                 "kernels": kernels}
+    fused_gbs = nbytes / t_fused / 1e9
+    fused = {"ms_avg": round(t_fused * 1e3, 5), "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+             "traffic": traffic.get("kda_fused_kernel") if traffic else None,
+             "scope": "kda_fwd_fused (one launch of kda_fused_kernel): algorithmic bytes of the forward over its "
+                      "average duration; not the headline path (kda_fwd runs the two-pass kernels)"}
     mfma = {"achieved": round(flops / t_kern / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(flops / t_kern / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "algorithmic_flop_per_launch": flops}
@@ -566,6 +641,7 @@ def main():
         "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
         "algorithmic_bytes_per_step": nbytes,
         "roofline": roofline,
+        "fused": fused,
         "mfma": mfma,
         "cpu_baseline": cpu,
     }
