@@ -493,11 +493,18 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     const float* ds = p.dhs + x.ch * BW_STATE;
     // element (i, c) accumulators: c = tid % 128, rows i = 16 rg + r
     const int c = tid & 127, rg = tid >> 7, i0 = 16 * rg;
-    // 64 x 64 accumulators: row ai = tid / 8, columns 8 aj .. + 7
+    // 64 x 64 tiles in phase B: row ai = tid / 8, columns 8 aj .. + 7
     const int ai = tid >> 3, aj = (tid & 7) * 8;
-    float aQ[16], aKG[16], aKH[16], aAQ[8], aTB[8], dgam = 0.f;
-    for (int r = 0; r < 16; ++r) aQ[r] = aKG[r] = aKH[r] = 0.f;
-    for (int s = 0; s < 8; ++s) aAQ[s] = aTB[s] = 0.f;
+    // The operand gradients summed over the value columns, on v_mfma_f32_16x16x4f32:
+    // wave w holds the 16x16 tiles (it, ct) of d(qg), -d(kg) and d(kh) (64 x 128) for
+    // token tile it = w % 4 and channel tiles ct = 4 (w / 4) .. + 3, and the tiles
+    // (it, jt) of dAqk and dTb (64 x 64) for jt = 2 (w / 4), + 1.  A tile's lane l
+    // holds rows 4 (l / 16) + r of column l % 16.
+    const int lane = tid & 63, wv = tid >> 6, it = wv & 3, chh = wv >> 2;
+    f32x4 accQ[4], accKG[4], accKH[4], accAQ[2], accTB[2];
+    for (int t = 0; t < 4; ++t) accQ[t] = accKG[t] = accKH[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) accAQ[t] = accTB[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgam = 0.f;
 
     load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, nullptr, tid, 512, GLD);
     {
@@ -508,7 +515,6 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
             F[GA_TB + (e >> 6) * GMD + j] = pr[BWP_T + e] * bj;
         }
     }
-    const int zn = tid & 15, zi = tid >> 4;   // rows zi and zi + 32, column zn
     // a slice's inputs for thread t: h and dh' elements t + 512 u (u < 4) of the
     // [128][16] slice, do and v elements t + 512 u (u < 2) of the [64][16] slice;
     // the next slice's are fetched while this one computes
@@ -543,84 +549,139 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
         }
         if (sl + 1 < GNSL) fetch(n0 + GSL);
         __syncthreads();
-        {   // Z = v - kg h;  dv_new = Aqk^T do + kh dh'
-            float z0 = F[GA_V + zn * GTS + zi], z1 = F[GA_V + zn * GTS + zi + 32], u0 = 0.f, u1 = 0.f;
-#pragma unroll 2
-            for (int cc = 0; cc < BW_D; cc += 4) {
-                const f32x4 g0 = lds4(F + GA_KG + zi * GLD + cc), g1 = lds4(F + GA_KG + (zi + 32) * GLD + cc);
-                const f32x4 k0 = lds4(F + GA_KH + zi * GLD + cc), k1 = lds4(F + GA_KH + (zi + 32) * GLD + cc);
-                for (int e = 0; e < 4; ++e) {
-                    const float h = F[GA_H + (cc + e) * GSD + zn], d = F[GA_DH + (cc + e) * GSD + zn];
-                    z0 -= g0[e] * h;
-                    z1 -= g1[e] * h;
-                    u0 += k0[e] * d;
-                    u1 += k1[e] * d;
+        {
+            // Z = v - kg h (waves 0..3) and dv_new = kh dh' + Aqk^T do (waves 4..7), token
+            // tile it of the slice each.  MFMA b of k block u sums the index
+            // 16 u + 4 (lane / 16) + b, so a lane reads four consecutive channels (or
+            // tokens) of its row with one 16-byte load.
+            const int m4 = 4 * (lane >> 4), rl = lane & 15, ti = 16 * it + rl;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (chh == 0) {
+#pragma unroll 4
+                for (int u = 0; u < BW_D / 16; ++u) {
+                    const int cc = 16 * u + m4;
+                    const f32x4 a4 = lds4(F + GA_KG + ti * GLD + cc);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[b], F[GA_H + (cc + b) * GSD + rl], acc, 0, 0, 0);
                 }
-            }
-            // Aqk is zero above the diagonal, so the sums may start at a multiple of 4
-            for (int m = zi & ~3; m < BW_C; m += 4) {
-                const f32x4 o4 = lds4(F + GA_DO + zn * GTS + m);
-                for (int e = 0; e < 4; ++e) {
-                    u0 += F[GA_AQ + (m + e) * BW_MD + zi] * o4[e];
-                    if (m >= 32) u1 += F[GA_AQ + (m + e) * BW_MD + zi + 32] * o4[e];
+                const f32x4 v4 = lds4(F + GA_V + rl * GTS + 16 * it + m4);
+                *reinterpret_cast<f32x4*>(F + GA_Z + rl * GTS + 16 * it + m4) = v4 - acc;
+            } else {
+#pragma unroll 4
+                for (int u = 0; u < BW_D / 16; ++u) {
+                    const int cc = 16 * u + m4;
+                    const f32x4 a4 = lds4(F + GA_KH + ti * GLD + cc);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[b], F[GA_DH + (cc + b) * GSD + rl], acc, 0, 0, 0);
                 }
+                // Aqk[m][i] is zero for m < i: token blocks u >= it
+                for (int u = it; u < BW_C / 16; ++u) {
+                    const int mm = 16 * u + m4;
+                    const f32x4 b4 = lds4(F + GA_DO + rl * GTS + mm);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(F[GA_AQ + (mm + b) * BW_MD + ti], b4[b], acc, 0, 0, 0);
+                }
+                *reinterpret_cast<f32x4*>(F + GA_DVN + rl * GTS + 16 * it + m4) = acc;
             }
-            F[GA_Z + zn * GTS + zi] = z0;
-            F[GA_Z + zn * GTS + zi + 32] = z1;
-            F[GA_DVN + zn * GTS + zi] = u0;
-            F[GA_DVN + zn * GTS + zi + 32] = u1;
         }
         __syncthreads();
-        for (int r = 0; r < 2; ++r) {   // v_new = Tb Z;  dZ = Tb^T dv_new = dv
-            const int i = zi + 32 * r;
-            float vn = 0.f, dz = 0.f;
-            // Tb is zero above the diagonal: whole groups of 4 cover the triangle
-            for (int j = 0; j <= i; j += 4) {
-                const f32x4 t4 = lds4(F + GA_TB + i * GMD + j), z4 = lds4(F + GA_Z + zn * GTS + j);
-                vn += t4[0] * z4[0] + t4[1] * z4[1] + t4[2] * z4[2] + t4[3] * z4[3];
-            }
-            for (int m = i & ~3; m < BW_C; m += 4) {
-                const f32x4 d4 = lds4(F + GA_DVN + zn * GTS + m);
-                for (int e = 0; e < 4; ++e) dz += F[GA_TB + (m + e) * GMD + i] * d4[e];
-            }
-            F[GA_VN + zn * GTS + i] = vn;
-            F[GA_DZ + zn * GTS + i] = dz;
-            if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + zn] = dz;
-        }
-        __syncthreads();
-#pragma unroll 1
-        for (int n = 0; n < GSL; ++n) {
-            const float h = F[GA_H + c * GSD + n], dhv = F[GA_DH + c * GSD + n];
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 o4 = lds4(F + GA_DO + n * GTS + i0 + 4 * q4);
-                const f32x4 z4 = lds4(F + GA_DZ + n * GTS + i0 + 4 * q4);
-                const f32x4 v4 = lds4(F + GA_VN + n * GTS + i0 + 4 * q4);
-                for (int e = 0; e < 4; ++e) {
-                    aQ[4 * q4 + e] += o4[e] * h;
-                    aKG[4 * q4 + e] -= z4[e] * h;
-                    aKH[4 * q4 + e] += v4[e] * dhv;
+        {
+            // v_new = Tb Z (waves 0..3, token tile it) and dZ = Tb^T dv_new = dv (waves
+            // 4..7, token tile it); Tb is lower triangular.
+            const int m4 = 4 * (lane >> 4), rl = lane & 15, ti = 16 * it + rl;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (chh == 0) {
+                for (int u = 0; u <= it; ++u) {
+                    const int jj = 16 * u + m4;
+                    const f32x4 a4 = lds4(F + GA_TB + ti * GMD + jj);
+                    const f32x4 b4 = lds4(F + GA_Z + rl * GTS + jj);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[b], b4[b], acc, 0, 0, 0);
+                }
+                *reinterpret_cast<f32x4*>(F + GA_VN + rl * GTS + 16 * it + m4) = acc;
+            } else {
+                for (int u = it; u < BW_C / 16; ++u) {
+                    const int mm = 16 * u + m4;
+                    const f32x4 b4 = lds4(F + GA_DVN + rl * GTS + mm);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(F[GA_TB + (mm + b) * GMD + ti], b4[b], acc, 0, 0, 0);
+                }
+                *reinterpret_cast<f32x4*>(F + GA_DZ + rl * GTS + 16 * it + m4) = acc;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + m4 + r;
+                    if (i < x.len) p.dv[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + rl] = acc[r];
                 }
             }
-            if (rg == 0) dgam += dhv * h;
-            const float oa = F[GA_DO + n * GTS + ai], va = F[GA_DVN + n * GTS + ai];
-            const f32x4 vA = lds4(F + GA_VN + n * GTS + aj), vB = lds4(F + GA_VN + n * GTS + aj + 4);
-            const f32x4 zA = lds4(F + GA_Z + n * GTS + aj), zB = lds4(F + GA_Z + n * GTS + aj + 4);
-            for (int e = 0; e < 4; ++e) {
-                aAQ[e] += oa * vA[e];
-                aAQ[4 + e] += oa * vB[e];
-                aTB[e] += va * zA[e];
-                aTB[4 + e] += va * zB[e];
+        }
+        __syncthreads();
+        if (rg == 0) {
+            for (int n = 0; n < GSL; ++n) dgam += F[GA_DH + c * GSD + n] * F[GA_H + c * GSD + n];
+        }
+        {
+            // Rank-16 updates of the slice: MFMA b of a k step sums the columns n = 4 m + b
+            // (m = lane / 16 supplies n); A rows are tokens 16 it + lane % 16, B columns
+            // channels (or tokens) 16 ct + lane % 16.
+            const int m4 = 4 * (lane >> 4), rl = lane & 15, ti = 16 * it + rl;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int n = m4 + b;
+                const float ado = F[GA_DO + n * GTS + ti], adz = F[GA_DZ + n * GTS + ti];
+                const float avn = F[GA_VN + n * GTS + ti], advn = F[GA_DVN + n * GTS + ti];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int cc = 16 * (4 * chh + t) + rl;
+                    const float bh = F[GA_H + cc * GSD + n], bdh = F[GA_DH + cc * GSD + n];
+                    accQ[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ado, bh, accQ[t], 0, 0, 0);
+                    accKG[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(adz, bh, accKG[t], 0, 0, 0);
+                    accKH[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(avn, bdh, accKH[t], 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int tj = 16 * (2 * chh + t) + rl;
+                    accAQ[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ado, F[GA_VN + n * GTS + tj], accAQ[t], 0, 0, 0);
+                    accTB[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(advn, F[GA_Z + n * GTS + tj], accTB[t], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
     }
 
-    // Phase B: dA = lower_strict(-T^T (dTb diag beta) T^T), dbeta, dAbar = diag(beta) dA.
-    for (int s = 0; s < 8; ++s) {
-        const int j = aj + s;
-        F[GB_DTB + ai * BW_MD + j] = aTB[s];
-        F[GC_DAQ + ai * BW_MD + j] = j <= ai ? aAQ[s] : 0.f;
+    // The accumulated tiles to LDS: dTb and the lower triangle of dAqk in their
+    // phase B/C places, d(qg), d(kg), d(kh) ([64][129] each) below them, from where
+    // each thread takes its own elements (rows i0 .. + 15 of channel c).
+    {
+        const int rb = 16 * it + 4 * (lane >> 4), cl = lane & 15;
+        for (int t = 0; t < 4; ++t) {
+            const int cc = 16 * (4 * chh + t) + cl;
+            for (int r = 0; r < 4; ++r) {
+                F[(rb + r) * BW_LD + cc] = accQ[t][r];
+                F[BW_C * BW_LD + (rb + r) * BW_LD + cc] = -accKG[t][r];
+                F[2 * BW_C * BW_LD + (rb + r) * BW_LD + cc] = accKH[t][r];
+            }
+        }
+        for (int t = 0; t < 2; ++t) {
+            const int j = 16 * (2 * chh + t) + cl;
+            for (int r = 0; r < 4; ++r) {
+                F[GB_DTB + (rb + r) * BW_MD + j] = accTB[t][r];
+                F[GC_DAQ + (rb + r) * BW_MD + j] = j <= rb + r ? accAQ[t][r] : 0.f;
+            }
+        }
     }
+    static_assert(3 * BW_C * BW_LD <= GC_DAQ && GC_DAQ + BW_C * BW_MD <= GB_DTB, "accumulator staging");
+    __syncthreads();
+    float aQ[16], aKG[16], aKH[16];
+    for (int r = 0; r < 16; ++r) {
+        aQ[r] = F[(i0 + r) * BW_LD + c];
+        aKG[r] = F[BW_C * BW_LD + (i0 + r) * BW_LD + c];
+        aKH[r] = F[2 * BW_C * BW_LD + (i0 + r) * BW_LD + c];
+    }
+    __syncthreads();
+
+    // Phase B: dA = lower_strict(-T^T (dTb diag beta) T^T), dbeta, dAbar = diag(beta) dA.
     for (int e = tid; e < BW_C * BW_C; e += 512) {
         F[GB_T + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_T + e];
         F[GB_AB + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_ABAR + e];
