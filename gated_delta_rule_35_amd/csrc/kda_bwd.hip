@@ -736,34 +736,114 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     }
     __syncthreads();
     const float Gl = F[GC_G + (BW_C - 1) * BW_LD + c];
-    float oq[16], ok[16], oG[16], oP[16];
+    float qi[16], ki[16], Gi[16];
     for (int r = 0; r < 16; ++r) {
-        const int i = i0 + r;
-        const float Gi = F[GC_G + i * BW_LD + c], qi = F[GC_Q + i * BW_LD + c], ki = F[GC_K + i * BW_LD + c];
-        float Rq = 0.f, Rk = 0.f, Cq = 0.f, Ck = 0.f;
-        for (int j = 0; j <= i; ++j) {
-            const float kE = F[GC_K + j * BW_LD + c] * fexp(Gi - F[GC_G + j * BW_LD + c]);
-            Rq += F[GC_DAQ + i * BW_MD + j] * kE;
-            Rk += F[GC_DAB + i * BW_MD + j] * kE;   // zero on the diagonal
-        }
-        for (int m = i; m < BW_C; ++m) {
-            const float E = fexp(F[GC_G + m * BW_LD + c] - Gi);
-            Cq += F[GC_DAQ + m * BW_MD + i] * F[GC_Q + m * BW_LD + c] * E;
-            Ck += F[GC_DAB + m * BW_MD + i] * F[GC_K + m * BW_LD + c] * E;
-        }
-        const float eG = fexp(Gi), eH = fexp(Gl - Gi);
-        oq[r] = p.scale * (aQ[r] * eG + Rq);
-        ok[r] = aKG[r] * eG + aKH[r] * eH + p.scale * Cq + Ck + Rk;
-        oP[r] = aKH[r] * ki * eH;
-        oG[r] = p.scale * qi * Rq + ki * Rk - p.scale * ki * Cq - ki * Ck + aKG[r] * ki * eG +
-                p.scale * aQ[r] * qi * eG - oP[r];
+        Gi[r] = F[GC_G + (i0 + r) * BW_LD + c];
+        qi[r] = F[GC_Q + (i0 + r) * BW_LD + c];
+        ki[r] = F[GC_K + (i0 + r) * BW_LD + c];
     }
-    for (int r = 0; r < 16; ++r) {
+    // The pairwise sums, per element (i, c):
+    //   Rq = sum_{j<=i} dAqk[i][j] k_j e^{G_i - G_j},  Rk = the same with dAbar,
+    //   Cq = sum_{m>=i} dAqk[m][i] q_m e^{G_m - G_i},  Ck = sum_{m>=i} dAbar[m][i] k_m e^{G_m - G_i}.
+    float oG[16], oP[16];
+    auto finish = [&](int r, float Rq, float Rk, float Cq, float Ck) {
         const int i = i0 + r;
+        const float eG = fexp(Gi[r]), eH = fexp(Gl - Gi[r]);
+        const float oq = p.scale * (aQ[r] * eG + Rq);
+        const float ok = aKG[r] * eG + aKH[r] * eH + p.scale * Cq + Ck + Rk;
+        oP[r] = aKH[r] * ki[r] * eH;
+        oG[r] = p.scale * qi[r] * Rq + ki[r] * Rk - p.scale * ki[r] * Cq - ki[r] * Ck + aKG[r] * ki[r] * eG +
+                p.scale * aQ[r] * qi[r] * eG - oP[r];
         if (i < x.len) {
             const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + c;
-            p.dqv[o] = oq[r];
-            p.dkv[o] = ok[r];
+            p.dqv[o] = oq;
+            p.dkv[o] = ok;
+        }
+    };
+    // With the anchor A = G_last / 2 of each channel, e^{G_i - G_j} = e^{G_i - A} e^{A - G_j}
+    // and every factor lies within e^{+-|G_last| / 2}: the four sums become products
+    // of dAqk, dAbar (64 x 64) with k e^{A-G}, q e^{G-A}, k e^{G-A} (64 x 128) on
+    // v_mfma_f32_16x16x4f32, scaled per element.  A chunk that decays by more than
+    // e^-120 on some channel (factors beyond e^60) takes the element-by-element sums.
+    const bool far = __syncthreads_or(rg == 0 && !(Gl >= -120.f)) != 0;
+    if (!far) {
+        const float A = 0.5f * Gl;
+        for (int r = 0; r < 16; ++r) {
+            const float eP = fexp(Gi[r] - A), eM = fexp(A - Gi[r]);
+            F[GC_Q + (i0 + r) * BW_LD + c] = qi[r] * eP;   // q e^{G-A}
+            F[GC_K + (i0 + r) * BW_LD + c] = ki[r] * eM;   // k e^{A-G}
+            F[GC_G + (i0 + r) * BW_LD + c] = ki[r] * eP;   // k e^{G-A}
+        }
+        __syncthreads();
+        f32x4 P1[4], P2[4], P3[4], P4[4];
+        for (int t = 0; t < 4; ++t) P1[t] = P2[t] = P3[t] = P4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            // wave (it, chh): token tile it, channel tiles 4 chh .. + 3; MFMA b of block u
+            // sums the index 16 u + 4 (lane / 16) + b
+            const int m4 = 4 * (lane >> 4), rl = lane & 15, ti = 16 * it + rl;
+            for (int u = 0; u <= it; ++u) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int j = 16 * u + m4 + b;
+                    const float a1 = F[GC_DAQ + ti * BW_MD + j], a2 = F[GC_DAB + ti * BW_MD + j];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float kb = F[GC_K + j * BW_LD + 16 * (4 * chh + t) + rl];
+                        P1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, kb, P1[t], 0, 0, 0);
+                        P2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, kb, P2[t], 0, 0, 0);
+                    }
+                }
+            }
+            for (int u = it; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int m = 16 * u + m4 + b;
+                    const float a3 = F[GC_DAQ + m * BW_MD + ti], a4 = F[GC_DAB + m * BW_MD + ti];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int cq = 16 * (4 * chh + t) + rl;
+                        P3[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, F[GC_Q + m * BW_LD + cq], P3[t], 0, 0, 0);
+                        P4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4, F[GC_G + m * BW_LD + cq], P4[t], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();   // operands read: the four products go to LDS ([4][64][129])
+        static_assert(4 * BW_C * BW_LD <= GC_END, "pairwise staging");
+        {
+            const int rb = 16 * it + 4 * (lane >> 4), cl = lane & 15;
+            for (int t = 0; t < 4; ++t) {
+                const int cc = 16 * (4 * chh + t) + cl;
+                for (int r = 0; r < 4; ++r) {
+                    const int o = (rb + r) * BW_LD + cc;
+                    F[o] = P1[t][r];
+                    F[BW_C * BW_LD + o] = P2[t][r];
+                    F[2 * BW_C * BW_LD + o] = P3[t][r];
+                    F[3 * BW_C * BW_LD + o] = P4[t][r];
+                }
+            }
+        }
+        __syncthreads();
+        for (int r = 0; r < 16; ++r) {
+            const int o = (i0 + r) * BW_LD + c;
+            const float eP = fexp(Gi[r] - A), eM = fexp(A - Gi[r]);
+            finish(r, F[o] * eP, F[BW_C * BW_LD + o] * eP, F[2 * BW_C * BW_LD + o] * eM, F[3 * BW_C * BW_LD + o] * eM);
+        }
+    } else {
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + r;
+            float Rq = 0.f, Rk = 0.f, Cq = 0.f, Ck = 0.f;
+            for (int j = 0; j <= i; ++j) {
+                const float kE = F[GC_K + j * BW_LD + c] * fexp(Gi[r] - F[GC_G + j * BW_LD + c]);
+                Rq += F[GC_DAQ + i * BW_MD + j] * kE;
+                Rk += F[GC_DAB + i * BW_MD + j] * kE;   // zero on the diagonal
+            }
+            for (int m = i; m < BW_C; ++m) {
+                const float E = fexp(F[GC_G + m * BW_LD + c] - Gi[r]);
+                Cq += F[GC_DAQ + m * BW_MD + i] * F[GC_Q + m * BW_LD + c] * E;
+                Ck += F[GC_DAB + m * BW_MD + i] * F[GC_K + m * BW_LD + c] * E;
+            }
+            finish(r, Rq, Rk, Cq, Ck);
         }
     }
     __syncthreads();   // q and k are no longer read: reuse them for dG and the kh terms
