@@ -374,26 +374,37 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
     __shared__ __attribute__((aligned(16))) float sDO[BW_C * BW_SD];
     __shared__ __attribute__((aligned(16))) float sDVN[BW_C * BW_SD];
     __shared__ __attribute__((aligned(16))) float sDZ[BW_C * BW_SD];
+    __shared__ float sGam[BW_D];
     const int tid = threadIdx.x;
     const int slice = blockIdx.x % BW_NSL;
     const int64_t bh = blockIdx.x / BW_NSL;
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
-    const int c = tid & 127, nb = (tid >> 7) * 8;
-    float dh[8];
-    for (int e = 0; e < 8; ++e)
-        dh[e] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
-    const int zn = tid & 31, zi = tid >> 5;
+    const int c = tid & 127;
+    // The chunk products on v_mfma_f32_16x16x4f32.  Wave (it, nt) = (w % 4, w / 4):
+    // value columns 16 nt .. + 15 of the slice; token tile it of dv_new and dZ; state
+    // tiles (channels) 2 it and 2 it + 1 of dh, kept in accumulators for the whole
+    // walk.  A tile's lane l holds rows 4 (l / 16) + r of column l % 16, and MFMA b
+    // of a 16-wide k block u sums the index 16 u + 4 (l / 16) + b.
+    const int lane = tid & 63, wv = tid >> 6, it = wv & 3, nt = wv >> 2;
+    const int m4 = 4 * (lane >> 4), rl = lane & 15, col = 16 * nt + rl;
+    f32x4 dh[2];
+    for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < 4; ++r)
+            dh[t][r] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + (32 * it + 16 * t + m4 + r) * BW_D + n0 + col]
+                             : 0.f;
     DstateRaw raw;
     if (p.nc > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + p.nc - 1) * p.Hv + hv), tid, n0, raw);
 #pragma unroll 1
     for (int ci = p.nc - 1; ci >= 0; --ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
-        float* ds = p.dhs + x.ch * BW_STATE + c * BW_D + n0 + nb;
-        for (int e = 0; e < 8; ++e) {
-            ds[e] = dh[e];
-            sDH[c * BW_SD + nb + e] = dh[e];
-        }
+        float* ds = p.dhs + x.ch * BW_STATE + n0 + col;
+        for (int t = 0; t < 2; ++t)
+            for (int r = 0; r < 4; ++r) {
+                const int cc = 32 * it + 16 * t + m4 + r;
+                ds[cc * BW_D] = dh[t][r];
+                sDH[cc * BW_SD + col] = dh[t][r];
+            }
         // this chunk's operands, from the registers fetched during the previous step
         for (int u = 0; u < 16; ++u) {
             const int i = (tid + BW_ST * u) >> 7;
@@ -410,55 +421,64 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
             const int e = tid + BW_ST * u;
             sDO[(e >> 5) * BW_SD + (e & 31)] = raw.dO[u];
         }
-        const float gam = fexp(raw.Gl);
+        if (tid < BW_D) sGam[tid] = fexp(raw.Gl);
         __syncthreads();
-        {   // dv_new = Aqk^T do + kh dh'
-            float u4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int cc = 0; cc < BW_D; cc += 4) {
-                const float d0 = sDH[cc * BW_SD + zn], d1 = sDH[(cc + 1) * BW_SD + zn];
-                const float d2 = sDH[(cc + 2) * BW_SD + zn], d3 = sDH[(cc + 3) * BW_SD + zn];
-                for (int r = 0; r < 4; ++r) {
-                    const f32x4 k4 = lds4(sKQ + (zi + 16 * r) * GLD + cc);
-                    u4[r] += k4[0] * d0 + k4[1] * d1 + k4[2] * d2 + k4[3] * d3;
+        {   // dv_new = kh dh' + Aqk^T do (Aqk[m][i] is zero for m < i)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int ti = 16 * it + rl;
+#pragma unroll 4
+            for (int u = 0; u < BW_D / 16; ++u) {
+                const f32x4 a4 = lds4(sKQ + ti * GLD + 16 * u + m4);
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[bb], sDH[(16 * u + m4 + bb) * BW_SD + col], acc, 0, 0, 0);
+            }
+            for (int u = it; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int m = 16 * u + m4 + bb;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sAQ[m * BW_MD + ti], sDO[m * BW_SD + col], acc, 0, 0, 0);
                 }
             }
-            for (int m = zi; m < BW_C; ++m) {
-                const float o = sDO[m * BW_SD + zn];
-                for (int r = 0; r < 4; ++r)
-                    if (zi + 16 * r <= m) u4[r] += sAQ[m * BW_MD + zi + 16 * r] * o;
-            }
-            for (int r = 0; r < 4; ++r) sDVN[(zi + 16 * r) * BW_SD + zn] = u4[r];
+            for (int r = 0; r < 4; ++r) sDVN[(16 * it + m4 + r) * BW_SD + col] = acc[r];
         }
         __syncthreads();
         for (int u = 0; u < 16; ++u)   // kh is done with: qg replaces it
             sKQ[((tid + BW_ST * u) >> 7) * GLD + c] = p.scale * bf2f(raw.q[u]) * fexp(raw.G[u]);
         if (ci > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci - 1) * p.Hv + hv), tid, n0, raw);
-        {   // dZ = Tb^T dv_new
-            float z[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int m = zi; m < BW_C; ++m) {
-                const float d = sDVN[m * BW_SD + zn];
-                for (int r = 0; r < 4; ++r)
-                    if (zi + 16 * r <= m) z[r] += sTB[m * BW_MD + zi + 16 * r] * d;
+        {   // dZ = Tb^T dv_new (Tb[i][j] is zero for i < j)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int tj = 16 * it + rl;
+            for (int u = it; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int i = 16 * u + m4 + bb;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sTB[i * BW_MD + tj], sDVN[i * BW_SD + col], acc, 0, 0, 0);
+                }
             }
-            for (int r = 0; r < 4; ++r) sDZ[(zi + 16 * r) * BW_SD + zn] = z[r];
+            for (int r = 0; r < 4; ++r) sDZ[(16 * it + m4 + r) * BW_SD + col] = acc[r];
         }
         __syncthreads();
-        for (int e = 0; e < 8; ++e) dh[e] *= gam;
+        // dh = gam dh' + qg^T do - kg^T dZ
+        for (int t = 0; t < 2; ++t) {
+            const int cb = 32 * it + 16 * t;
+            for (int r = 0; r < 4; ++r) dh[t][r] *= sGam[cb + m4 + r];
 #pragma unroll 2
-        for (int i = 0; i < BW_C; ++i) {   // dh = gam dh' + qg^T do - kg^T dZ
-            const float q1 = sKQ[i * GLD + c], k1 = sKG[i * GLD + c];
-            const f32x4 o0 = lds4(sDO + i * BW_SD + nb), o1 = lds4(sDO + i * BW_SD + nb + 4);
-            const f32x4 z0 = lds4(sDZ + i * BW_SD + nb), z1 = lds4(sDZ + i * BW_SD + nb + 4);
-            for (int e = 0; e < 4; ++e) {
-                dh[e] += q1 * o0[e] - k1 * z0[e];
-                dh[4 + e] += q1 * o1[e] - k1 * z1[e];
+            for (int u = 0; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int m = 16 * u + m4 + bb;
+                    dh[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKQ[m * GLD + cb + rl], sDO[m * BW_SD + col], dh[t], 0, 0, 0);
+                    dh[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(-sKG[m * GLD + cb + rl], sDZ[m * BW_SD + col], dh[t], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
     }
     if (p.dh0)
-        for (int e = 0; e < 8; ++e) p.dh0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] = dh[e];
+        for (int t = 0; t < 2; ++t)
+            for (int r = 0; r < 4; ++r)
+                p.dh0[((int64_t)b * p.Hv + hv) * BW_STATE + (32 * it + 16 * t + m4 + r) * BW_D + n0 + col] = dh[t][r];
 }
 
 // ---------------------------------------------------------------- grad
