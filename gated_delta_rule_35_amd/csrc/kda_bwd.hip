@@ -254,26 +254,36 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
     __shared__ __attribute__((aligned(16))) float sV[BW_C * BW_SD];
     __shared__ __attribute__((aligned(16))) float sZ[BW_C * BW_SD];
     __shared__ __attribute__((aligned(16))) float sVN[BW_C * BW_SD];
+    __shared__ float sGam[BW_D];
     const int tid = threadIdx.x;
     const int slice = blockIdx.x % BW_NSL;
     const int64_t bh = blockIdx.x / BW_NSL;
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
-    const int c = tid & 127, nb = (tid >> 7) * 8;
-    float S[8];
-    for (int e = 0; e < 8; ++e)
-        S[e] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + c * BW_D + n0 + nb + e] : 0.f;
-    const int zn = tid & 31, zi = tid >> 5;
+    const int c = tid & 127;
+    // The chunk products on v_mfma_f32_16x16x4f32, with the tiles of the reverse walk:
+    // wave (it, nt) = (w % 4, w / 4) takes value columns 16 nt .. + 15 of the slice,
+    // token tile it of Z and v_new, and state tiles (channels) 2 it, 2 it + 1 of h,
+    // kept in accumulators for the whole walk.
+    const int lane = tid & 63, wv = tid >> 6, it = wv & 3, nt = wv >> 2;
+    const int m4 = 4 * (lane >> 4), rl = lane & 15, col = 16 * nt + rl;
+    f32x4 S[2];
+    for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < 4; ++r)
+            S[t][r] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + (32 * it + 16 * t + m4 + r) * BW_D + n0 + col]
+                           : 0.f;
     StatesRaw raw;
     if (p.nc > 1) states_fetch(p, chunk_of(p, (int64_t)b * p.nc * p.Hv + hv), tid, n0, raw);
 #pragma unroll 1
     for (int ci = 0; ci < p.nc; ++ci) {
         const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
-        float* hs = p.hs + x.ch * BW_STATE + c * BW_D + n0 + nb;
-        for (int e = 0; e < 8; ++e) {
-            hs[e] = S[e];
-            sS[c * BW_SD + nb + e] = S[e];
-        }
+        float* hs = p.hs + x.ch * BW_STATE + n0 + col;
+        for (int t = 0; t < 2; ++t)
+            for (int r = 0; r < 4; ++r) {
+                const int cc = 32 * it + 16 * t + m4 + r;
+                hs[cc * BW_D] = S[t][r];
+                sS[cc * BW_SD + col] = S[t][r];
+            }
         if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
         for (int u = 0; u < 16; ++u) {
             const int i = (tid + BW_ST * u) >> 7;
@@ -289,39 +299,49 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
             const int e = tid + BW_ST * u;
             sV[(e >> 5) * BW_SD + (e & 31)] = raw.v[u];
         }
-        const float gam = fexp(raw.Gl);
+        if (tid < BW_D) sGam[tid] = fexp(raw.Gl);
         if (ci + 1 < p.nc - 1) states_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci + 1) * p.Hv + hv), tid, n0, raw);
         __syncthreads();
         {   // Z = v - kg h
-            float z[4];
-            for (int r = 0; r < 4; ++r) z[r] = sV[(zi + 16 * r) * BW_SD + zn];
-#pragma unroll 2
-            for (int cc = 0; cc < BW_D; cc += 4) {
-                const float h0 = sS[cc * BW_SD + zn], h1 = sS[(cc + 1) * BW_SD + zn];
-                const float h2 = sS[(cc + 2) * BW_SD + zn], h3 = sS[(cc + 3) * BW_SD + zn];
-                for (int r = 0; r < 4; ++r) {
-                    const f32x4 g4 = lds4(sKG + (zi + 16 * r) * GLD + cc);
-                    z[r] -= g4[0] * h0 + g4[1] * h1 + g4[2] * h2 + g4[3] * h3;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int ti = 16 * it + rl;
+#pragma unroll 4
+            for (int u = 0; u < BW_D / 16; ++u) {
+                const f32x4 a4 = lds4(sKG + ti * GLD + 16 * u + m4);
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[bb], sS[(16 * u + m4 + bb) * BW_SD + col], acc, 0, 0, 0);
+            }
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + m4 + r;
+                sZ[i * BW_SD + col] = sV[i * BW_SD + col] - acc[r];
+            }
+        }
+        __syncthreads();
+        {   // v_new = Tb Z (Tb[i][j] is zero for j > i)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int ti = 16 * it + rl;
+            for (int u = 0; u <= it; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int j = 16 * u + m4 + bb;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sTB[ti * BW_MD + j], sZ[j * BW_SD + col], acc, 0, 0, 0);
                 }
             }
-            for (int r = 0; r < 4; ++r) sZ[(zi + 16 * r) * BW_SD + zn] = z[r];
+            for (int r = 0; r < 4; ++r) sVN[(16 * it + m4 + r) * BW_SD + col] = acc[r];
         }
         __syncthreads();
-        for (int r = 0; r < 4; ++r) {   // v_new = Tb Z
-            const int i = zi + 16 * r;
-            float u = 0.f;
-            for (int j = 0; j <= i; ++j) u += sTB[i * BW_MD + j] * sZ[j * BW_SD + zn];
-            sVN[i * BW_SD + zn] = u;
-        }
-        __syncthreads();
-        for (int e = 0; e < 8; ++e) S[e] *= gam;
+        // h' = gam h + kh^T v_new
+        for (int t = 0; t < 2; ++t) {
+            const int cb = 32 * it + 16 * t;
+            for (int r = 0; r < 4; ++r) S[t][r] *= sGam[cb + m4 + r];
 #pragma unroll 2
-        for (int i = 0; i < BW_C; ++i) {   // h' = gam h + kh^T v_new
-            const float kh = sKH[i * GLD + c];
-            const f32x4 a4 = lds4(sVN + i * BW_SD + nb), b4 = lds4(sVN + i * BW_SD + nb + 4);
-            for (int e = 0; e < 4; ++e) {
-                S[e] += kh * a4[e];
-                S[4 + e] += kh * b4[e];
+            for (int u = 0; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int i = 16 * u + m4 + bb;
+                    S[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKH[i * GLD + cb + rl], sVN[i * BW_SD + col], S[t], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
