@@ -139,50 +139,155 @@ __global__ void __launch_bounds__(BW_PT, 2) kda_bwd_prep_kernel(const BwdParams 
     __syncthreads();
     float* pr = p.prep + x.ch * BWP_FLOATS;
     for (int e = tid; e < BW_C * BW_D; e += BW_PT) pr[BWP_G + e] = L.G[(e >> 7) * GLD + (e & 127)];
-    // Aqk (j <= i) and Abar (j < i): one wave per row i, lane j, four channels per LDS read.
+    // Aqk (j <= i) and Abar (j < i).  With the anchor A = G_last / 2 of each channel,
+    // e^{G_i - G_j} = e^{G_i - A} e^{A - G_j} and every factor lies within
+    // e^{+-|G_last| / 2}: Aqk = scale (q e^{G-A}) (k e^{A-G})^T and Abar = (k e^{G-A})
+    // (k e^{A-G})^T on v_mfma_f32_16x16x4f32.  A chunk that decays by more than e^-120
+    // on some channel (factors beyond e^60) takes the element-by-element sums.
     float abar[BW_C * BW_C / BW_PT];
-    for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
-        const int e = tid + BW_PT * s, i = e >> 6, j = e & 63;
-        float aq = 0.f, ak = 0.f;
-        if (j <= i) {
-#pragma unroll 4
-            for (int c = 0; c < BW_D; c += 4) {
-                const f32x4 gi = lds4(L.G + i * GLD + c), gj = lds4(L.G + j * GLD + c);
-                const f32x4 kj = lds_bf4(L.u.in.k + j * PQ_LD + c);
-                const f32x4 qi = lds_bf4(L.u.in.q + i * PQ_LD + c), ki = lds_bf4(L.u.in.k + i * PQ_LD + c);
-                for (int u = 0; u < 4; ++u) {
-                    const float d = fexp(gi[u] - gj[u]) * kj[u];
-                    aq += qi[u] * d;
-                    ak += ki[u] * d;
-                }
-            }
-            if (j == i) ak = 0.f;
+    const bool far = __syncthreads_or(tid < BW_D && !(L.G[(BW_C - 1) * GLD + tid] >= -120.f)) != 0;
+    if (!far) {
+        // This thread's 16 elements (row e / 128, channel e % 128, e = tid + 512 u).
+        float qa[16], ka[16], kb[16];
+        for (int u = 0; u < 16; ++u) {
+            const int e = tid + BW_PT * u, i = e >> 7, c = e & 127;
+            const float G = L.G[i * GLD + c], A = 0.5f * L.G[(BW_C - 1) * GLD + c];
+            const float eP = fexp(G - A), eM = fexp(A - G);
+            const float kv = bf2f(L.u.in.k[i * PQ_LD + c]);
+            qa[u] = bf2f(L.u.in.q[i * PQ_LD + c]) * eP;
+            ka[u] = kv * eM;
+            kb[u] = kv * eP;
         }
-        pr[BWP_AQK + e] = p.scale * aq;
-        pr[BWP_ABAR + e] = ak;
-        abar[s] = ak;
+        __syncthreads();   // q, k and G are read: q e^{G-A} goes over G, k e^{A-G} over q and k
+        float* X = L.G;
+        float* Y = reinterpret_cast<float*>(&L.u);
+        static_assert(BW_C * GLD * 4 <= sizeof(L.u), "anchored operand over q and k");
+        for (int u = 0; u < 16; ++u) {
+            const int e = tid + BW_PT * u, i = e >> 7, c = e & 127;
+            X[i * GLD + c] = qa[u];
+            Y[i * GLD + c] = ka[u];
+        }
+        // zeros of the tiles above the diagonal (the products below write the rest)
+        for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
+            const int e = tid + BW_PT * s, i = e >> 6, j = e & 63;
+            if ((j >> 4) > (i >> 4)) {
+                pr[BWP_AQK + e] = 0.f;
+                pr[BWP_ABAR + e] = 0.f;
+            }
+        }
+        __syncthreads();
+        // Wave w: the lower-triangle tiles w and w + 8 (row-major order over (it, jt),
+        // jt <= it).  MFMA b of channel block u sums channel 16 u + 4 (lane / 16) + b.
+        const int lane = tid & 63, wv = tid >> 6, m4 = 4 * (lane >> 4), rl = lane & 15;
+        auto tile_of = [](int t, int& ti, int& tj) {
+            ti = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+            tj = t - ti * (ti + 1) / 2;
+        };
+        auto product = [&](const float* Aop, int ti, int tj) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int u = 0; u < BW_D / 16; ++u) {
+                const f32x4 a4 = lds4(Aop + (16 * ti + rl) * GLD + 16 * u + m4);
+                const f32x4 b4 = lds4(Y + (16 * tj + rl) * GLD + 16 * u + m4);
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[bb], b4[bb], acc, 0, 0, 0);
+            }
+            return acc;
+        };
+        const int ntile = wv + 8 < 10 ? 2 : 1;
+        for (int k = 0; k < ntile; ++k) {
+            int ti, tj;
+            tile_of(wv + 8 * k, ti, tj);
+            const f32x4 acc = product(X, ti, tj);
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + m4 + r, j = 16 * tj + rl;
+                pr[BWP_AQK + i * BW_C + j] = j <= i ? p.scale * acc[r] : 0.f;
+            }
+        }
+        __syncthreads();   // q e^{G-A} is read: k e^{G-A} replaces it
+        for (int u = 0; u < 16; ++u) {
+            const int e = tid + BW_PT * u;
+            X[(e >> 7) * GLD + (e & 127)] = kb[u];
+        }
+        __syncthreads();
+        f32x4 accb[2];
+        for (int k = 0; k < ntile; ++k) {
+            int ti, tj;
+            tile_of(wv + 8 * k, ti, tj);
+            accb[k] = product(X, ti, tj);
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + m4 + r, j = 16 * tj + rl;
+                if (j >= i) accb[k][r] = 0.f;
+                pr[BWP_ABAR + i * BW_C + j] = accb[k][r];
+            }
+        }
+        __syncthreads();   // the operands are read: Abar goes to L.u.out.A
+        for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {   // zeros above the diagonal tiles
+            const int e = tid + BW_PT * s, i = e >> 6, j = e & 63;
+            if ((j >> 4) > (i >> 4)) L.u.out.A[i * BW_MD + j] = 0.f;
+        }
+        for (int k = 0; k < ntile; ++k) {
+            int ti, tj;
+            tile_of(wv + 8 * k, ti, tj);
+            for (int r = 0; r < 4; ++r) L.u.out.A[(16 * ti + m4 + r) * BW_MD + 16 * tj + rl] = accb[k][r];
+        }
+        __syncthreads();
+    } else {
+        // one wave per row i, lane j, four channels per LDS read
+        for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
+            const int e = tid + BW_PT * s, i = e >> 6, j = e & 63;
+            float aq = 0.f, ak = 0.f;
+            if (j <= i) {
+#pragma unroll 4
+                for (int c = 0; c < BW_D; c += 4) {
+                    const f32x4 gi = lds4(L.G + i * GLD + c), gj = lds4(L.G + j * GLD + c);
+                    const f32x4 kj = lds_bf4(L.u.in.k + j * PQ_LD + c);
+                    const f32x4 qi = lds_bf4(L.u.in.q + i * PQ_LD + c), ki = lds_bf4(L.u.in.k + i * PQ_LD + c);
+                    for (int u = 0; u < 4; ++u) {
+                        const float d = fexp(gi[u] - gj[u]) * kj[u];
+                        aq += qi[u] * d;
+                        ak += ki[u] * d;
+                    }
+                }
+                if (j == i) ak = 0.f;
+            }
+            pr[BWP_AQK + e] = p.scale * aq;
+            pr[BWP_ABAR + e] = ak;
+            abar[s] = ak;
+        }
+        __syncthreads();   // q and k are dead: Abar and T take their space
+        for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
+            const int e = tid + BW_PT * s;
+            L.u.out.A[(e >> 6) * BW_MD + (e & 63)] = abar[s];
+        }
+        __syncthreads();
     }
-    __syncthreads();   // q and k are dead: Abar and T take their space
-    for (int s = 0; s < BW_C * BW_C / BW_PT; ++s) {
-        const int e = tid + BW_PT * s;
-        L.u.out.A[(e >> 6) * BW_MD + (e & 63)] = abar[s];
-    }
-    __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution: lane j owns column j,
-    // T[i][j] = delta_ij - beta_i sum_{j <= m < i} Abar[i][m] T[m][j].
+    // T[i][j] = delta_ij - beta_i sum_{m < i} Abar[i][m] T[m][j] (T[m][j] = 0 for m < j).
+    // Rows go in blocks of 16: the columns m of earlier blocks are summed into the
+    // block's 16 running sums (independent chains), then each finished row of the
+    // block is added into the later rows' sums; every sum runs over m in increasing
+    // order.
     if (tid < BW_C) {
         const int j = tid;
-        for (int i = 0; i < BW_C; ++i) {
-            float t = 0.f;
-            if (i == j) {
-                t = 1.f;
-            } else if (i > j) {
-                float s = 0.f;
-                for (int m = j; m < i; ++m) s += L.u.out.A[i * BW_MD + m] * L.u.out.T[m * BW_MD + j];
-                t = -L.beta[i] * s;
+        for (int I = 0; I < BW_C / 16; ++I) {
+            float sacc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+            for (int m = 0; m < 16 * I; ++m) {
+                const float tm = L.u.out.T[m * BW_MD + j];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[r] += L.u.out.A[(16 * I + r) * BW_MD + m] * tm;
             }
-            L.u.out.T[i * BW_MD + j] = t;
-            pr[BWP_T + i * BW_C + j] = t;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 16 * I + r;
+                const float tm = m == j ? 1.f : (m > j ? -L.beta[m] * sacc[r] : 0.f);
+                L.u.out.T[m * BW_MD + j] = tm;
+                pr[BWP_T + m * BW_C + j] = tm;
+#pragma unroll
+                for (int r2 = r + 1; r2 < 16; ++r2) sacc[r2] += L.u.out.A[(16 * I + r2) * BW_MD + m] * tm;
+            }
         }
     }
 }
