@@ -839,19 +839,50 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
         F[GB_M1 + ai * BW_MD + j] = F[GB_DTB + ai * BW_MD + j] * F[GB_BETA + j];
     }
     __syncthreads();
-    for (int s = 0; s < 8; ++s) {   // M2 = T^T M1
-        const int j = aj + s;
-        float a = 0.f;
-        for (int m = 0; m < BW_C; ++m) a += F[GB_T + m * BW_MD + ai] * F[GB_M1 + m * BW_MD + j];
-        F[GB_M2 + ai * BW_MD + j] = a;
+    {
+        // M2 = T^T M1 on v_mfma_f32_16x16x4f32 (T[m][a] is zero for m < a): wave (it, chh)
+        // takes tiles (it, 2 chh) and (it, 2 chh + 1); MFMA b of block u sums m = 16 u +
+        // 4 (lane / 16) + b.  The zeros of dA above its diagonal tiles are written here.
+        const int m4 = 4 * (lane >> 4), rl = lane & 15, ta = 16 * it + rl;
+        for (int t = 0; t < 2; ++t) {
+            const int jt = 2 * chh + t;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = it; u < BW_C / 16; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int m = 16 * u + m4 + bb;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(F[GB_T + m * BW_MD + ta], F[GB_M1 + m * BW_MD + 16 * jt + rl],
+                                                               acc, 0, 0, 0);
+                }
+            }
+            for (int r = 0; r < 4; ++r) {
+                F[GB_M2 + (16 * it + m4 + r) * BW_MD + 16 * jt + rl] = acc[r];
+                if (jt > it) F[GB_DA + (16 * it + m4 + r) * BW_MD + 16 * jt + rl] = 0.f;
+            }
+        }
     }
     __syncthreads();
-    for (int s = 0; s < 8; ++s) {   // dA = -M2 T^T, strictly lower
-        const int j = aj + s;
-        float a = 0.f;
-        if (j < ai)
-            for (int m = 0; m < BW_C; ++m) a -= F[GB_M2 + ai * BW_MD + m] * F[GB_T + j * BW_MD + m];
-        F[GB_DA + ai * BW_MD + j] = a;
+    {
+        // dA = -M2 T^T, strictly lower (T[j][m] is zero for m > j): wave w takes the
+        // lower-triangle tiles w and w + 8 (row-major order over (at, jt), jt <= at)
+        const int m4 = 4 * (lane >> 4), rl = lane & 15;
+        for (int k = 0; k < (wv + 8 < 10 ? 2 : 1); ++k) {
+            const int t = wv + 8 * k;
+            const int at = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)), jt = t - at * (at + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u <= jt; ++u) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int m = 16 * u + m4 + bb;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(F[GB_M2 + (16 * at + rl) * BW_MD + m],
+                                                               F[GB_T + (16 * jt + rl) * BW_MD + m], acc, 0, 0, 0);
+                }
+            }
+            for (int r = 0; r < 4; ++r) {
+                const int a = 16 * at + m4 + r, j = 16 * jt + rl;
+                F[GB_DA + a * BW_MD + j] = j < a ? -acc[r] : 0.f;
+            }
+        }
     }
     __syncthreads();
     if (tid < BW_C) {
