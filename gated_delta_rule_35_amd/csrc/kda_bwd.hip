@@ -326,29 +326,35 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
 // state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.  For the
 // chunk-sized products thread t takes column zn = t % 32 of rows zi + 16 r.
 // The next chunk's raw inputs are fetched into registers while this one computes.
+// Raw inputs of one chunk, fetched into registers with 8- and 16-byte loads while
+// the chunk before computes.  Thread t takes, of the [64][128] tiles (k, q, G),
+// channels 4 (t % 32) .. + 3 of rows t / 32 + 16 v (v < 4); of the [64][64] tiles (T,
+// Aqk), elements 4 (t + 512 v) .. + 3 (v < 2), whose columns 4 (t % 16) .. + 3 are the
+// same for both; of the [64][32] value slice (v, do), elements 4 t .. + 3.
 struct StatesRaw {
-    uint16_t k[16];
-    float G[16], T[8], v[4];
-    float Gl, beta;
+    uint2 k[4];
+    f32x4 G[4], Gl, T[2];
+    float beta[4];
+    uint2 v;
 };
+__device__ __forceinline__ uint2 ld_bf4(const uint16_t* a) { return *reinterpret_cast<const uint2*>(a); }
+__device__ __forceinline__ f32x4 bf4_to_f32(uint2 w) { return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)}; }
 
-// Raw inputs of one chunk for thread t (the element layout of DstateRaw).
 __device__ __forceinline__ void states_fetch(const BwdParams& p, const ChunkIdx& x, int tid, int n0, StatesRaw& r) {
     const float* pr = p.prep + x.ch * BWP_FLOATS;
-    const int c = tid & 127;
-    for (int u = 0; u < 16; ++u) {
-        const int i = (tid + BW_ST * u) >> 7;
-        r.k[u] = i < x.len ? p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
-        r.G[u] = pr[BWP_G + tid + BW_ST * u];
+    const int c4 = 4 * (tid & 31);
+    for (int v = 0; v < 4; ++v) {
+        const int i = (tid >> 5) + 16 * v;
+        r.k[v] = i < x.len ? ld_bf4(p.k + qk_off(p, x.b, x.t0 + i, x.hq) + c4) : make_uint2(0u, 0u);
+        r.G[v] = lds4(pr + BWP_G + i * BW_D + c4);
     }
-    r.Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
-    for (int u = 0; u < 8; ++u) r.T[u] = pr[BWP_T + tid + BW_ST * u];
-    const int j = tid & 63;
-    r.beta = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
-    for (int u = 0; u < 4; ++u) {
-        const int e = tid + BW_ST * u, i = e >> 5, n = e & 31;
-        r.v[u] = i < x.len ? bf2f(p.v[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n]) : 0.f;
-    }
+    r.Gl = lds4(pr + BWP_G + (BW_C - 1) * BW_D + c4);
+    for (int v = 0; v < 2; ++v) r.T[v] = lds4(pr + BWP_T + 4 * (tid + BW_ST * v));
+    const int j4 = 4 * (tid & 15);
+    for (int e = 0; e < 4; ++e)
+        r.beta[e] = j4 + e < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j4 + e) * p.Hv + x.hv) : 0.f;
+    const int iv = tid >> 3, nv = 4 * (tid & 7);
+    r.v = iv < x.len ? ld_bf4(p.v + vh_off(p, x.b, x.t0 + iv, x.hv) + n0 + nv) : make_uint2(0u, 0u);
 }
 
 __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p) {
@@ -365,7 +371,6 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
     const int64_t bh = blockIdx.x / BW_NSL;
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
-    const int c = tid & 127;
     // The chunk products on v_mfma_f32_16x16x4f32, with the tiles of the reverse walk:
     // wave (it, nt) = (w % 4, w / 4) takes value columns 16 nt .. + 15 of the slice,
     // token tile it of Z and v_new, and state tiles (channels) 2 it, 2 it + 1 of h,
@@ -390,21 +395,27 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
                 sS[cc * BW_SD + col] = S[t][r];
             }
         if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
-        for (int u = 0; u < 16; ++u) {
-            const int i = (tid + BW_ST * u) >> 7;
-            const float kv = bf2f(raw.k[u]);
-            sKG[i * GLD + c] = kv * fexp(raw.G[u]);
-            sKH[i * GLD + c] = kv * fexp(raw.Gl - raw.G[u]);
+        {
+            const int c4 = 4 * (tid & 31);
+            for (int v = 0; v < 4; ++v) {
+                const int i = (tid >> 5) + 16 * v;
+                const f32x4 kv = bf4_to_f32(raw.k[v]);
+                f32x4 kg, kh;
+                for (int e = 0; e < 4; ++e) {
+                    kg[e] = kv[e] * fexp(raw.G[v][e]);
+                    kh[e] = kv[e] * fexp(raw.Gl[e] - raw.G[v][e]);
+                }
+                *reinterpret_cast<f32x4*>(sKG + i * GLD + c4) = kg;
+                *reinterpret_cast<f32x4*>(sKH + i * GLD + c4) = kh;
+            }
+            if (tid < 32)
+                for (int e = 0; e < 4; ++e) sGam[c4 + e] = fexp(raw.Gl[e]);
+            for (int v = 0; v < 2; ++v) {
+                const int e0 = 4 * (tid + BW_ST * v), i = e0 >> 6, j = e0 & 63;
+                for (int e = 0; e < 4; ++e) sTB[i * BW_MD + j + e] = raw.T[v][e] * raw.beta[e];
+            }
+            *reinterpret_cast<f32x4*>(sV + (tid >> 3) * BW_SD + 4 * (tid & 7)) = bf4_to_f32(raw.v);
         }
-        for (int u = 0; u < 8; ++u) {
-            const int e = tid + BW_ST * u;
-            sTB[(e >> 6) * BW_MD + (e & 63)] = raw.T[u] * raw.beta;
-        }
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + BW_ST * u;
-            sV[(e >> 5) * BW_SD + (e & 31)] = raw.v[u];
-        }
-        if (tid < BW_D) sGam[tid] = fexp(raw.Gl);
         if (ci + 1 < p.nc - 1) states_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci + 1) * p.Hv + hv), tid, n0, raw);
         __syncthreads();
         {   // Z = v - kg h
@@ -462,32 +473,32 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
 // e = t + 512 u of the [64][128] tiles (channel c = t % 128 for all of them) and
 // of the [64][64] tiles (column t % 64).
 struct DstateRaw {
-    uint16_t k[16], q[16];
-    float G[16], T[8], A[8], dO[4];
-    float Gl, beta;
+    uint2 k[4], q[4];
+    f32x4 G[4], Gl, T[2], A[2];
+    float beta[4];
+    uint2 dO;
 };
 
 __device__ __forceinline__ void dstate_fetch(const BwdParams& p, const ChunkIdx& x, int tid, int n0, DstateRaw& r) {
     const float* pr = p.prep + x.ch * BWP_FLOATS;
-    const int c = tid & 127;
-    for (int u = 0; u < 16; ++u) {
-        const int i = (tid + BW_ST * u) >> 7;
+    const int c4 = 4 * (tid & 31);
+    for (int v = 0; v < 4; ++v) {
+        const int i = (tid >> 5) + 16 * v;
         const bool in = i < x.len;
-        r.k[u] = in ? p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
-        r.q[u] = in ? p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c] : (uint16_t)0;
-        r.G[u] = pr[BWP_G + tid + BW_ST * u];
+        r.k[v] = in ? ld_bf4(p.k + qk_off(p, x.b, x.t0 + i, x.hq) + c4) : make_uint2(0u, 0u);
+        r.q[v] = in ? ld_bf4(p.q + qk_off(p, x.b, x.t0 + i, x.hq) + c4) : make_uint2(0u, 0u);
+        r.G[v] = lds4(pr + BWP_G + i * BW_D + c4);
     }
-    r.Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
-    for (int u = 0; u < 8; ++u) {
-        r.T[u] = pr[BWP_T + tid + BW_ST * u];
-        r.A[u] = pr[BWP_AQK + tid + BW_ST * u];
+    r.Gl = lds4(pr + BWP_G + (BW_C - 1) * BW_D + c4);
+    for (int v = 0; v < 2; ++v) {
+        r.T[v] = lds4(pr + BWP_T + 4 * (tid + BW_ST * v));
+        r.A[v] = lds4(pr + BWP_AQK + 4 * (tid + BW_ST * v));
     }
-    const int j = tid & 63;
-    r.beta = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
-    for (int u = 0; u < 4; ++u) {
-        const int e = tid + BW_ST * u, i = e >> 5, n = e & 31;
-        r.dO[u] = i < x.len ? bf2f(p.dO[vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n]) : 0.f;
-    }
+    const int j4 = 4 * (tid & 15);
+    for (int e = 0; e < 4; ++e)
+        r.beta[e] = j4 + e < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j4 + e) * p.Hv + x.hv) : 0.f;
+    const int iv = tid >> 3, nv = 4 * (tid & 7);
+    r.dO = iv < x.len ? ld_bf4(p.dO + vh_off(p, x.b, x.t0 + iv, x.hv) + n0 + nv) : make_uint2(0u, 0u);
 }
 
 __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p) {
@@ -505,7 +516,6 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
     const int64_t bh = blockIdx.x / BW_NSL;
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
-    const int c = tid & 127;
     // The chunk products on v_mfma_f32_16x16x4f32.  Wave (it, nt) = (w % 4, w / 4):
     // value columns 16 nt .. + 15 of the slice; token tile it of dv_new and dZ; state
     // tiles (channels) 2 it and 2 it + 1 of dh, kept in accumulators for the whole
@@ -531,22 +541,30 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
                 sDH[cc * BW_SD + col] = dh[t][r];
             }
         // this chunk's operands, from the registers fetched during the previous step
-        for (int u = 0; u < 16; ++u) {
-            const int i = (tid + BW_ST * u) >> 7;
-            const float kv = bf2f(raw.k[u]);
-            sKG[i * GLD + c] = kv * fexp(raw.G[u]);
-            sKQ[i * GLD + c] = kv * fexp(raw.Gl - raw.G[u]);
+        {
+            const int c4 = 4 * (tid & 31);
+            for (int v = 0; v < 4; ++v) {
+                const int i = (tid >> 5) + 16 * v;
+                const f32x4 kv = bf4_to_f32(raw.k[v]);
+                f32x4 kg, kh;
+                for (int e = 0; e < 4; ++e) {
+                    kg[e] = kv[e] * fexp(raw.G[v][e]);
+                    kh[e] = kv[e] * fexp(raw.Gl[e] - raw.G[v][e]);
+                }
+                *reinterpret_cast<f32x4*>(sKG + i * GLD + c4) = kg;
+                *reinterpret_cast<f32x4*>(sKQ + i * GLD + c4) = kh;
+            }
+            if (tid < 32)
+                for (int e = 0; e < 4; ++e) sGam[c4 + e] = fexp(raw.Gl[e]);
+            for (int v = 0; v < 2; ++v) {
+                const int e0 = 4 * (tid + BW_ST * v), i = e0 >> 6, j = e0 & 63;
+                for (int e = 0; e < 4; ++e) {
+                    sTB[i * BW_MD + j + e] = raw.T[v][e] * raw.beta[e];
+                    sAQ[i * BW_MD + j + e] = raw.A[v][e];
+                }
+            }
+            *reinterpret_cast<f32x4*>(sDO + (tid >> 3) * BW_SD + 4 * (tid & 7)) = bf4_to_f32(raw.dO);
         }
-        for (int u = 0; u < 8; ++u) {
-            const int e = tid + BW_ST * u, i = e >> 6, j = e & 63;
-            sTB[i * BW_MD + j] = raw.T[u] * raw.beta;
-            sAQ[i * BW_MD + j] = raw.A[u];
-        }
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + BW_ST * u;
-            sDO[(e >> 5) * BW_SD + (e & 31)] = raw.dO[u];
-        }
-        if (tid < BW_D) sGam[tid] = fexp(raw.Gl);
         __syncthreads();
         {   // dv_new = kh dh' + Aqk^T do (Aqk[m][i] is zero for m < i)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -568,8 +586,12 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
             for (int r = 0; r < 4; ++r) sDVN[(16 * it + m4 + r) * BW_SD + col] = acc[r];
         }
         __syncthreads();
-        for (int u = 0; u < 16; ++u)   // kh is done with: qg replaces it
-            sKQ[((tid + BW_ST * u) >> 7) * GLD + c] = p.scale * bf2f(raw.q[u]) * fexp(raw.G[u]);
+        for (int v = 0; v < 4; ++v) {   // kh is done with: qg replaces it
+            const f32x4 qv = bf4_to_f32(raw.q[v]);
+            f32x4 qg;
+            for (int e = 0; e < 4; ++e) qg[e] = p.scale * qv[e] * fexp(raw.G[v][e]);
+            *reinterpret_cast<f32x4*>(sKQ + ((tid >> 5) + 16 * v) * GLD + 4 * (tid & 31)) = qg;
+        }
         if (ci > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci - 1) * p.Hv + hv), tid, n0, raw);
         {   // dZ = Tb^T dv_new (Tb[i][j] is zero for i < j)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
