@@ -113,19 +113,24 @@ __global__ void __launch_bounds__(BW_PT, 2) kda_bwd_prep_kernel(const BwdParams 
     __shared__ __attribute__((aligned(16))) PrepLds L;
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
-    for (int e = tid; e < BW_C * BW_D; e += BW_PT) {
-        const int i = e >> 7, c = e & 127;
-        uint16_t qv = 0, kv = 0;   // rows past the sequence's end: q = k = 0, g = 0
-        float gv = 0.f;
-        if (i < x.len) {
-            const int64_t t = x.t0 + i;
-            qv = p.q[qk_off(p, x.b, t, x.hq) + c];
-            kv = p.k[qk_off(p, x.b, t, x.hq) + c];
-            gv = p.g[vh_off(p, x.b, t, x.hv) + c];
+    {
+        // thread t: channels 4 (t % 32) .. + 3 of rows t / 32 + 16 v; rows past the
+        // sequence's end: q = k = 0, g = 0
+        const int c4 = 4 * (tid & 31);
+        for (int v = 0; v < 4; ++v) {
+            const int i = (tid >> 5) + 16 * v;
+            uint2 qw = make_uint2(0u, 0u), kw = make_uint2(0u, 0u);
+            f32x4 gv = {0.f, 0.f, 0.f, 0.f};
+            if (i < x.len) {
+                const int64_t t = x.t0 + i;
+                qw = *reinterpret_cast<const uint2*>(p.q + qk_off(p, x.b, t, x.hq) + c4);
+                kw = *reinterpret_cast<const uint2*>(p.k + qk_off(p, x.b, t, x.hq) + c4);
+                gv = *reinterpret_cast<const f32x4*>(p.g + vh_off(p, x.b, t, x.hv) + c4);
+            }
+            *reinterpret_cast<uint2*>(L.u.in.q + i * PQ_LD + c4) = qw;
+            *reinterpret_cast<uint2*>(L.u.in.k + i * PQ_LD + c4) = kw;
+            *reinterpret_cast<f32x4*>(L.G + i * GLD + c4) = gv;
         }
-        L.u.in.q[i * PQ_LD + c] = qv;
-        L.u.in.k[i * PQ_LD + c] = kv;
-        L.G[i * GLD + c] = gv;
     }
     if (tid < BW_C) L.beta[tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
     __syncthreads();
@@ -292,32 +297,26 @@ __global__ void __launch_bounds__(BW_PT, 2) kda_bwd_prep_kernel(const BwdParams 
     }
 }
 
-// Loads the chunk's decayed key operands, and optionally Tb, into LDS.
-// Any of sKG, sKH, sQG, sTB may be null (not loaded).
+// The chunk's decayed key operands k e^G and k e^{G_last - G} into LDS ([64][ld]):
+// thread t takes channels 4 (t % 32) .. + 3 of rows t / 32 + 16 v (v < 4), with 8- and
+// 16-byte loads.
 __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx& x, const float* pr, float* sKG,
-                                             float* sKH, float* sQG, float* sTB, int tid, int nthreads,
-                                             int ld = BW_LD) {
-    if (sKG || sKH || sQG) {
-        for (int e = tid; e < BW_C * BW_D; e += nthreads) {
-            const int i = e >> 7, c = e & 127;
-            float kv = 0.f, qv = 0.f;
-            if (i < x.len) {
-                if (sKG || sKH) kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
-                if (sQG) qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + c]);
-            }
-            const float G = pr[BWP_G + e], Gl = pr[BWP_G + (BW_C - 1) * BW_D + c];
-            const float eG = fexp(G);
-            if (sKG) sKG[i * ld + c] = kv * eG;
-            if (sKH) sKH[i * ld + c] = kv * fexp(Gl - G);
-            if (sQG) sQG[i * ld + c] = p.scale * qv * eG;
+                                             float* sKH, int tid, int ld) {
+    const int c4 = 4 * (tid & 31);
+    const f32x4 Gl = *reinterpret_cast<const f32x4*>(pr + BWP_G + (BW_C - 1) * BW_D + c4);
+    for (int v = 0; v < 4; ++v) {
+        const int i = (tid >> 5) + 16 * v;
+        const uint2 kw = i < x.len ? *reinterpret_cast<const uint2*>(p.k + qk_off(p, x.b, x.t0 + i, x.hq) + c4)
+                                   : make_uint2(0u, 0u);
+        const f32x4 G = *reinterpret_cast<const f32x4*>(pr + BWP_G + i * BW_D + c4);
+        const f32x4 kv = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y)};
+        f32x4 kg, kh;
+        for (int e = 0; e < 4; ++e) {
+            kg[e] = kv[e] * fexp(G[e]);
+            kh[e] = kv[e] * fexp(Gl[e] - G[e]);
         }
-    }
-    if (sTB) {
-        for (int e = tid; e < BW_C * BW_C; e += nthreads) {
-            const int i = e >> 6, j = e & 63;
-            const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
-            sTB[i * BW_MD + j] = pr[BWP_T + e] * bj;
-        }
+        *reinterpret_cast<f32x4*>(sKG + i * ld + c4) = kg;
+        *reinterpret_cast<f32x4*>(sKH + i * ld + c4) = kh;
     }
 }
 
@@ -673,46 +672,52 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     for (int t = 0; t < 2; ++t) accAQ[t] = accTB[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dgam = 0.f;
 
-    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, nullptr, nullptr, tid, 512, GLD);
+    load_key_ops(p, x, pr, F + GA_KG, F + GA_KH, tid, GLD);
     {
-        const int j = tid & 63;   // the same column for every element this thread loads
-        const float bj = j < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j) * p.Hv + x.hv) : 0.f;
-        for (int e = tid; e < BW_C * BW_C; e += 512) {
-            F[GA_AQ + (e >> 6) * BW_MD + j] = pr[BWP_AQK + e];
-            F[GA_TB + (e >> 6) * GMD + j] = pr[BWP_T + e] * bj;
+        // Aqk and Tb: elements 4 (t + 512 v) .. + 3, columns 4 (t % 16) .. + 3 for both v
+        const int j4 = 4 * (tid & 15);
+        float bj[4];
+        for (int e = 0; e < 4; ++e)
+            bj[e] = j4 + e < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + j4 + e) * p.Hv + x.hv) : 0.f;
+        for (int v = 0; v < 2; ++v) {
+            const int e0 = 4 * (tid + 512 * v), i = e0 >> 6;
+            const f32x4 a4 = lds4(pr + BWP_AQK + e0), t4 = lds4(pr + BWP_T + e0);
+            for (int e = 0; e < 4; ++e) {
+                F[GA_AQ + i * BW_MD + j4 + e] = a4[e];
+                F[GA_TB + i * GMD + j4 + e] = t4[e] * bj[e];
+            }
         }
     }
-    // a slice's inputs for thread t: h and dh' elements t + 512 u (u < 4) of the
-    // [128][16] slice, do and v elements t + 512 u (u < 2) of the [64][16] slice;
-    // the next slice's are fetched while this one computes
-    float rH[4], rDH[4], rDO[2], rV[2];
+    // a slice's inputs for thread t: h and dh' of row t / 4, columns 4 (t % 4) .. + 3 of
+    // the [128][16] slice; do and v of token t / 8, columns 2 (t % 8), + 1 of the
+    // [64][16] slice; the next slice's are fetched while this one computes
+    f32x4 rH, rDH;
+    uint32_t rDO, rV;
     auto fetch = [&](int n0) {
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + 512 * u, cc = e >> 4, n = e & 15;
-            rH[u] = hs[cc * BW_D + n0 + n];
-            rDH[u] = ds[cc * BW_D + n0 + n];
-        }
-        for (int u = 0; u < 2; ++u) {
-            const int e = tid + 512 * u, i = e >> 4, n = e & 15;
-            const bool in = i < x.len;
-            const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n;
-            rDO[u] = in ? bf2f(p.dO[o]) : 0.f;
-            rV[u] = in ? bf2f(p.v[o]) : 0.f;
-        }
+        const int cc = tid >> 2, n = 4 * (tid & 3);
+        rH = *reinterpret_cast<const f32x4*>(hs + cc * BW_D + n0 + n);
+        rDH = *reinterpret_cast<const f32x4*>(ds + cc * BW_D + n0 + n);
+        const int i = tid >> 3, n2 = 2 * (tid & 7);
+        const bool in = i < x.len;
+        const int64_t o = vh_off(p, x.b, x.t0 + i, x.hv) + n0 + n2;
+        rDO = in ? *reinterpret_cast<const uint32_t*>(p.dO + o) : 0u;
+        rV = in ? *reinterpret_cast<const uint32_t*>(p.v + o) : 0u;
     };
     fetch(0);
 #pragma unroll 1
     for (int sl = 0; sl < GNSL; ++sl) {
         const int n0 = sl * GSL;
-        for (int u = 0; u < 4; ++u) {
-            const int e = tid + 512 * u, cc = e >> 4, n = e & 15;
-            F[GA_H + cc * GSD + n] = rH[u];
-            F[GA_DH + cc * GSD + n] = rDH[u];
-        }
-        for (int u = 0; u < 2; ++u) {
-            const int e = tid + 512 * u, i = e >> 4, n = e & 15;
-            F[GA_DO + n * GTS + i] = rDO[u];
-            F[GA_V + n * GTS + i] = rV[u];
+        {
+            const int cc = tid >> 2, n = 4 * (tid & 3);
+            for (int e = 0; e < 4; ++e) {
+                F[GA_H + cc * GSD + n + e] = rH[e];
+                F[GA_DH + cc * GSD + n + e] = rDH[e];
+            }
+            const int i = tid >> 3, n2 = 2 * (tid & 7);
+            F[GA_DO + n2 * GTS + i] = bf_lo(rDO);
+            F[GA_DO + (n2 + 1) * GTS + i] = bf_hi(rDO);
+            F[GA_V + n2 * GTS + i] = bf_lo(rV);
+            F[GA_V + (n2 + 1) * GTS + i] = bf_hi(rV);
         }
         if (sl + 1 < GNSL) fetch(n0 + GSL);
         __syncthreads();
@@ -849,9 +854,13 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     __syncthreads();
 
     // Phase B: dA = lower_strict(-T^T (dTb diag beta) T^T), dbeta, dAbar = diag(beta) dA.
-    for (int e = tid; e < BW_C * BW_C; e += 512) {
-        F[GB_T + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_T + e];
-        F[GB_AB + (e >> 6) * BW_MD + (e & 63)] = pr[BWP_ABAR + e];
+    for (int v = 0; v < 2; ++v) {
+        const int e0 = 4 * (tid + 512 * v), i = e0 >> 6, j = e0 & 63;
+        const f32x4 t4 = lds4(pr + BWP_T + e0), a4 = lds4(pr + BWP_ABAR + e0);
+        for (int e = 0; e < 4; ++e) {
+            F[GB_T + i * BW_MD + j + e] = t4[e];
+            F[GB_AB + i * BW_MD + j + e] = a4[e];
+        }
     }
     if (tid < BW_C)
         F[GB_BETA + tid] = tid < x.len ? ld_beta(p, ((int64_t)x.b * p.T + x.t0 + tid) * p.Hv + x.hv) : 0.f;
@@ -920,17 +929,26 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    // Phase C: q, k and G of the chunk, then the pairwise terms per channel.
-    for (int e = tid; e < BW_C * BW_D; e += 512) {
-        const int i = e >> 7, cc = e & 127;
-        float qv = 0.f, kv = 0.f;
-        if (i < x.len) {
-            qv = bf2f(p.q[qk_off(p, x.b, x.t0 + i, x.hq) + cc]);
-            kv = bf2f(p.k[qk_off(p, x.b, x.t0 + i, x.hq) + cc]);
+    // Phase C: q, k and G of the chunk (thread t: channels 4 (t % 32) .. + 3 of rows
+    // t / 32 + 16 v), then the pairwise terms per channel.
+    {
+        const int c4 = 4 * (tid & 31);
+        for (int v = 0; v < 4; ++v) {
+            const int i = (tid >> 5) + 16 * v;
+            uint2 qw = make_uint2(0u, 0u), kw = make_uint2(0u, 0u);
+            if (i < x.len) {
+                qw = *reinterpret_cast<const uint2*>(p.q + qk_off(p, x.b, x.t0 + i, x.hq) + c4);
+                kw = *reinterpret_cast<const uint2*>(p.k + qk_off(p, x.b, x.t0 + i, x.hq) + c4);
+            }
+            const f32x4 G = lds4(pr + BWP_G + i * BW_D + c4);
+            const float qf[4] = {bf_lo(qw.x), bf_hi(qw.x), bf_lo(qw.y), bf_hi(qw.y)};
+            const float kf[4] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y)};
+            for (int e = 0; e < 4; ++e) {
+                F[GC_Q + i * BW_LD + c4 + e] = qf[e];
+                F[GC_K + i * BW_LD + c4 + e] = kf[e];
+                F[GC_G + i * BW_LD + c4 + e] = G[e];
+            }
         }
-        F[GC_Q + i * BW_LD + cc] = qv;
-        F[GC_K + i * BW_LD + cc] = kv;
-        F[GC_G + i * BW_LD + cc] = pr[BWP_G + e];
     }
     __syncthreads();
     const float Gl = F[GC_G + (BW_C - 1) * BW_LD + c];
