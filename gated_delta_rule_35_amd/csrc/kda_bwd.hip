@@ -22,7 +22,8 @@
 // q, k, beta and g through their definitions (dA = -T^T dT T^T on the strict lower
 // triangle, and dg the reverse cumsum of dG within the chunk).
 //
-// Five kernels, all fp32 on the vector ALUs with LDS tiles:
+// Five kernels, all in fp32: the contractions on v_mfma_f32_16x16x4f32 (fp32
+// operands, fp32 accumulation), the rest on the vector ALUs, operands in LDS:
 //   prep    one work-group per (chunk, value head): G, Aqk, Abar and T
 //   states  one per (sequence, value head, 32 value columns): walks the chunks
 //           forward and stores each chunk's entering state h
@@ -30,8 +31,11 @@
 //           and writes the initial state's gradient
 //   grad    one per (chunk, value head): dv, dbeta, and dq, dk, dg per value head
 //   group   sums dq and dk over the value heads that share a q/k head
-// Every output element has one writer and a fixed summation order, so results
-// are bitwise reproducible.
+// The decay factors e^{G_i - G_j} of Aqk, Abar and the pairwise gradient sums are
+// split at a per-channel anchor A = G_last / 2 (e^{G_i - A} e^{A - G_j}), so those
+// sums become MFMA products; a chunk that decays by more than e^-120 on some channel
+// (factors beyond e^60) is summed element by element instead.  Every output element
+// has one writer and a fixed summation order, so results are bitwise reproducible.
 #include "kda_device.h"
 
 namespace kda {
@@ -320,11 +324,24 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
     }
 }
 
+// Work-group -> (row, value head, slice) of the state walks.  Work-groups are dealt
+// to the 8 XCDs round robin; the BW_NSL slices of a head read the same chunk
+// operands, so they are kept on one XCD (one L2) when the head count allows.
+__device__ __forceinline__ void walk_item(const BwdParams& p, int& slice, int64_t& bh) {
+    const int64_t idx = blockIdx.x, nbh = (int64_t)p.B * p.Hv;
+    if ((nbh & 7) == 0 && BW_NSL == 4) {
+        const int64_t k = idx >> 3;
+        bh = (idx & 7) + 8 * (k >> 2);
+        slice = (int)(k & 3);
+    } else {
+        bh = idx / BW_NSL;
+        slice = (int)(idx % BW_NSL);
+    }
+}
+
 // ---------------------------------------------------------------- states
-// Work-group (b, hv, slice of 32 value columns), 512 threads: thread t holds
-// state row c = t % 128, columns 8 (t / 128) .. + 7 of the slice.  For the
-// chunk-sized products thread t takes column zn = t % 32 of rows zi + 16 r.
-// The next chunk's raw inputs are fetched into registers while this one computes.
+// Work-group (b, hv, slice of 32 value columns), 512 threads: eight waves that
+// keep the state's 16x16 tiles in MFMA accumulators (tile layout at the kernel).
 // Raw inputs of one chunk, fetched into registers with 8- and 16-byte loads while
 // the chunk before computes.  Thread t takes, of the [64][128] tiles (k, q, G),
 // channels 4 (t % 32) .. + 3 of rows t / 32 + 16 v (v < 4); of the [64][64] tiles (T,
@@ -366,8 +383,9 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
     __shared__ __attribute__((aligned(16))) float sVN[BW_C * BW_SD];
     __shared__ float sGam[BW_D];
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x % BW_NSL;
-    const int64_t bh = blockIdx.x / BW_NSL;
+    int slice;
+    int64_t bh;
+    walk_item(p, slice, bh);
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
     // The chunk products on v_mfma_f32_16x16x4f32, with the tiles of the reverse walk:
@@ -464,13 +482,11 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
 }
 
 // ---------------------------------------------------------------- dstate
-// Same grid and thread layout as states.  kh is needed only for dv_new and qg
-// only for the state update, so they share one LDS tile: qg is written once
-// dv_new is done.  The walk is bound by the latency of each chunk's loads, so
-// the raw inputs of the next chunk (k, q, G, T, beta, Aqk, do) are fetched into
-// registers while the current chunk computes dZ and the state update.  Thread t loads elements
-// e = t + 512 u of the [64][128] tiles (channel c = t % 128 for all of them) and
-// of the [64][64] tiles (column t % 64).
+// Same grid and layout as states.  kh is needed only for dv_new and qg only for
+// the state update, so they share one LDS tile: qg is written once dv_new is
+// done.  The raw inputs of the next chunk (k, q, G, T, beta, Aqk, do; element
+// layout of StatesRaw) are fetched into registers while the current chunk
+// computes dZ and the state update.
 struct DstateRaw {
     uint2 k[4], q[4];
     f32x4 G[4], Gl, T[2], A[2];
@@ -511,8 +527,9 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
     __shared__ __attribute__((aligned(16))) float sDZ[BW_C * BW_SD];
     __shared__ float sGam[BW_D];
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x % BW_NSL;
-    const int64_t bh = blockIdx.x / BW_NSL;
+    int slice;
+    int64_t bh;
+    walk_item(p, slice, bh);
     const int hv = (int)(bh % p.Hv), b = (int)(bh / p.Hv);
     const int n0 = slice * BW_SL;
     // The chunk products on v_mfma_f32_16x16x4f32.  Wave (it, nt) = (w % 4, w / 4):
