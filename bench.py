@@ -178,7 +178,6 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
-FP32_VALU_PEAK_TFLOPS = 157.3
 FP32_MFMA_PEAK_TFLOPS = 157.3   # dense v_mfma_f32 (fp32 operands) on MI355X
 
 
