@@ -106,8 +106,9 @@ def test_bwd_matches_oracle(B, T, Hq, Hv, h0, dhT, beta_dtype):
 
 def test_bwd_strong_decay():
     # g near -3 per token and channel: e^G underflows within a chunk, the regime where
-    # the forward needs its exact diagonal path; every factor here is exp of a
-    # non-positive difference, so nothing overflows
+    # the forward needs its exact diagonal path; a chunk decays by about e^-190, past
+    # the e^-120 bound of the anchored MFMA products, so the decay-weighted sums are
+    # taken element by element (every factor exp of a non-positive difference)
     x = make_inputs(2, 140, 2, 2, torch.float32, True, seed=9, g_shift=-3.0)
     gen = torch.Generator("cpu").manual_seed(1009)
     x["do"] = torch.randn(2, 140, 2, 128, generator=gen).to(torch.bfloat16)
@@ -221,3 +222,21 @@ def test_bwd_padded_rows_equal_separate_sequences():
         if L < T:
             for n in ("dq", "dk", "dv", "dbeta"):
                 assert not np.any(got[n][b, L:]), n   # pads get no gradient
+
+
+@pytest.mark.parametrize("g_shift", [-1.25, -1.3, -1.65])
+def test_bwd_decay_near_the_anchored_limit(g_shift):
+    # chunk decays of e^-82 .. e^-119 per channel (g_shift -1.25: every chunk on the
+    # anchored MFMA products, factors up to e^59), e^-87 .. e^-121 (-1.3: the first
+    # chunk of a head past e^-120 on some channel, so element by element, the second
+    # anchored) and e^-103 .. e^-140 (-1.65: element by element throughout)
+    x = make_inputs(1, 140, 2, 2, torch.float32, True, seed=19, g_shift=g_shift)
+    gen = torch.Generator("cpu").manual_seed(1019)
+    x["do"] = torch.randn(1, 140, 2, 128, generator=gen).to(torch.bfloat16)
+    x["dhT"] = torch.randn(1, 2, 128, 128, generator=gen)
+    G_last = x["g"][0, :64].sum(0)
+    _say(f"kda_bwd B=1 T=140 g_shift {g_shift}: first chunk's decay e^{G_last.min():.1f} .. e^{G_last.max():.1f}")
+    got = _gpu_grads(x)
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    _compare(got, _oracle(x), f"g_shift {g_shift}")
