@@ -60,6 +60,28 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+SETTLE_S = 0.25
+
+
+def settle(call):
+    """Runs `call` untimed for at least SETTLE_S seconds before the warm-up steps.
+    From idle (as while the inputs are generated on the host) the GPU takes about
+    35 ms of work to reach its steady clocks: the headline forward measured 0.99,
+    0.80, 0.75, 0.73 ms per call over its first four blocks of ten calls and 0.72
+    ms from the fifth on.  The timed steps then measure the steady state."""
+    import torch
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < 1 or time.perf_counter() - t0 < SETTLE_S:
+        call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"settled: {n} untimed calls in {time.perf_counter() - t0:.2f} s")
+
+
+
 def algorithmic_bytes(n_tok, N, Hq, Hv, beta_bytes, has_h0, d=128):
     per_tok = Hq * d * 2 * 2 + Hv * d * 2 * 2 + Hv * d * 4 + Hv * beta_bytes
     states = N * Hv * d * d * 4 * (2 if has_h0 else 1)
@@ -146,6 +168,7 @@ def bench_decode(args):
     else:
         launch = one
     stream = torch.cuda.current_stream(dev)
+    settle(launch)
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
@@ -224,6 +247,7 @@ def bench_bwd(args):
                         grads=grads, workspace=ws)
 
     stream = torch.cuda.current_stream(dev)
+    settle(one)
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
@@ -398,6 +422,7 @@ def bench_cp(args):
     stream = torch.cuda.current_stream(dev)
 
     def timed(call):
+        settle(call)
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
@@ -511,59 +536,67 @@ def main():
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        kda_fwd_intra(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
-                      out=out, final_state=hT)
-        if ev:
-            ev[1].record(stream)
-        kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
-                     out=out, final_state=hT)
-        if ev:
-            ev[2].record(stream)
+    from gated_delta_rule_35_amd import kda_fwd, kda_fwd_ws
 
+    def step():
+        # the whole forward with a caller-owned workspace (kda_fwd_ws): the two
+        # kernels and nothing else
+        kda_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                   out=out, final_state=hT, workspace=ws)
+
+    settle(step)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps of kda_fwd_ws")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    scan_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    t_intra = sum(intra_ms) / len(intra_ms) / 1e3
-    t_scan = sum(scan_ms) / len(scan_ms) / 1e3
-    t_kern = t_intra + t_scan
     ms_per_step = wall / args.steps * 1e3
     tokens_per_s = n_tok / (ms_per_step / 1e3)
-    log(f"{ms_per_step:.4f} ms/step (wall); intra kernel avg {t_intra * 1e3:.4f} ms (min {min(intra_ms):.4f}), "
-        f"scan kernel avg {t_scan * 1e3:.4f} ms (min {min(scan_ms):.4f}); {tokens_per_s / 1e6:.2f} M tokens/s")
+    log(f"{ms_per_step:.4f} ms/step (wall), {tokens_per_s / 1e6:.2f} M tokens/s")
 
-    # The 11-argument kda_fwd on the same inputs: its device memory beyond the
-    # caller's tensors comes from hipMallocAsync / hipFreeAsync on the stream,
-    # inside the call (HIP events around each whole call).
-    from gated_delta_rule_35_amd import kda_fwd
-    for _ in range(2):
+    # Per-kernel durations, in passes of their own so that no timing event sits inside
+    # the timed steps: args.steps launches of each kernel back to back (the scan reads
+    # the records the last intra launch wrote), HIP events on the launch stream around
+    # each batch.
+    def batch_ms(launch):
+        launch()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(args.steps):
+            launch()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / args.steps
+
+    t_intra = batch_ms(lambda: kda_fwd_intra(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d,
+                                              initial_state=d["h0"], out=out, final_state=hT)) / 1e3
+    t_scan = batch_ms(lambda: kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, ws, cu_seqlens=cu_d,
+                                            initial_state=d["h0"], out=out, final_state=hT)) / 1e3
+    t_kern = t_intra + t_scan
+    log(f"intra kernel avg {t_intra * 1e3:.4f} ms, scan kernel avg {t_scan * 1e3:.4f} ms")
+
+    # The eleven-argument kda_fwd, whose workspace comes from hipMallocAsync /
+    # hipFreeAsync on the stream inside the call, timed like the steps above right
+    # after its own warm-up.
+    def call11():
         kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
                 out=out, final_state=hT)
+    for _ in range(args.warmup):
+        call11()
     torch.cuda.synchronize()
-    ev11 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in ev11:
-        e[0].record(stream)
-        kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
-                out=out, final_state=hT)
-        e[1].record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call11()
     torch.cuda.synchronize()
-    call11 = [e[0].elapsed_time(e[1]) for e in ev11]
-    t_call11 = sum(call11) / len(call11) / 1e3
-    log(f"kda_fwd (11 arguments) avg {t_call11 * 1e3:.4f} ms per call")
+    t_call11 = (time.perf_counter() - t0) / args.steps
+    log(f"kda_fwd (eleven arguments, workspace allocated in the call) {t_call11 * 1e3:.4f} ms per call (wall)")
 
     # kda_fwd_fused, the single-pass kernel, on the same inputs (HIP events around
     # each call: one launch of kda_fused_kernel)
@@ -638,6 +671,8 @@ def main():
                    "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0),
                    "dv_slices": kda_dv_slices(N, w.Hv), "mfma_operands": "f16", "accumulate": "f32",
                    "io": "bf16 q/k/v/o, f32 g/state"},
+        "step": "kda_fwd_ws: the whole forward on a caller-owned workspace (the two kernels)",
+        "settle_s": SETTLE_S,
         "kernel_ms_avg": round(t_kern * 1e3, 5),
         "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
         "algorithmic_bytes_per_step": nbytes,
