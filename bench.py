@@ -238,7 +238,7 @@ def bench_bwd(args):
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     do_d = do.to(dev)
-    ws = torch.empty(kda_bwd_workspace_size(B, T, w.Hq, w.Hv), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda_bwd_workspace_size(B * T, B, w.Hq, w.Hv), dtype=torch.uint8, device=dev)
     grads = None
 
     def one():

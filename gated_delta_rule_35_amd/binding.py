@@ -85,8 +85,8 @@ def load_library(path=None):
     lib.kda_fwd_cp_plan.restype = ctypes.c_int32
     lib.kda_decode.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_void_p]
     lib.kda_decode.restype = ctypes.c_int
-    lib.kda_bwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float] + [tp] * 9 + [ctypes.c_void_p, ctypes.c_int64,
-                                                                           ctypes.c_void_p]
+    lib.kda_bwd.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float] + [tp] * 10 + [ctypes.c_void_p, ctypes.c_int64,
+                                                                            ctypes.c_void_p]
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_bwd_workspace_size.argtypes = [ctypes.c_int64] * 4
     lib.kda_bwd_workspace_size.restype = ctypes.c_int64
@@ -343,21 +343,24 @@ def kda_decode(q, k, v, g, beta, scale, state, out=None, new_state=None, stream=
     return out, new_state
 
 
-def kda_bwd_workspace_size(batch, seq_len, num_qk_heads, num_value_heads):
-    """Bytes of device workspace kda_bwd needs (see include/kda.h)."""
-    return int(load_library().kda_bwd_workspace_size(batch, seq_len, num_qk_heads, num_value_heads))
+def kda_bwd_workspace_size(total_tokens, num_sequences, num_qk_heads, num_value_heads):
+    """Bytes of device workspace kda_bwd needs for total_tokens = B * T tokens in
+    num_sequences sequences (B, or N with cu_seqlens); see include/kda.h."""
+    return int(load_library().kda_bwd_workspace_size(total_tokens, num_sequences, num_qk_heads, num_value_heads))
 
 
 def kda_bwd(q, k, v, g, beta, scale, d_out, initial_state=None, d_final_state=None, grads=None,
-            d_initial_state=False, stream=None, workspace=None):
-    """Gradients of the forward over a fixed-length batch: q, k [B, T, Hq, 128] and
-    v, d_out [B, T, Hv, 128] bf16; g [B, T, Hv, 128] fp32; beta [B, T, Hv].
-    Returns a dict with dq, dk, dv, dg, dbeta (fp32, the inputs' shapes) and dh0
-    ([B, Hv, 128, 128] fp32 when d_initial_state is True or a tensor, else None).
-    `grads` may hold preallocated outputs under those names."""
+            d_initial_state=False, stream=None, workspace=None, cu_seqlens=None):
+    """Gradients of the forward: q, k [B, T, Hq, 128] and v, d_out [B, T, Hv, 128]
+    bf16; g [B, T, Hv, 128] fp32; beta [B, T, Hv]; cu_seqlens (int32 [N + 1], B = 1)
+    packs N sequences into the row, else N = B.  Returns a dict with dq, dk, dv, dg,
+    dbeta (fp32, the inputs' shapes) and dh0 ([N, Hv, 128, 128] fp32 when
+    d_initial_state is True or a tensor, else None).  `grads` may hold preallocated
+    outputs under those names."""
     lib = load_library()
     B, T, Hq, _ = q.shape
     Hv = v.shape[2]
+    N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
     dev = v.device
     out = dict(grads or {})
     f32 = torch.float32
@@ -367,11 +370,11 @@ def kda_bwd(q, k, v, g, beta, scale, d_out, initial_state=None, d_final_state=No
     if isinstance(d_initial_state, torch.Tensor):
         out["dh0"] = d_initial_state
     elif d_initial_state:
-        out["dh0"] = torch.empty((B, Hv, q.shape[3], v.shape[3]), dtype=f32, device=dev)
+        out["dh0"] = torch.empty((N, Hv, q.shape[3], v.shape[3]), dtype=f32, device=dev)
     else:
         out["dh0"] = None
-    tensors = (q, k, v, g, beta, initial_state, d_out, d_final_state, out["dq"], out["dk"], out["dv"], out["dg"],
-               out["dbeta"], out["dh0"])
+    tensors = (q, k, v, g, beta, cu_seqlens, initial_state, d_out, d_final_state, out["dq"], out["dk"], out["dv"],
+               out["dg"], out["dbeta"], out["dh0"])
     for t in tensors:
         if t is not None and not t.is_cuda:
             raise ValueError("kda_bwd needs every tensor on the GPU")

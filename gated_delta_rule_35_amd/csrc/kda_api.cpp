@@ -501,20 +501,22 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
 namespace {
 // Workspace of kda_bwd, in 256-byte aligned blocks: the chunk operands (G, Aqk, T,
 // Abar), the states entering the chunks, the state gradients leaving them, then,
-// when Hq < Hv, dq and dk per value head.
+// when Hq < Hv, dq and dk per value head.  Sized for ceil(total / 64) + N chunk
+// slots per value head, which covers both chunk numberings of the kernels: B rows
+// of ceil(T / 64) chunks, or the slots of N packed sequences.
 struct BwdLayout {
     int64_t prep, hs, dhs, dqv, dkv, total;
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hv) {
+BwdLayout bwd_layout(int64_t total_tokens, int64_t N, int64_t Hq, int64_t Hv) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-    const int64_t units = B * ((T + 63) / 64) * Hv;
+    const int64_t units = total_tokens > 0 ? ((total_tokens + 63) / 64 + N) * Hv : 0;
     BwdLayout L{};
     L.prep = 0;
     L.hs = L.prep + up(units * kda::BWP_FLOATS * 4);
     L.dhs = L.hs + up(units * kHeadDim * kHeadDim * 4);
     L.dqv = L.dhs + up(units * kHeadDim * kHeadDim * 4);
-    const int64_t per = Hq < Hv ? up(B * T * Hv * kHeadDim * 4) : 0;
+    const int64_t per = Hq < Hv ? up(total_tokens * Hv * kHeadDim * 4) : 0;
     L.dkv = L.dqv + per;
     L.total = L.dkv + per;
     return L;
@@ -523,13 +525,15 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hv) {
 
 extern "C" {
 
-int64_t kda_bwd_workspace_size(int64_t batch, int64_t seq_len, int64_t num_qk_heads, int64_t num_value_heads) {
-    if (batch < 0 || seq_len < 0 || num_qk_heads <= 0 || num_value_heads <= 0) return -1;
-    return bwd_layout(batch, seq_len, num_qk_heads, num_value_heads).total;
+int64_t kda_bwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_qk_heads,
+                               int64_t num_value_heads) {
+    if (total_tokens < 0 || num_sequences < 0 || num_qk_heads <= 0 || num_value_heads <= 0) return -1;
+    return bwd_layout(total_tokens, num_sequences, num_qk_heads, num_value_heads).total;
 }
 
 kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
-                     const kda_tensor_t* beta, float scale, const kda_tensor_t* initial_state,
+                     const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
+                     const kda_tensor_t* initial_state,
                      const kda_tensor_t* d_out, const kda_tensor_t* d_final_state, const kda_tensor_t* dq,
                      const kda_tensor_t* dk, const kda_tensor_t* dv, const kda_tensor_t* dg,
                      const kda_tensor_t* dbeta, const kda_tensor_t* d_initial_state, void* workspace,
@@ -541,6 +545,7 @@ kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
     if ((st = check_tensor(g, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
     if (!beta) return KDA_ERR_NULL;
     if ((st = check_tensor(beta, 3, KDA_BF16, KDA_F32, elem_size(beta->dtype))) != KDA_OK) return st;
+    if (cu_seqlens && (st = check_tensor(cu_seqlens, 1, KDA_I32, KDA_I32, 4)) != KDA_OK) return st;
     if (initial_state && (st = check_tensor(initial_state, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
     if ((st = check_tensor(d_out, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
     if (d_final_state && (st = check_tensor(d_final_state, 4, KDA_F32, KDA_F32, 16)) != KDA_OK) return st;
@@ -561,19 +566,26 @@ kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
         return KDA_ERR_SHAPE;
     const int64_t bs[3] = {B, T, Hv};
     if (!same_shape(beta, bs, 3) || !same_shape(dbeta, bs, 3)) return KDA_ERR_SHAPE;
-    const int64_t ss[4] = {B, Hv, kHeadDim, kHeadDim};
+    if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
+    if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
+    int64_t N = B;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_UNSUPPORTED;
+        if (cu_seqlens->shape[0] < 1) return KDA_ERR_SHAPE;
+        N = cu_seqlens->shape[0] - 1;
+    }
+    const int64_t ss[4] = {N, Hv, kHeadDim, kHeadDim};
     if (initial_state && !same_shape(initial_state, ss, 4)) return KDA_ERR_SHAPE;
     if (d_final_state && !same_shape(d_final_state, ss, 4)) return KDA_ERR_SHAPE;
     if (d_initial_state && !same_shape(d_initial_state, ss, 4)) return KDA_ERR_SHAPE;
-    if (Hq <= 0 || Hv <= 0) return KDA_ERR_SHAPE;
-    if (Hv % Hq != 0) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale) || !(scale > 0.f)) return KDA_ERR_VALUE;
     const int64_t nc = (T + 63) / 64;
-    if (B * nc * Hv > kMaxBlocks || B * Hv * 8 > kMaxBlocks || B > (int64_t(1) << 24) || Hv > (int64_t(1) << 16))
+    const int64_t nslots = cu_seqlens ? nc + N : B * nc;
+    if (nslots * Hv > kMaxBlocks || N * Hv * 8 > kMaxBlocks || N > (int64_t(1) << 24) || Hv > (int64_t(1) << 16))
         return KDA_ERR_UNSUPPORTED;
     // the group kernel's grid, (B T Hq 128) / 256 work-groups, must fit 32 bits
     if (B * T * Hq * kHeadDim > (int64_t(1) << 39)) return KDA_ERR_UNSUPPORTED;
-    const BwdLayout L = bwd_layout(B, T, Hq, Hv);
+    const BwdLayout L = bwd_layout(B * T, N, Hq, Hv);
     if (workspace && (workspace_size < L.total || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
         return KDA_ERR_WORKSPACE;
 
@@ -593,13 +605,16 @@ kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
     p.dg = static_cast<float*>(dg->data);
     p.dbeta = static_cast<float*>(dbeta->data);
     p.dh0 = d_initial_state ? static_cast<float*>(d_initial_state->data) : nullptr;
+    p.cu = cu_seqlens ? static_cast<const int32_t*>(cu_seqlens->data) : nullptr;
     p.T = T;
+    p.nslots = nslots;
     p.B = static_cast<int32_t>(B);
+    p.N = static_cast<int32_t>(N);
     p.Hq = static_cast<int32_t>(Hq);
     p.Hv = static_cast<int32_t>(Hv);
     p.nc = static_cast<int32_t>(nc);
     p.scale = scale;
-    if (B == 0 || (T == 0 && !d_initial_state)) return KDA_OK;
+    if (N == 0 || (T == 0 && !d_initial_state)) return KDA_OK;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     void* ws = workspace;
     if (!ws && T > 0 && hipMallocAsync(&ws, (size_t)L.total, hs) != hipSuccess) return KDA_ERR_HIP;

@@ -1,5 +1,6 @@
 // KDA backward pass on gfx950 (MI355X): gradients of the chunked forward with
-// respect to q, k, v, g, beta and the initial state, for fixed-length batches.
+// respect to q, k, v, g, beta and the initial state, for fixed-length batches and
+// for sequences packed into one row (cu_seqlens).
 //
 // The pages list chunk backward kernels beside the forward ("cuLA REPO_LAYOUT.md",
 // the kda/ entries for chunk_bwd and the WY dq/dk/dg kernels) but give no
@@ -63,15 +64,58 @@ __device__ __forceinline__ float ld_beta(const BwdParams& p, int64_t idx) {
 }
 
 struct ChunkIdx {
-    int b, ci, hv, hq, len;
-    int64_t t0, ch;   // first token of the chunk within its row; (chunk, value head) index
+    int b, ci, hv, hq, len;   // b: the chunk's token row (0 for packed sequences); len 0: no chunk
+    int64_t t0, ch;   // first token of the chunk within its row; (chunk slot, value head) index
 };
 
-// Work-group index of a (chunk, value head) grid: blk = (b * nc + ci) * Hv + hv.
-__device__ __forceinline__ ChunkIdx chunk_of(const BwdParams& p, int64_t blk) {
+// Token range of packed sequence n, [cu[n], cu[n+1]) clamped to [0, T), so that
+// malformed offsets can never send an access out of bounds.
+__device__ __forceinline__ void packed_seq(const BwdParams& p, int n, int64_t& bos, int64_t& len) {
+    int64_t a = p.cu[n], e = p.cu[n + 1];
+    a = a < 0 ? 0 : (a > p.T ? p.T : a);
+    e = e < a ? a : (e > p.T ? p.T : e);
+    bos = a;
+    len = e - a;
+}
+
+// Chunk ci of packed sequence n (first token bos, len tokens) in value head hv.  Its
+// slot is floor(bos / 64) + n + ci: slots of different chunks differ whenever the
+// sequences do not overlap, and all lie below ceil(T / 64) + N.
+__device__ __forceinline__ ChunkIdx packed_chunk(const BwdParams& p, int n, int64_t bos, int64_t len, int64_t ci,
+                                                 int hv) {
     ChunkIdx x;
-    x.hv = (int)(blk % p.Hv);
+    x.hv = hv;
+    x.hq = hv / (p.Hv / p.Hq);
+    x.b = 0;
+    x.ci = (int)ci;
+    x.t0 = bos + ci * BW_C;
+    const int64_t rest = len - ci * BW_C;
+    x.len = rest <= 0 ? 0 : (rest < BW_C ? (int)rest : BW_C);
+    x.ch = (bos / BW_C + n + ci) * p.Hv + hv;
+    return x;
+}
+
+// Work-group index of a (chunk, value head) grid.  Fixed-length rows:
+// blk = (b * nc + ci) * Hv + hv.  Packed sequences: blk = slot * Hv + hv, the
+// sequence found by bisection (the first slot of sequence n, floor(bos_n / 64) + n,
+// grows with n); a slot that holds no chunk comes back with len = 0.
+__device__ __forceinline__ ChunkIdx chunk_of(const BwdParams& p, int64_t blk) {
+    const int hv = (int)(blk % p.Hv);
     const int64_t cid = blk / p.Hv;
+    if (p.cu) {
+        int lo = 0, hi = p.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            int64_t b0, l0;
+            packed_seq(p, mid, b0, l0);
+            if (b0 / BW_C + mid <= cid) lo = mid; else hi = mid - 1;
+        }
+        int64_t bos, len;
+        packed_seq(p, lo, bos, len);
+        return packed_chunk(p, lo, bos, len, cid - (bos / BW_C + lo), hv);
+    }
+    ChunkIdx x;
+    x.hv = hv;
     x.b = (int)(cid / p.nc);
     x.ci = (int)(cid % p.nc);
     x.hq = x.hv / (p.Hv / p.Hq);
@@ -80,6 +124,23 @@ __device__ __forceinline__ ChunkIdx chunk_of(const BwdParams& p, int64_t blk) {
     x.len = rest < BW_C ? (int)rest : BW_C;
     x.ch = blk;
     return x;
+}
+
+// The state walks' view of sequence n: its chunk count, and chunk ci of it.
+struct SeqWalk {
+    int64_t bos, len;
+    int nc;
+};
+__device__ __forceinline__ SeqWalk seq_walk(const BwdParams& p, int n) {
+    SeqWalk w{0, 0, p.nc};
+    if (p.cu) {
+        packed_seq(p, n, w.bos, w.len);
+        w.nc = (int)((w.len + BW_C - 1) / BW_C);
+    }
+    return w;
+}
+__device__ __forceinline__ ChunkIdx walk_chunk(const BwdParams& p, const SeqWalk& w, int n, int ci, int hv) {
+    return p.cu ? packed_chunk(p, n, w.bos, w.len, ci, hv) : chunk_of(p, ((int64_t)n * p.nc + ci) * p.Hv + hv);
 }
 
 __device__ __forceinline__ int64_t qk_off(const BwdParams& p, int b, int64_t t, int hq) {
@@ -117,6 +178,7 @@ __global__ void __launch_bounds__(BW_PT, 2) kda_bwd_prep_kernel(const BwdParams 
     __shared__ __attribute__((aligned(16))) PrepLds L;
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
+    if (x.len == 0) return;   // a slot that holds no chunk (uniform per work-group)
     {
         // thread t: channels 4 (t % 32) .. + 3 of rows t / 32 + 16 v; rows past the
         // sequence's end: q = k = 0, g = 0
@@ -328,7 +390,7 @@ __device__ __forceinline__ void load_key_ops(const BwdParams& p, const ChunkIdx&
 // to the 8 XCDs round robin; the BW_NSL slices of a head read the same chunk
 // operands, so they are kept on one XCD (one L2) when the head count allows.
 __device__ __forceinline__ void walk_item(const BwdParams& p, int& slice, int64_t& bh) {
-    const int64_t idx = blockIdx.x, nbh = (int64_t)p.B * p.Hv;
+    const int64_t idx = blockIdx.x, nbh = (int64_t)p.N * p.Hv;
     if ((nbh & 7) == 0 && BW_NSL == 4) {
         const int64_t k = idx >> 3;
         bh = (idx & 7) + 8 * (k >> 2);
@@ -340,7 +402,7 @@ __device__ __forceinline__ void walk_item(const BwdParams& p, int& slice, int64_
 }
 
 // ---------------------------------------------------------------- states
-// Work-group (b, hv, slice of 32 value columns), 512 threads: eight waves that
+// Work-group (sequence b, hv, slice of 32 value columns), 512 threads: eight waves that
 // keep the state's 16x16 tiles in MFMA accumulators (tile layout at the kernel).
 // Raw inputs of one chunk, fetched into registers with 8- and 16-byte loads while
 // the chunk before computes.  Thread t takes, of the [64][128] tiles (k, q, G),
@@ -399,11 +461,12 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
         for (int r = 0; r < 4; ++r)
             S[t][r] = p.h0 ? p.h0[((int64_t)b * p.Hv + hv) * BW_STATE + (32 * it + 16 * t + m4 + r) * BW_D + n0 + col]
                            : 0.f;
+    const SeqWalk w = seq_walk(p, b);
     StatesRaw raw;
-    if (p.nc > 1) states_fetch(p, chunk_of(p, (int64_t)b * p.nc * p.Hv + hv), tid, n0, raw);
+    if (w.nc > 1) states_fetch(p, walk_chunk(p, w, b, 0, hv), tid, n0, raw);
 #pragma unroll 1
-    for (int ci = 0; ci < p.nc; ++ci) {
-        const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
+    for (int ci = 0; ci < w.nc; ++ci) {
+        const ChunkIdx x = walk_chunk(p, w, b, ci, hv);
         float* hs = p.hs + x.ch * BW_STATE + n0 + col;
         for (int t = 0; t < 2; ++t)
             for (int r = 0; r < 4; ++r) {
@@ -411,7 +474,7 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
                 hs[cc * BW_D] = S[t][r];
                 sS[cc * BW_SD + col] = S[t][r];
             }
-        if (ci == p.nc - 1) break;   // the state leaving the last chunk is not needed
+        if (ci == w.nc - 1) break;   // the state leaving the last chunk is not needed
         {
             const int c4 = 4 * (tid & 31);
             for (int v = 0; v < 4; ++v) {
@@ -433,7 +496,7 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_states_kernel(const BwdParams p
             }
             *reinterpret_cast<f32x4*>(sV + (tid >> 3) * BW_SD + 4 * (tid & 7)) = bf4_to_f32(raw.v);
         }
-        if (ci + 1 < p.nc - 1) states_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci + 1) * p.Hv + hv), tid, n0, raw);
+        if (ci + 1 < w.nc - 1) states_fetch(p, walk_chunk(p, w, b, ci + 1, hv), tid, n0, raw);
         __syncthreads();
         {   // Z = v - kg h
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -544,11 +607,12 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
         for (int r = 0; r < 4; ++r)
             dh[t][r] = p.dhT ? p.dhT[((int64_t)b * p.Hv + hv) * BW_STATE + (32 * it + 16 * t + m4 + r) * BW_D + n0 + col]
                              : 0.f;
+    const SeqWalk w = seq_walk(p, b);
     DstateRaw raw;
-    if (p.nc > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + p.nc - 1) * p.Hv + hv), tid, n0, raw);
+    if (w.nc > 0) dstate_fetch(p, walk_chunk(p, w, b, w.nc - 1, hv), tid, n0, raw);
 #pragma unroll 1
-    for (int ci = p.nc - 1; ci >= 0; --ci) {
-        const ChunkIdx x = chunk_of(p, ((int64_t)b * p.nc + ci) * p.Hv + hv);
+    for (int ci = w.nc - 1; ci >= 0; --ci) {
+        const ChunkIdx x = walk_chunk(p, w, b, ci, hv);
         float* ds = p.dhs + x.ch * BW_STATE + n0 + col;
         for (int t = 0; t < 2; ++t)
             for (int r = 0; r < 4; ++r) {
@@ -608,7 +672,7 @@ __global__ void __launch_bounds__(BW_ST) kda_bwd_dstate_kernel(const BwdParams p
             for (int e = 0; e < 4; ++e) qg[e] = p.scale * qv[e] * fexp(raw.G[v][e]);
             *reinterpret_cast<f32x4*>(sKQ + ((tid >> 5) + 16 * v) * GLD + 4 * (tid & 31)) = qg;
         }
-        if (ci > 0) dstate_fetch(p, chunk_of(p, ((int64_t)b * p.nc + ci - 1) * p.Hv + hv), tid, n0, raw);
+        if (ci > 0) dstate_fetch(p, walk_chunk(p, w, b, ci - 1, hv), tid, n0, raw);
         {   // dZ = Tb^T dv_new (Tb[i][j] is zero for i < j)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             const int tj = 16 * it + rl;
@@ -671,6 +735,7 @@ __global__ void __launch_bounds__(512) kda_bwd_grad_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float F[G_LDS];
     const int tid = threadIdx.x;
     const ChunkIdx x = chunk_of(p, blockIdx.x);
+    if (x.len == 0) return;   // a slot that holds no chunk (uniform per work-group)
     const float* pr = p.prep + x.ch * BWP_FLOATS;
     const float* hs = p.hs + x.ch * BW_STATE;
     const float* ds = p.dhs + x.ch * BW_STATE;
@@ -1106,6 +1171,10 @@ __global__ void __launch_bounds__(256) kda_bwd_group_kernel(const BwdParams p, i
     const int64_t rest = e >> 7;
     const int hq = (int)(rest % p.Hq);
     const int64_t tok = rest / p.Hq;
+    if (p.cu) {   // tokens of no packed sequence are not written
+        const int64_t a = p.cu[0], z = p.cu[p.N];
+        if (tok < a || tok >= z) return;
+    }
     const int group = p.Hv / p.Hq;
     float sq = 0.f, sk = 0.f;
     for (int u = 0; u < group; ++u) {
@@ -1120,8 +1189,8 @@ __global__ void __launch_bounds__(256) kda_bwd_group_kernel(const BwdParams p, i
 }  // namespace
 
 hipError_t launch_kda_bwd(const BwdParams& p, hipStream_t stream) {
-    const int64_t chunks = (int64_t)p.B * p.nc * p.Hv;
-    const int64_t scans = (int64_t)p.B * p.Hv * BW_NSL;
+    const int64_t chunks = p.T > 0 ? p.nslots * p.Hv : 0;
+    const int64_t scans = (int64_t)p.N * p.Hv * BW_NSL;
     if (chunks > 0) {
         hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)chunks), dim3(BW_PT), 0, stream, p);
         hipLaunchKernelGGL(kda_bwd_states_kernel, dim3((unsigned)scans), dim3(BW_ST), 0, stream, p);

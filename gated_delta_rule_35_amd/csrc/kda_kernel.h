@@ -62,7 +62,8 @@ struct DecodeParams {
 
 hipError_t launch_kda_decode(const DecodeParams& p, hipStream_t stream);
 
-// Backward pass over a fixed-length batch [B, T] (kda_bwd.hip).
+// Backward pass (kda_bwd.hip) over a fixed-length batch [B, T] or, with cu, N
+// sequences packed into one row of T tokens.
 struct BwdParams {
     const uint16_t* q;     // [B, T, Hq, 128] bf16 bits
     const uint16_t* k;     // [B, T, Hq, 128] bf16 bits
@@ -70,21 +71,23 @@ struct BwdParams {
     const uint16_t* dO;    // [B, T, Hv, 128] bf16 bits: gradient of the output
     const float* g;        // [B, T, Hv, 128]
     const void* beta;      // [B, T, Hv] bf16 bits or fp32
-    const float* h0;       // [B, Hv, 128, 128] or nullptr (zero state)
-    const float* dhT;      // [B, Hv, 128, 128] gradient of the final state, or nullptr (zero)
+    const int32_t* cu;     // [N + 1] sequence offsets into the packed row (B = 1), or nullptr
+    const float* h0;       // [N, Hv, 128, 128] or nullptr (zero state)
+    const float* dhT;      // [N, Hv, 128, 128] gradient of the final state, or nullptr (zero)
     float* dq;             // [B, T, Hq, 128]
     float* dk;             // [B, T, Hq, 128]
     float* dv;             // [B, T, Hv, 128]
     float* dg;             // [B, T, Hv, 128]
     float* dbeta;          // [B, T, Hv]
-    float* dh0;            // [B, Hv, 128, 128] or nullptr (not written)
-    float* prep;           // [B * nc * Hv][BWP_FLOATS]: G, Aqk, T, Abar of each chunk
-    float* hs;             // [B * nc * Hv][128 * 128]: state entering each chunk
-    float* dhs;            // [B * nc * Hv][128 * 128]: gradient of the state leaving each chunk
+    float* dh0;            // [N, Hv, 128, 128] or nullptr (not written)
+    float* prep;           // [nslots * Hv][BWP_FLOATS]: G, Aqk, T, Abar of each chunk
+    float* hs;             // [nslots * Hv][128 * 128]: state entering each chunk
+    float* dhs;            // [nslots * Hv][128 * 128]: gradient of the state leaving each chunk
     float* dqv;            // [B, T, Hv, 128]: dq per value head (equals dq when Hq == Hv)
     float* dkv;            // [B, T, Hv, 128]: dk per value head (equals dk when Hq == Hv)
     int64_t T;
-    int32_t B, Hq, Hv, nc;  // nc = ceil(T / 64) chunks per row
+    int64_t nslots;         // chunk slots: B * nc, or with cu ceil(T / 64) + N
+    int32_t B, N, Hq, Hv, nc;  // N sequences (B without cu); nc = ceil(T / 64) chunks per row
     int32_t beta_f32;
     float scale;
 };

@@ -318,53 +318,60 @@ kda_status_t kda_decode(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
                         const kda_tensor_t* out, void* stream);
 
 /*
- * kda_bwd_workspace_size -- bytes of device workspace kda_bwd needs for a
- * fixed-length batch of B rows of T tokens with Hq query/key heads and Hv value
- * heads: per 64-token chunk and value head, 80 KB of chunk operands and two
- * 64 KB states; when Hq < Hv, also 2 * B * T * Hv * 512 bytes for dq and dk per
- * value head.  Returns -1 for negative sizes or non-positive head counts.
+ * kda_bwd_workspace_size -- bytes of device workspace kda_bwd needs for
+ * total_tokens = B * T tokens in num_sequences sequences (B for a fixed-length
+ * batch, N with cu_seqlens) with Hq query/key heads and Hv value heads: per
+ * value head and each of ceil(total_tokens / 64) + num_sequences chunk slots,
+ * 80 KB of chunk operands and two 64 KB states; when Hq < Hv, also
+ * 2 * total_tokens * Hv * 512 bytes for dq and dk per value head.  Returns -1
+ * for negative sizes or non-positive head counts.
  */
-int64_t kda_bwd_workspace_size(int64_t batch, int64_t seq_len, int64_t num_qk_heads, int64_t num_value_heads);
+int64_t kda_bwd_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_qk_heads,
+                               int64_t num_value_heads);
 
 /*
- * kda_bwd -- gradients of kda_fwd over a fixed-length batch (no cu_seqlens) with
- * respect to q, k, v, g, beta and the initial state, given the gradients of the
- * output (d_out) and of the final state (d_final_state, NULL for zero).
+ * kda_bwd -- gradients of kda_fwd with respect to q, k, v, g, beta and the
+ * initial state, given the gradients of the output (d_out) and of the final
+ * state (d_final_state, NULL for zero).
  *
  * The pages list the chunk backward among the library's KDA kernels ("cuLA
  * REPO_LAYOUT.md", the kda/ entries for chunk_bwd and the WY dq/dk/dg kernels)
- * without equations; this is the exact gradient of the recurrence above,
- * evaluated through the chunk form of the forward (64-token chunks): a forward
- * walk over each sequence's chunks stores the state entering each, a backward
- * walk carries the state gradient, and a chunk-parallel pass forms the token
- * gradients.  All arithmetic is fp32 (no MFMA).
+ * without equations, and the bot summary of "cuLA PR #131" (New Features) has
+ * the forward and backward take packed variable-length inputs.  This is the
+ * exact gradient of the recurrence above, evaluated through the chunk form of
+ * the forward (64-token chunks from each sequence's start): a forward walk
+ * over each sequence's chunks stores the state entering each, a backward walk
+ * carries the state gradient, and a chunk-parallel pass forms the token
+ * gradients.  All arithmetic is fp32; the contractions run on fp32 matrix
+ * instructions.
  *
- * Shapes and dtypes (B, T, Hq, Hv as for kda_fwd, head dimension 128):
- *   q, k, v, g, beta, initial_state   as for kda_fwd (initial_state may be NULL)
+ * Shapes and dtypes (B, T, Hq, Hv, N as for kda_fwd, head dimension 128):
+ *   q, k, v, g, beta, cu_seqlens, initial_state   as for kda_fwd (cu_seqlens
+ *                    and initial_state may be NULL)
  *   d_out            [B, T, Hv, 128]      bf16
- *   d_final_state    [B, Hv, 128, 128]    fp32, or NULL
+ *   d_final_state    [N, Hv, 128, 128]    fp32, or NULL
  *   dq, dk           [B, T, Hq, 128]      fp32 (summed over the value heads of a group)
  *   dv, dg           [B, T, Hv, 128]      fp32
  *   dbeta            [B, T, Hv]           fp32
- *   d_initial_state  [B, Hv, 128, 128]    fp32, or NULL (not computed)
- * Outputs must not overlap inputs or each other.  workspace: device memory of
- * at least kda_bwd_workspace_size() bytes, 256-byte aligned, owned by the
- * caller and not used by anything else until the call's work on `stream` has
- * finished; NULL makes the library allocate it with hipMallocAsync on `stream`
- * and release it with hipFreeAsync.  Checks, error codes, stream semantics and
- * reproducibility are those of kda_fwd; the call does not synchronise.
- * Sequences of different lengths: pad them to a common T with q = k = v = 0,
- * g = 0, beta = 0 and d_out = 0.  Such tokens neither decay nor write the
- * state, so each row's gradients are those of its own sequence; the pads get
- * zero dq, dk, dv and dbeta.
+ *   d_initial_state  [N, Hv, 128, 128]    fp32, or NULL (not computed)
+ * With cu_seqlens, gradient rows of tokens that lie in no sequence are not
+ * written, and an empty sequence passes d_final_state through to its
+ * d_initial_state.  Outputs must not overlap inputs or each other.
+ * workspace: device memory of at least kda_bwd_workspace_size(B * T, N, Hq, Hv)
+ * bytes, 256-byte aligned, owned by the caller and not used by anything else
+ * until the call's work on `stream` has finished; NULL makes the library
+ * allocate it with hipMallocAsync on `stream` and release it with
+ * hipFreeAsync.  Checks, error codes, the cu_seqlens precondition, stream
+ * semantics and reproducibility are those of kda_fwd; the call does not
+ * synchronise.
  */
 kda_status_t kda_bwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                      const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
-                     const kda_tensor_t* initial_state, const kda_tensor_t* d_out,
-                     const kda_tensor_t* d_final_state, const kda_tensor_t* dq, const kda_tensor_t* dk,
-                     const kda_tensor_t* dv, const kda_tensor_t* dg, const kda_tensor_t* dbeta,
-                     const kda_tensor_t* d_initial_state, void* workspace, int64_t workspace_size,
-                     void* stream);
+                     const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                     const kda_tensor_t* d_out, const kda_tensor_t* d_final_state, const kda_tensor_t* dq,
+                     const kda_tensor_t* dk, const kda_tensor_t* dv, const kda_tensor_t* dg,
+                     const kda_tensor_t* dbeta, const kda_tensor_t* d_initial_state, void* workspace,
+                     int64_t workspace_size, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status_t status);

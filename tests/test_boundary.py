@@ -412,7 +412,7 @@ def good_bwd(B=2, T_=100, Hq=2, Hv=4, beta_dtype=binding.KDA_F32, h0=True, dh0=T
 
 
 BWD_ARGS = ("q", "k", "v", "g", "beta")
-BWD_REST = ("h0", "do", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0")
+BWD_REST = ("cu", "h0", "do", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
 def call_bwd(lib, a, scale=0.088, ws=None, ws_size=0):
@@ -428,12 +428,15 @@ def expect_bwd(lib, a, name, **kw):
 
 def test_bwd_workspace_size(lib):
     unit = 20480 * 4 + 2 * 128 * 128 * 4
-    assert lib.kda_bwd_workspace_size(2, 8192, 64, 64) == 2 * 128 * 64 * unit
+    # (total tokens, sequences, Hq, Hv): ceil(total / 64) + N chunk slots per value head
+    assert lib.kda_bwd_workspace_size(2 * 8192, 2, 64, 64) == (256 + 2) * 64 * unit
     # grouped value heads add dq and dk per value head; partial chunks count whole
-    assert lib.kda_bwd_workspace_size(1, 100, 2, 4) == 2 * 4 * unit + 2 * 100 * 4 * 512
-    assert lib.kda_bwd_workspace_size(3, 0, 1, 1) == 0
+    assert lib.kda_bwd_workspace_size(100, 1, 2, 4) == (2 + 1) * 4 * unit + 2 * 100 * 4 * 512
+    assert lib.kda_bwd_workspace_size(1000, 14, 4, 4) == (16 + 14) * 4 * unit
+    assert lib.kda_bwd_workspace_size(0, 3, 1, 1) == 0
     assert lib.kda_bwd_workspace_size(-1, 10, 1, 1) == -1
-    assert lib.kda_bwd_workspace_size(1, 10, 0, 1) == -1
+    assert lib.kda_bwd_workspace_size(10, -1, 1, 1) == -1
+    assert lib.kda_bwd_workspace_size(10, 1, 0, 1) == -1
 
 
 def test_bwd_rejects_bad_arguments(lib):
@@ -460,9 +463,42 @@ def test_bwd_rejects_bad_arguments(lib):
     expect_bwd(lib, a, "KDA_ERR_LAYOUT")
     for s in (0.0, -1.0, float("inf")):
         expect_bwd(lib, good_bwd(), "KDA_ERR_VALUE", scale=s)
-    need = lib.kda_bwd_workspace_size(2, 100, 2, 4)
+    need = lib.kda_bwd_workspace_size(2 * 100, 2, 2, 4)
     expect_bwd(lib, good_bwd(), "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
     expect_bwd(lib, good_bwd(), "KDA_ERR_WORKSPACE", ws=FAKE + 16, ws_size=need)
+
+
+def test_bwd_rejects_bad_packed_batches(lib):
+    I32 = binding.KDA_I32
+    a = good_bwd()                       # cu_seqlens needs a single packed row
+    a["cu"] = T([3], I32, data=FAKE)
+    expect_bwd(lib, a, "KDA_ERR_UNSUPPORTED")
+    a = good_bwd(B=1, h0=False, dh0=False)
+    a["dhT"] = None
+    a["cu"] = T([4], binding.KDA_F32, data=FAKE)
+    expect_bwd(lib, a, "KDA_ERR_DTYPE")
+    a["cu"] = T([0], I32, data=FAKE)
+    expect_bwd(lib, a, "KDA_ERR_SHAPE")
+    # the states follow the number of sequences, N = len(cu) - 1, not B
+    for key in ("h0", "dhT", "dh0"):
+        a = good_bwd(B=1, h0=False, dh0=False)
+        a["dhT"] = None
+        a["cu"] = T([4], I32, data=FAKE)
+        a[key] = T([1, 4, 128, 128], binding.KDA_F32)
+        expect_bwd(lib, a, "KDA_ERR_SHAPE")
+    # the workspace is sized by the slots of the packed sequences
+    a = good_bwd(B=1, h0=False, dh0=False)
+    a["dhT"] = None
+    a["cu"] = T([4], I32, data=FAKE)
+    need = lib.kda_bwd_workspace_size(100, 3, 2, 4)
+    expect_bwd(lib, a, "KDA_ERR_WORKSPACE", ws=FAKE, ws_size=need - 1)
+    # no sequences: nothing to compute, no launch
+    a = good_bwd(B=1, h0=False, dh0=False)
+    a["dhT"] = None
+    a["cu"] = T([1], I32, data=FAKE)
+    for key in ("h0", "dhT", "dh0"):
+        a[key] = T([0, 4, 128, 128], binding.KDA_F32, data=None)
+    expect_bwd(lib, a, "KDA_OK")
 
 
 def test_bwd_empty_problem_needs_no_launch(lib):

@@ -15,9 +15,9 @@ import pytest
 import torch
 
 from gated_delta_rule_35_amd import kda_bwd, kda_bwd_workspace_size, load_library
-from gated_delta_rule_35_amd.inputs import make_inputs
+from gated_delta_rule_35_amd.inputs import cu_from_lengths, make_inputs, varlen_lengths
 from oracle import grad as og
-from tests.kda_check import head_subset, to_device
+from tests.kda_check import head_subset, seq_slices, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -130,7 +130,7 @@ def test_bwd_empty_sequence_passes_the_state_gradient_through():
 
 def test_bwd_without_initial_state_gradient_and_with_caller_workspace():
     x = _case(1, 130, 2, 4, seed=6)
-    need = kda_bwd_workspace_size(1, 130, 2, 4)
+    need = kda_bwd_workspace_size(130, 1, 2, 4)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     _say("kda_bwd B=1 T=130 caller workspace, no dh0")
     a = _gpu_grads(x, want_dh0=False, workspace=ws)
@@ -240,3 +240,131 @@ def test_bwd_decay_near_the_anchored_limit(g_shift):
     for n in NAMES:
         assert np.isfinite(got[n]).all(), n
     _compare(got, _oracle(x), f"g_shift {g_shift}")
+
+
+# ---- packed sequences (cu_seqlens) ----
+
+def _packed_case(lens, Hq, Hv, seed, h0=True, dhT=True, beta_dtype=torch.float32, tail=0):
+    """One row of sum(lens) + tail tokens holding len(lens) sequences back to back;
+    the last `tail` tokens belong to no sequence."""
+    N, T = len(lens), sum(lens) + tail
+    x = make_inputs(1, T, Hq, Hv, beta_dtype, h0, N=N, seed=seed)
+    gen = torch.Generator("cpu").manual_seed(seed + 1000)
+    x["do"] = torch.randn(1, T, Hv, 128, generator=gen).to(torch.bfloat16)
+    x["dhT"] = torch.randn(N, Hv, 128, 128, generator=gen) if dhT else None
+    return x, cu_from_lengths(lens)
+
+
+def _packed_grads(x, cu, want_dh0=True, fill=None):
+    d = to_device(x)
+    grads = None
+    if fill is not None:   # prefilled outputs: rows the call must leave alone keep the fill
+        f32 = dict(device="cuda", dtype=torch.float32)
+        grads = {n: torch.full(tuple(d[src].shape), fill, **f32)
+                 for n, src in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"))}
+    g = kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, d["do"], initial_state=d["h0"],
+                d_final_state=d["dhT"], d_initial_state=want_dh0, grads=grads, cu_seqlens=cu.cuda())
+    torch.cuda.synchronize()
+    return {n: (None if t is None else t.cpu().numpy().astype(np.float64)) for n, t in g.items()}
+
+
+def _sequence(x, n, sl):
+    """Sequence n of a packed batch as a one-row batch of its own."""
+    sub = {key: x[key][:, sl] for key in ("q", "k", "v", "g", "beta", "do")}
+    sub["h0"] = None if x["h0"] is None else x["h0"][n:n + 1]
+    sub["dhT"] = None if x["dhT"] is None else x["dhT"][n:n + 1]
+    return sub
+
+
+def _compare_packed(got, x, cu, label, recurrence=False):
+    """Each sequence's gradients against the oracle run on that sequence alone."""
+    Hv = x["v"].shape[2]
+    for n, sl in enumerate(seq_slices(cu)):
+        sub = _sequence(x, n, sl)
+        part = {key: (got[key][:, sl] if key != "dh0" else got["dh0"][n:n + 1]) for key in NAMES}
+        if sl.stop == sl.start:   # an empty sequence passes the state gradient through
+            want = np.zeros((1, Hv, 128, 128)) if sub["dhT"] is None else _f64(sub["dhT"])
+            assert np.array_equal(part["dh0"], want), (label, n)
+            continue
+        _compare(part, _oracle(sub), f"{label} seq {n} ({sl.stop - sl.start} tokens)")
+        if recurrence:
+            h0 = sub["h0"] if sub["h0"] is not None else torch.zeros(1, Hv, 128, 128)
+            rec = og.grads(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], SCALE, h0, sub["do"], sub["dhT"])
+            _compare(part, rec, f"{label} seq {n} vs recurrence")
+
+
+@pytest.mark.parametrize("lens,Hq,Hv,h0,dhT,beta_dtype", [
+    ([1, 63, 64, 65, 130, 7], 2, 4, True, True, torch.float32),    # chunk starts off the 64-token grid, GVA
+    ([0, 200, 0, 0, 33], 1, 1, True, True, torch.bfloat16),          # empty sequences, bf16 beta
+    ([129], 2, 2, False, False, torch.float32),                       # one sequence, zero state
+])
+def test_bwd_packed_matches_oracle_per_sequence(lens, Hq, Hv, h0, dhT, beta_dtype):
+    x, cu = _packed_case(lens, Hq, Hv, seed=sum(lens) + len(lens), h0=h0, dhT=dhT, beta_dtype=beta_dtype)
+    _say(f"kda_bwd packed lens={lens} Hq={Hq} Hv={Hv} h0={h0} dhT={dhT} beta={beta_dtype}")
+    got = _packed_grads(x, cu)
+    _compare_packed(got, x, cu, f"packed {lens}", recurrence=sum(lens) <= 200)
+
+
+def test_bwd_packed_leaves_tokens_of_no_sequence_alone():
+    # 40 trailing tokens lie in no sequence: their gradient rows keep the NaN fill,
+    # every other row is written (finite)
+    lens, tail = [70, 5, 64], 40
+    for Hq, Hv in ((2, 2), (1, 4)):   # dq, dk written directly, and summed over a group
+        x, cu = _packed_case(lens, Hq, Hv, seed=31 + Hv, tail=tail)
+        _say(f"kda_bwd packed lens={lens} + {tail} uncovered tokens, Hq={Hq} Hv={Hv}")
+        got = _packed_grads(x, cu, fill=float("nan"))
+        covered = sum(lens)
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert np.isfinite(got[n][:, :covered]).all(), n
+            assert np.isnan(got[n][:, covered:]).all(), n
+        _compare_packed(got, x, cu, f"packed + tail Hv={Hv}")
+
+
+def test_bwd_packed_equal_lengths_is_the_fixed_batch_bit_for_bit():
+    # three sequences of 130 tokens packed into one row take the same chunks, in the
+    # same order of arithmetic, as a fixed-length batch of three rows
+    B, T, Hq, Hv = 3, 130, 2, 4
+    x = _case(B, T, Hq, Hv, seed=41)
+    _say("kda_bwd fixed B=3 T=130 against the same rows packed")
+    a = _gpu_grads(x)
+    packed = {key: (x[key].reshape(1, B * T, *x[key].shape[2:]) if key in ("q", "k", "v", "g", "beta", "do")
+                    else x[key]) for key in x}
+    b = _packed_grads(packed, cu_from_lengths([T] * B))
+    for n in NAMES:
+        want = a[n] if n == "dh0" else a[n].reshape(b[n].shape)
+        assert np.array_equal(b[n], want), n
+
+
+def test_bwd_packed_is_reproducible_and_takes_a_caller_workspace():
+    lens = [300, 1, 90]
+    x, cu = _packed_case(lens, 2, 4, seed=43)
+    need = kda_bwd_workspace_size(sum(lens), len(lens), 2, 4)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _say(f"kda_bwd packed lens={lens} twice, library and caller workspace")
+    a = _packed_grads(x, cu)
+    d = to_device(x)
+    g = kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, d["do"], initial_state=d["h0"],
+                d_final_state=d["dhT"], d_initial_state=True, workspace=ws, cu_seqlens=cu.cuda())
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert np.array_equal(a[n], g[n].cpu().numpy().astype(np.float64)), n
+
+
+def test_bwd_full_size_packed_sampled_heads():
+    # the 14-sequence, 16,384-token packed batch the forward is measured on, with an
+    # initial state, a random final-state gradient and dh0; two value heads checked
+    # on every sequence
+    from gated_delta_rule_35_amd.inputs import WORKLOADS
+    w = WORKLOADS["varlen_h64_16k"]
+    lens = varlen_lengths(w.varlen_total, w.length_seed)
+    x, cu = _packed_case(lens, w.Hq, w.Hv, seed=45)
+    _say(f"kda_bwd packed {len(lens)} sequences, {sum(lens)} tokens, H={w.Hv}")
+    got = _packed_grads(x, cu)
+    heads = [3, 60]
+    sub = head_subset(x, heads, w.Hq, w.Hv)
+    sub["do"] = x["do"][:, :, heads]
+    sub["dhT"] = x["dhT"][:, heads]
+    part = {n: (got[n][:, heads] if n == "dh0" else got[n][:, :, heads]) for n in NAMES}
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    _compare_packed(part, sub, cu, "full-size packed")

@@ -111,7 +111,7 @@ def test_kda_bwd_in_a_graph():
     torch.cuda.synchronize()
     names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
     outs = {n: torch.empty_like(ref[n]) for n in names}
-    ws = torch.empty(kda_bwd_workspace_size(2, 150, 2, 4), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kda_bwd_workspace_size(2 * 150, 2, 2, 4), dtype=torch.uint8, device="cuda")
     capture_and_replay(lambda: kda_bwd(*args, initial_state=d["h0"], d_final_state=dhT, grads=outs,
                                        d_initial_state=outs["dh0"], workspace=ws),
                        [outs[n] for n in names], [ref[n] for n in names])
