@@ -219,8 +219,9 @@ def bwd_macs_per_chunk(C=64, d=128):
 
 
 def bench_bwd(args):
-    """kda_bwd on --workload (fixed-length rows): HIP events around each call on
-    its stream, with a caller workspace so no allocation is timed."""
+    """kda_bwd on --workload (fixed-length rows, or packed sequences with
+    cu_seqlens): HIP events around each call on its stream, with a caller
+    workspace so no allocation is timed."""
     import torch
     from gated_delta_rule_35_amd import kda_bwd, kda_bwd_workspace_size
     from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
@@ -228,23 +229,23 @@ def bench_bwd(args):
         print("bench.py measures one GPU only", file=sys.stderr, flush=True)
         sys.exit(2)
     w = WORKLOADS[args.workload]
-    if w.varlen_total:
-        raise SystemExit("the backward takes fixed-length rows only")
     log(f"generating inputs for {args.workload}")
-    x, _ = workload_inputs(w)
-    B, T = w.B, w.T
+    x, cu = workload_inputs(w)
+    B, T = x["q"].shape[0], x["q"].shape[1]
+    lens = [T] * B if cu is None else [int(cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]
     gen = torch.Generator("cpu").manual_seed(1)
     do = torch.randn(B, T, w.Hv, 128, generator=gen).to(torch.bfloat16)
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     do_d = do.to(dev)
-    ws = torch.empty(kda_bwd_workspace_size(B * T, B, w.Hq, w.Hv), dtype=torch.uint8, device=dev)
+    cu_d = None if cu is None else cu.to(dev)
+    ws = torch.empty(kda_bwd_workspace_size(B * T, len(lens), w.Hq, w.Hv), dtype=torch.uint8, device=dev)
     grads = None
 
     def one():
         nonlocal grads
         grads = kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, do_d, initial_state=d["h0"],
-                        grads=grads, workspace=ws)
+                        grads=grads, workspace=ws, cu_seqlens=cu_d)
 
     stream = torch.cuda.current_stream(dev)
     settle(one)
@@ -261,8 +262,8 @@ def bench_bwd(args):
     wall = time.perf_counter() - t0
     ms = [e[0].elapsed_time(e[1]) for e in ev]
     t = sum(ms) / len(ms) / 1e3
-    n_tok = B * T
-    units = B * ((T + 63) // 64) * w.Hv
+    n_tok = sum(lens)
+    units = sum((n + 63) // 64 for n in lens) * w.Hv
     flops = 2 * bwd_macs_per_chunk() * units
     tf = flops / t / 1e12
     log(f"backward {args.workload}: call avg {t * 1e3:.3f} ms (min {min(ms):.3f}), {n_tok / t / 1e6:.2f} M tok/s, "
@@ -279,7 +280,13 @@ def bench_bwd(args):
         dos = f64(do[:, :, heads])
         reps, c0 = 0, time.perf_counter()
         while True:
-            og.chunked_grads(*sub, w.scale, h0, dos, None, chunk=64)
+            if cu is None:
+                og.chunked_grads(*sub, w.scale, h0, dos, None, chunk=64)
+            else:   # each packed sequence on its own
+                for n in range(len(lens)):
+                    a, z = int(cu[n]), int(cu[n + 1])
+                    og.chunked_grads(*[t[:, a:z] for t in sub], w.scale, None if h0 is None else h0[n:n + 1],
+                                     dos[:, a:z], None, chunk=64)
             reps += 1
             if time.perf_counter() - c0 >= args.cpu_seconds:
                 break
@@ -293,7 +300,8 @@ def bench_bwd(args):
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": args.workload, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128},
+           "config": {"workload": args.workload, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128,
+                      "sequences": len(lens), "packed": cu is not None},
            "call_ms_avg": round(t * 1e3, 4), "algorithmic_flops_per_call": flops,
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
