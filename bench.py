@@ -562,6 +562,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    t_enq = (time.perf_counter() - t0) / args.steps   # host time to enqueue a call
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -602,9 +603,30 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         call11()
+    t_enq11 = (time.perf_counter() - t0) / args.steps
     torch.cuda.synchronize()
     t_call11 = (time.perf_counter() - t0) / args.steps
     log(f"kda_fwd (eleven arguments, workspace allocated in the call) {t_call11 * 1e3:.4f} ms per call (wall)")
+
+    # The same step with the last-level cache flushed before each call: a 1 GiB
+    # buffer (four times the 256 MB MALL) is read between the calls, outside the
+    # events, so each call finds its inputs in HBM rather than in the cache the
+    # previous call left them in.  The flush only reads, so it leaves no dirty
+    # lines for the timed call to write back.  Workloads whose inputs fit in the
+    # cache (T = 512, 1024) read faster without the flush.
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    flush_sum = torch.zeros((), dtype=torch.float32, device=dev)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evc:
+        torch.sum(flush, 0, out=flush_sum)
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    cold = [e[0].elapsed_time(e[1]) for e in evc]
+    t_cold = sum(cold) / len(cold) / 1e3
+    del flush, flush_sum
+    log(f"kda_fwd_ws after a cache flush: {t_cold * 1e3:.4f} ms per call (min {min(cold):.4f})")
 
     # kda_fwd_fused, the single-pass kernel, on the same inputs (HIP events around
     # each call: one launch of kda_fused_kernel)
@@ -683,6 +705,13 @@ def main():
         "settle_s": SETTLE_S,
         "kernel_ms_avg": round(t_kern * 1e3, 5),
         "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
+        "host_enqueue_ms": {"kda_fwd_ws": round(t_enq * 1e3, 4), "kda_fwd": round(t_enq11 * 1e3, 4),
+                            "scope": "host time from the first call of the timed loop to the return of the last, "
+                                     "before the synchronisation, per call (argument checks, descriptor "
+                                     "marshalling, launches; kda_fwd also its stream-ordered allocation)"},
+        "cold_cache": {"ms_avg": round(t_cold * 1e3, 5), "tokens_per_s": round(n_tok / t_cold, 1),
+                       "scope": "kda_fwd_ws with a 1 GiB buffer read before each call (outside the HIP events), "
+                                "so no input is left in the 256 MB last-level cache"},
         "algorithmic_bytes_per_step": nbytes,
         "roofline": roofline,
         "fused": fused,
