@@ -4,4 +4,4 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU leg of ``bench.py``
 may import this package.  The GPU library never imports it and shares no code
 with it.
 """
-from .oracle import recurrence, chunked, num_chunks, load, threads  # noqa: F401
+from .oracle import recurrence, chunked, num_chunks, load, qg, threads  # noqa: F401

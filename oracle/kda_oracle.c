@@ -46,6 +46,14 @@
  * Partial chunks: a sequence is cut into chunks of C tokens from its own start;
  * the last chunk may be shorter.
  *
+ * A third function gives the optional QG output of the forward:
+ *   kda_oracle_qg          qg[t][hv][c] = q[t][hq(hv)][c] * exp(G[t][hv][c]), G the
+ *                          chunk-local inclusive cumsum of g.  The pages ("cuLA PR
+ *                          #131", Summary, and the Changes table of its walkthrough)
+ *                          list an optional QG output of the intra and recompute
+ *                          paths without defining it; this is the decayed query the
+ *                          output product uses, before the scale.
+ *
  * Every function returns 0 on success and -1 on invalid sizes.
  */
 #include <math.h>
@@ -286,4 +294,25 @@ int kda_oracle_chunked(const double* q, const double* k, const double* v, const 
     }
     free(chunk_base);
     return bad ? -1 : 0;
+}
+
+/* qg = q exp(G) per token, value head and key channel, with G the inclusive cumsum
+ * of g over the token's chunk (chunks of C tokens from each sequence's start).
+ * qg is [Ttot][Hv][dk]; tokens in no sequence are left as they are. */
+int kda_oracle_qg(const double* q, const double* g, const int64_t* cu, int64_t N, int64_t Hq, int64_t Hv,
+                  int64_t dk, int64_t C, double* qg) {
+    if (check_sizes(N, Hq, Hv, dk, 1, cu) != 0 || C <= 0) return -1;
+    const int64_t group = Hv / Hq;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t hv = 0; hv < Hv; ++hv)
+            for (int64_t c = 0; c < dk; ++c) {
+                const int64_t hq = hv / group;
+                double G = 0.0;
+                for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
+                    if ((t - cu[n]) % C == 0) G = 0.0;   /* a chunk starts: the cumsum restarts */
+                    G += g[(t * Hv + hv) * dk + c];
+                    qg[(t * Hv + hv) * dk + c] = q[(t * Hq + hq) * dk + c] * exp(G);
+                }
+            }
+    return 0;
 }

@@ -43,6 +43,8 @@ def load(path=None):
     lib.kda_oracle_chunked.restype = ctypes.c_int
     lib.kda_oracle_num_chunks.argtypes = [_ip, i64, i64]
     lib.kda_oracle_num_chunks.restype = i64
+    lib.kda_oracle_qg.argtypes = [_dp, _dp, _ip, i64, i64, i64, i64, i64, _dp]
+    lib.kda_oracle_qg.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = []
     lib.kda_oracle_threads.restype = ctypes.c_int
     if path is None:
@@ -134,3 +136,26 @@ def chunked(q, k, v, g, beta, scale, cu_seqlens=None, h0=None, chunk=64, interme
     if intermediates:
         return o, hT, inter
     return o, hT
+
+
+def qg(q, g, cu_seqlens=None, chunk=64, lib=None):
+    """The optional QG output, q exp(G) with G the chunk-local inclusive cumsum of
+    g, as an fp64 [B, T, Hv, dk] array (rows of tokens in no sequence are zero)."""
+    lib = lib or load()
+    q, g = _f64(q), _f64(g)
+    B, T, Hq, dk = q.shape
+    Hv = g.shape[2]
+    if g.shape != (B, T, Hv, dk) or Hv % Hq:
+        raise ValueError("inconsistent input shapes")
+    if cu_seqlens is None:
+        N, cu = B, np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                                             dtype=np.int64))
+        N = cu.shape[0] - 1
+    out = np.zeros((B, T, Hv, dk), np.float64)
+    if lib.kda_oracle_qg(_ptr(q), _ptr(g), cu.ctypes.data_as(_ip), N, Hq, Hv, dk, int(chunk), _ptr(out)) != 0:
+        raise RuntimeError("oracle qg rejected its inputs")
+    return out

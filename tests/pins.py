@@ -231,3 +231,44 @@ def pin_chunk_intermediates(rec, chk, seed=12):
         else:
             err = max(err, float(np.max(np.abs(im["h_c"][0, 0] - x["h0"][0, 0]))))
     return err
+
+
+# ---- the optional QG output (q exp(G), G the chunk-local inclusive cumsum) ----
+
+def pin_qg_zero_gate(qg_fn, seed=21):
+    """g = 0: nothing decays, so QG is q itself; with grouped values, value head hv
+    takes q/k head hv // (Hv / Hq)."""
+    c = rand_case(1, 150, 2, 4, 48, 8, seed, h0=False)
+    out = qg_fn(c["q"], np.zeros_like(c["g"]))
+    return _rel(out, np.repeat(c["q"], 2, axis=2))
+
+
+def pin_qg_constant_gate(qg_fn, seed=22):
+    """g constant per (value head, channel): token i of a chunk (counted from the
+    chunk's first token) has G = (i + 1) g, so QG = q exp((i + 1) g), and chunks
+    start every 64 tokens from each sequence's own first token (packed lengths
+    that put sequence starts off the 64-token grid, an empty sequence, tails)."""
+    lens = [0, 5, 64, 130, 1, 70]
+    T = sum(lens)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, T, 2, 48))
+    gc = -rng.uniform(0.0, 0.3, size=(4, 48))
+    g = np.broadcast_to(gc, (1, T, 4, 48)).copy()
+    cu = np.cumsum([0] + lens)
+    out = qg_fn(q, g, cu_seqlens=cu, chunk=64)
+    want = np.zeros_like(out)
+    for n in range(len(lens)):
+        for t in range(cu[n], cu[n + 1]):
+            i = (t - cu[n]) % 64
+            want[0, t] = np.repeat(q[0, t], 2, axis=0) * np.exp((i + 1) * gc)
+    return _rel(out, want)
+
+
+def pin_qg_matches_chunked_G(qg_fn, chk, seed=23):
+    """QG equals q exp(G) with the G that the chunked evaluation of the recurrence
+    (pinned above against the token recurrence) reports as its intermediate."""
+    c = rand_case(1, 200, 2, 4, 48, 8, seed, h0=False)
+    cu = np.array([0, 70, 70, 200])
+    _, _, inter = chk(c["q"], c["k"], c["v"], c["g"], c["beta"], 0.3, cu_seqlens=cu, chunk=64, intermediates=True)
+    want = np.repeat(c["q"], 2, axis=2) * np.exp(inter["G"].reshape(c["g"].shape))
+    return _rel(qg_fn(c["q"], c["g"], cu_seqlens=cu, chunk=64), want)

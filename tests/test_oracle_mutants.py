@@ -81,3 +81,48 @@ def test_planted_mistake_is_caught(name):
             if not err <= bound:
                 caught.append(i)
         assert caught, f"no pin caught the planted mistake {name}"
+
+
+# The optional QG output (kda_oracle_qg) against its own pins.
+QG_MUTANTS = {
+    "qg_no_chunk_restart": [("if ((t - cu[n]) % C == 0) G = 0.0;", "if (t == cu[n]) G = 0.0;")],
+    "qg_chunks_on_the_packed_grid": [("if ((t - cu[n]) % C == 0) G = 0.0;", "if (t % C == 0 || t == cu[n]) G = 0.0;")],
+    "qg_exclusive_cumsum": [("G += g[(t * Hv + hv) * dk + c];\n                    qg[(t * Hv + hv) * dk + c] = "
+                             "q[(t * Hq + hq) * dk + c] * exp(G);",
+                             "qg[(t * Hv + hv) * dk + c] = q[(t * Hq + hq) * dk + c] * exp(G);\n"
+                             "                    G += g[(t * Hv + hv) * dk + c];")],
+    "qg_gva_interleaved": [("const int64_t hq = hv / group;\n                double G", "const int64_t hq = hv % Hq;\n"
+                            "                double G")],
+    "qg_gate_dropped": [("* exp(G);\n", "* 1.0;\n")],
+}
+
+QG_PINS = [
+    (lambda f, c: pins.pin_qg_zero_gate(f), 0.0),
+    (lambda f, c: pins.pin_qg_constant_gate(f), 1e-14),
+    (lambda f, c: pins.pin_qg_matches_chunked_G(f, c), 1e-13),
+]
+
+
+@pytest.mark.parametrize("name", sorted(QG_MUTANTS))
+def test_planted_qg_mistake_is_caught(name):
+    src = open(SRC).read()
+    for old, new in QG_MUTANTS[name]:
+        assert old in src, f"mutation anchor for {name} not found"
+        src = src.replace(old, new, 1)
+    with tempfile.TemporaryDirectory() as d:
+        c_path, so_path = os.path.join(d, "m.c"), os.path.join(d, "m.so")
+        open(c_path, "w").write(src)
+        subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", so_path, c_path, "-lm"],
+                       check=True)
+        lib = load(so_path)
+        qg_fn = functools.partial(oracle.qg, lib=lib)
+        chk = functools.partial(oracle.chunked, lib=lib)
+        caught = []
+        for i, (pin, bound) in enumerate(QG_PINS):
+            try:
+                err = pin(qg_fn, chk)
+            except Exception:  # a crash or a rejected input also counts as caught
+                err = float("inf")
+            if not err <= bound:
+                caught.append(i)
+        assert caught, f"no pin caught the planted QG mistake {name}"

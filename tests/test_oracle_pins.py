@@ -85,3 +85,15 @@ def test_oracle_rejects_bad_sizes():
     y = pins.rand_case(1, 4, 1, 1, 4, 3, 16, N=2)
     with pytest.raises(RuntimeError):  # decreasing cu_seqlens
         oracle.recurrence(y["q"], y["k"], y["v"], y["g"], y["beta"], 1.0, cu_seqlens=np.array([0, 3, 2]))
+
+
+def test_qg_zero_gate_is_q():
+    assert pins.pin_qg_zero_gate(oracle.qg) == 0.0
+
+
+def test_qg_constant_gate_closed_form():
+    assert pins.pin_qg_constant_gate(oracle.qg) <= 1e-14
+
+
+def test_qg_matches_the_chunked_forms_G():
+    assert pins.pin_qg_matches_chunked_G(oracle.qg, oracle.chunked) <= 1e-13
