@@ -21,7 +21,7 @@ KDA_BF16, KDA_F16, KDA_F32, KDA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.bfloat16: KDA_BF16, torch.float16: KDA_F16, torch.float32: KDA_F32, torch.int32: KDA_I32}
 STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA_ERR_LAYOUT",
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
-EXPORTED = ["kda_fwd", "kda_fwd_fused", "kda_fwd_ws", "kda_fwd_noalloc", "kda_fwd_noalloc_max_bytes", "kda_fwd_intra",
+EXPORTED = ["kda_fwd", "kda_fwd_fused", "kda_fwd_ws", "kda_fwd_qg", "kda_fwd_noalloc", "kda_fwd_noalloc_max_bytes", "kda_fwd_intra",
             "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode", "kda_bwd", "kda_fwd_workspace_size",
             "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_bwd_workspace_size", "kda_status_string",
             "kda_dv_slices"]
@@ -72,6 +72,9 @@ def load_library(path=None):
     for name in ("kda_fwd_intra", "kda_fwd_scan"):
         getattr(lib, name).argtypes = lib.kda_fwd_ws.argtypes
         getattr(lib, name).restype = ctypes.c_int
+    lib.kda_fwd_qg.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, tp, ctypes.c_void_p,
+                               ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_fwd_qg.restype = ctypes.c_int
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
@@ -228,6 +231,31 @@ def kda_fwd_ws(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out
     _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace,
           "kda_fwd_ws")
     return out, final_state
+
+
+def kda_fwd_qg(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+               qg=None, stream=None, workspace=None):
+    """The forward with its QG output (C kda_fwd_qg): q exp(G), G the chunk-local
+    inclusive cumsum of g, bf16 of v's shape.  Returns (out, final_state, qg); out,
+    qg and final_state=True are allocated here when not given.  Without
+    `workspace` the C call allocates its records in stream order."""
+    out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
+    if qg is None:
+        qg = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    lib = load_library()
+    tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, qg)
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kda_fwd_qg needs every tensor on the GPU")
+    descs = [describe(t) for t in tensors]
+    s = _stream_handle(stream, tensors)
+    ws_ptr, ws_size = None, 0
+    if workspace is not None:
+        _ws, ws_ptr, ws_size = _workspace(workspace, q, v, cu_seqlens, stream)
+    _check(lib, lib.kda_fwd_qg(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
+                               float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8]),
+                               _ref(descs[9]), ws_ptr, ws_size, s))
+    return out, final_state, qg
 
 
 def kda_fwd_noalloc(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=None, final_state=None,

@@ -63,6 +63,14 @@ bool partly_overlap(const void* in, const void* out, int64_t bytes) {
     return a < b + bytes && b < a + bytes;
 }
 
+// Two byte ranges that share memory (empty ranges share none).
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (abytes <= 0 || bbytes <= 0 || !a || !b) return false;
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + bbytes && y < x + abytes;
+}
+
 bool same_shape(const kda_tensor_t* a, const int64_t* s, int nd) {
     for (int i = 0; i < nd; ++i)
         if (a->shape[i] != s[i]) return false;
@@ -144,11 +152,23 @@ kda_status_t finish(hipError_t e, hipStream_t hs) {
 kda_status_t run(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
                  const kda_tensor_t* beta, float scale, const kda_tensor_t* cu, const kda_tensor_t* h0,
                  const kda_tensor_t* out, const kda_tensor_t* hT, void* workspace, int64_t workspace_size,
-                 const kda_trace_t* trace, int stages, void* stream) {
+                 const kda_trace_t* trace, int stages, void* stream, const kda_tensor_t* qg = nullptr) {
     kda::KdaParams p;
     int64_t B, T, N;
     kda_status_t st = prepare(q, k, v, g, beta, scale, cu, h0, out, hT, p, B, T, N);
     if (st != KDA_OK) return st;
+    if (qg) {
+        // The optional QG output: v's shape, bf16, overlapping no input or output.
+        if ((st = check_tensor(qg, 4, KDA_BF16, KDA_BF16, 16)) != KDA_OK) return st;
+        const int64_t qs[4] = {B, T, (int64_t)p.Hv, kHeadDim};
+        if (!same_shape(qg, qs, 4)) return KDA_ERR_SHAPE;
+        const int64_t qb = B * T * p.Hv * kHeadDim * 2;
+        const kda_tensor_t* others[] = {q, k, v, g, beta, out, h0, hT};
+        for (const kda_tensor_t* t : others)
+            if (t && ranges_overlap(qg->data, qb, t->data, numel(t) * (int64_t)elem_size(t->dtype)))
+                return KDA_ERR_LAYOUT;
+        p.qg = static_cast<uint16_t*>(qg->data);
+    }
     const int64_t Hv = p.Hv;
     const int S = kda::scan_slices();
     if (N * Hv * S > kMaxBlocks) return KDA_ERR_UNSUPPORTED;
@@ -258,6 +278,15 @@ kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
     if (!workspace) return KDA_ERR_WORKSPACE;
     return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
                nullptr, kBoth, stream);
+}
+
+kda_status_t kda_fwd_qg(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
+                        const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
+                        const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
+                        const kda_tensor_t* qg, void* workspace, int64_t workspace_size, void* stream) {
+    if (!qg) return KDA_ERR_NULL;
+    return run(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, workspace, workspace_size,
+               nullptr, kBoth, stream, qg);
 }
 
 int64_t kda_fwd_noalloc_max_bytes(void) { return kda::NOALLOC_SCRATCH_BYTES; }

@@ -185,7 +185,7 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int j) {
 
 }  // namespace
 
-template <bool TRACE>
+template <bool TRACE, bool QGO>
 __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams p) {
     using L = IntraLds;
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -386,6 +386,17 @@ __global__ void __launch_bounds__(NTHREADS, 4) kda_intra_kernel(const KdaParams 
     // four lanes of a quad; (k e^{G_last - G})^T per channel as its eight rows.
     {
         const float sq0 = p.scale * eb[0], sq1 = p.scale * eb[1];
+        if constexpr (QGO) {
+            // The QG output, q e^G = q F e^{G_b} (no scale), rounded once to bf16:
+            // each row is one 256-byte run over the wave's 64 channel pairs.
+            uint16_t* qgo = p.qg + (tok0 + 8 * hb) * v_tok + (int64_t)hv * DK + 2 * cp;
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                if (8 * hb + rr < Lc)
+                    *reinterpret_cast<uint32_t*>(qgo + rr * v_tok) =
+                        pack_bf2(bf_lo(qw[rr]) * F[rr][0] * eb[0], bf_hi(qw[rr]) * F[rr][1] * eb[1]);
+            }
+        }
         uint32_t qg[8], kg[8];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
@@ -682,9 +693,11 @@ hipError_t launch_kda_intra(const KdaParams& p, bool trace, hipStream_t stream) 
     const int64_t nblocks = p.nslots * p.Hv;
     if (nblocks == 0) return hipSuccess;
     if (trace)
-        hipLaunchKernelGGL((kda_intra_kernel<true>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
+        hipLaunchKernelGGL((kda_intra_kernel<true, false>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
+    else if (p.qg)
+        hipLaunchKernelGGL((kda_intra_kernel<false, true>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_intra_kernel<false>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
+        hipLaunchKernelGGL((kda_intra_kernel<false, false>), dim3((unsigned)nblocks), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

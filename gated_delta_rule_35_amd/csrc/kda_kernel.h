@@ -43,6 +43,10 @@ struct KdaParams {
     float* tr_U;
     float* tr_vnew;
     float* tr_h;
+    // Optional QG output: q e^G per token, value head and key channel, G the
+    // chunk-local inclusive cumsum of g ([tokens, Hv, 128] bf16 bits; nullptr: not
+    // written).  Only the intra kernel writes it.
+    uint16_t* qg;
 };
 
 // One recurrent step for a batch of single tokens (decode).

@@ -160,7 +160,32 @@ kda_status_t kda_fwd_ws(const kda_tensor_t* q, const kda_tensor_t* k, const kda_
                         void* workspace, int64_t workspace_size, void* stream);
 
 /*
- * kda_fwd_noalloc -- kda_fwd_ws without a workspace argument and without any
+ * kda_fwd_qg -- the forward with its optional QG output ("cuLA PR #131: SM100/
+ * SM103 KDA forward to pure CuTeDSL", Summary, lists an optional QG among the
+ * forward's outputs and its Changes table the intra and recompute paths that
+ * produce it; no page defines it).  Read here as the decayed query of the output
+ * product, before the scale:
+ *   qg[b, t, hv, c] = q[b, t, hv / (Hv / Hq), c] * exp(G[b, t, hv, c]),
+ * G the chunk-local inclusive cumsum of g (chunks of 64 tokens from each
+ * sequence's start), computed in fp32 and rounded once to bf16 (nearest even).
+ * qg: [B, T, Hv, 128] bf16 (v's shape), contiguous, 16-byte aligned, device
+ * memory owned by the caller, sharing no byte with any other tensor argument;
+ * NULL returns KDA_ERR_NULL.  Rows of tokens outside every sequence (packed
+ * batches whose last offset is below T) are not written.
+ * workspace, workspace_size: as kda_fwd_ws; workspace NULL allocates the
+ * records in stream order on `stream`, as kda_fwd does.
+ * out and final_state are bitwise those of kda_fwd_ws on the same inputs.
+ * Errors: as kda_fwd_ws, plus KDA_ERR_DTYPE / KDA_ERR_SHAPE / KDA_ERR_LAYOUT for
+ * a qg of the wrong dtype, shape, layout or one that overlaps another tensor.
+ */
+kda_status_t kda_fwd_qg(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
+                        const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
+                        const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                        const kda_tensor_t* out, const kda_tensor_t* final_state, const kda_tensor_t* qg,
+                        void* workspace, int64_t workspace_size, void* stream);
+
+/*
+ * kda_fwd_noalloc --kda_fwd_ws without a workspace argument and without any
  * allocation, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *

@@ -520,3 +520,31 @@ def test_binding_refuses_host_tensors():
         kda_bwd(q, q, q, g, beta, 0.1, q)
     with pytest.raises(ValueError):
         kda_decode(q[:, 0], q[:, 0], q[:, 0], g[:, 0], beta[:, 0], 0.1, None)
+
+
+def call_qg(lib, a, qg, scale=0.088):
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    return lib.kda_fwd_qg(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale,
+                          None, None, r(a.get("out")), None, r(qg), None, 0, None)
+
+
+def test_qg_output_is_checked_before_any_hip_call(lib):
+    """kda_fwd_qg: a NULL qg, a qg of the wrong dtype or shape, a non-contiguous or
+    misaligned one, or one that overlaps another tensor is refused on the host; the
+    forward's own checks still apply."""
+    name = lambda st: binding.STATUS_NAMES[st]  # noqa: E731
+    qg_addr = FAKE + (1 << 30)
+    assert name(call_qg(lib, good(), None)) == "KDA_ERR_NULL"
+    assert name(call_qg(lib, good(), T([1, 64, 2, 128], binding.KDA_F32, data=qg_addr))) == "KDA_ERR_DTYPE"
+    assert name(call_qg(lib, good(), T([1, 64, 4, 128], data=qg_addr))) == "KDA_ERR_SHAPE"
+    assert name(call_qg(lib, good(), T([1, 64, 2], data=qg_addr))) == "KDA_ERR_SHAPE"
+    assert name(call_qg(lib, good(), T([1, 64, 2, 128], data=qg_addr + 2))) == "KDA_ERR_LAYOUT"
+    assert name(call_qg(lib, good(), T([1, 64, 2, 128], data=qg_addr,
+                                       strides=[64 * 256, 128, 64 * 128, 1]))) == "KDA_ERR_LAYOUT"
+    a = good()
+    a["out"] = T([1, 64, 2, 128], data=qg_addr + 4096)   # out inside qg's bytes
+    assert name(call_qg(lib, a, T([1, 64, 2, 128], data=qg_addr))) == "KDA_ERR_LAYOUT"
+    a = good()
+    a["v"] = None
+    assert name(call_qg(lib, a, T([1, 64, 2, 128], data=qg_addr))) == "KDA_ERR_NULL"
+    assert name(call_qg(lib, good(), T([1, 64, 2, 128], data=qg_addr), scale=-1.0)) == "KDA_ERR_VALUE"
