@@ -122,6 +122,83 @@ def load_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def torch_float32():
+    import torch
+    return torch.float32
+
+
+def _counter_medians(folder, counter):
+    """Median per dispatch of `counter` for every kernel name in the rocprofv3
+    counter-collection CSV files under `folder`."""
+    import csv
+    import glob
+    vals = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    out = {}
+    for name, v in vals.items():
+        v = sorted(v)
+        out[name] = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return out
+
+
+def write_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """profiles/traffic_kda_fwd_<workload>.json from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch, median over dispatches), each scaled by what
+    the same counter reads for a 1 GiB device copy (bench.py --calibrate-copy)."""
+    from gated_delta_rule_35_amd.inputs import WORKLOADS, varlen_lengths
+    w = WORKLOADS[workload]
+    lengths = varlen_lengths(w.varlen_total, w.length_seed) if w.varlen_total else [w.T] * w.B
+    n_tok, N = sum(lengths), len(lengths)
+    beta_bytes = 4 if w.beta_dtype == torch_float32() else 2
+    copy_bytes = 1 << 30
+    cf = [v for k, v in _counter_medians(copy_fetch_dir, "FETCH_SIZE").items() if "copyBuffer" in k]
+    cw = [v for k, v in _counter_medians(copy_write_dir, "WRITE_SIZE").items() if "copyBuffer" in k]
+    if not cf or not cw:
+        raise SystemExit("no copy kernel in the calibration runs")
+    fetch_scale = copy_bytes / (cf[0] * 1024.0)
+    write_scale = copy_bytes / (cw[0] * 1024.0)
+    fetch = _counter_medians(fetch_dir, "FETCH_SIZE")
+    write = _counter_medians(write_dir, "WRITE_SIZE")
+    alg = kernel_bytes(n_tok, chunk_heads(lengths, w.Hv), N, w.Hq, w.Hv, beta_bytes, w.has_h0)
+    alg["kda_fused_kernel"] = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
+    per, hbm = {}, {}
+    for short in ("kda_intra_kernel", "kda_scan_kernel", "kda_fused_kernel"):
+        fk = [k for k in fetch if short in k]
+        wk = [k for k in write if short in k]
+        if not fk or not wk:
+            continue
+        rd, wr = fetch[fk[0]] * 1024.0 * fetch_scale, write[wk[0]] * 1024.0 * write_scale
+        per[short] = {"fetch_size_kib_per_dispatch": fetch[fk[0]], "write_size_kib_per_dispatch": write[wk[0]],
+                      "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr), "hbm_bytes": int(rd + wr),
+                      "algorithmic_bytes": alg.get(short)}
+        hbm[short] = int(rd + wr)
+    rec = {"workload": workload, "kernel_source_sha256": kernel_sha(),
+           "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": cf[0], "write_size_kib": cw[0],
+                                "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+           "per_kernel": per, "hbm_bytes_per_launch": hbm,
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o kda -- python3 bench.py "
+               f"--workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o kda -- python3 bench.py "
+               f"--workload {workload} --steps 3 --warmup 1 --no-cpu-baseline",
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {copy_fetch_dir} -o copy -- python3 bench.py "
+               "--calibrate-copy",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {copy_write_dir} -o copy -- python3 bench.py "
+               "--calibrate-copy",
+               f"python3 bench.py --workload {workload} --write-traffic {fetch_dir} {write_dir} "
+               f"{copy_fetch_dir} {copy_write_dir}"]}
+    path = os.path.join(ROOT, "profiles", f"traffic_kda_fwd_{workload}.json")
+    json.dump(rec, open(path, "w"), indent=1)
+    print(json.dumps(rec["hbm_bytes_per_launch"]))
+
+
 def decode_bytes(N, Hq, Hv, beta_bytes, d=128):
     """Algorithmic bytes of one decode step: the state read and written once, the
     token's q, k (per q/k head), v, g, beta and o (per value head)."""
@@ -395,26 +472,29 @@ def bench_cp(args):
     HIP events around each whole call (intra kernel, two scan launches and the
     composition) on its stream, and kda_fwd on the same inputs for comparison."""
     import torch
-    from gated_delta_rule_35_amd import (kda_fwd, kda_fwd_cp, kda_fwd_cp_plan, kda_fwd_cp_workspace_size,
-                                         kda_fwd_workspace_size)
+    from gated_delta_rule_35_amd import (kda_fwd, kda_fwd_cp, kda_fwd_cp_packed_workspace_size, kda_fwd_cp_plan,
+                                         kda_fwd_cp_workspace_size, kda_fwd_workspace_size)
     from gated_delta_rule_35_amd.inputs import WORKLOADS, workload_inputs
     if args.gpus != 1:
         print("bench.py measures one GPU only", file=sys.stderr, flush=True)
         sys.exit(2)
     w = WORKLOADS[args.workload]
-    if w.varlen_total:
-        print("the segmented forward takes fixed-length batches only", file=sys.stderr, flush=True)
-        sys.exit(2)
     log(f"generating inputs for {w.name}")
-    x, _ = workload_inputs(w)
+    x, cu = workload_inputs(w)
     B, T = x["q"].shape[0], x["q"].shape[1]
     n_tok = B * T
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    cu_d = cu.to(dev) if cu is not None else None
+    N = B if cu is None else len(cu) - 1
     out = torch.empty_like(d["v"])
-    hT = torch.empty((B, w.Hv, 128, 128), dtype=torch.float32, device=dev)
+    hT = torch.empty((N, w.Hv, 128, 128), dtype=torch.float32, device=dev)
     if args.cp > 0:
         L, L0 = args.cp, (args.cp_first or args.cp)
+    elif cu is not None:
+        print("packed workloads: pass --cp N (and --cp-first N0); the plan needs the lengths", file=sys.stderr,
+              flush=True)
+        sys.exit(2)
     else:
         pl = kda_fwd_cp_plan(B, T, w.Hv)
         if pl is None:
@@ -422,10 +502,13 @@ def bench_cp(args):
                   "pass --cp N to force N chunks per segment", file=sys.stderr, flush=True)
             sys.exit(2)
         L, L0 = pl
-    nch = (T + 63) // 64
-    P = 1 if nch <= L0 else 1 + -(-(nch - L0) // L)
-    ws_cp = torch.empty(kda_fwd_cp_workspace_size(B, T, w.Hv, L, L0), dtype=torch.uint8, device=dev)
-    ws = torch.empty(kda_fwd_workspace_size(B * T, B, w.Hv), dtype=torch.uint8, device=dev)
+    lens = [T] * B if cu is None else [int(cu[i + 1] - cu[i]) for i in range(N)]
+    P = max(1 if (n + 63) // 64 <= L0 else 1 + -(-((n + 63) // 64 - L0) // L) for n in lens)
+    if cu is None:
+        ws_cp = torch.empty(kda_fwd_cp_workspace_size(B, T, w.Hv, L, L0), dtype=torch.uint8, device=dev)
+    else:
+        ws_cp = torch.empty(kda_fwd_cp_packed_workspace_size(n_tok, N, w.Hv, L, L0), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda_fwd_workspace_size(B * T, N, w.Hv), dtype=torch.uint8, device=dev)
     a = (d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale)
     stream = torch.cuda.current_stream(dev)
 
@@ -445,25 +528,27 @@ def bench_cp(args):
         ms = [e[0].elapsed_time(e[1]) for e in ev]
         return wall / args.steps * 1e3, sum(ms) / len(ms)
 
-    log(f"kda_fwd_cp: first segment {L0} chunks, then {L} per segment, {P} segments per row; {args.steps} steps")
+    log(f"kda_fwd_cp: first segment {L0} chunks, then {L} per segment, up to {P} segments per sequence; "
+        f"{args.steps} steps")
     step_ms, call_ms = timed(lambda: kda_fwd_cp(*a, L, L0, initial_state=d["h0"], out=out, final_state=hT,
-                                                workspace=ws_cp))
+                                                workspace=ws_cp, cu_seqlens=cu_d))
     log(f"kda_fwd (ordinary): {args.steps} steps")
-    plain_step_ms, plain_call_ms = timed(lambda: kda_fwd(*a, initial_state=d["h0"], out=out, final_state=hT,
-                                                         workspace=ws))
+    plain_step_ms, plain_call_ms = timed(lambda: kda_fwd(*a, cu_seqlens=cu_d, initial_state=d["h0"], out=out,
+                                                         final_state=hT, workspace=ws))
     log(f"segmented {call_ms:.4f} ms/call, ordinary {plain_call_ms:.4f} ms/call ({plain_call_ms / call_ms:.2f}x)")
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
-    nbytes = algorithmic_bytes(n_tok, B, w.Hq, w.Hv, beta_bytes, w.has_h0)
+    nbytes = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
     gbs = nbytes / (call_ms / 1e3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = oracle_cpu_baseline(x, None, w, B, n_tok, w.scale, args.cpu_seconds, args.cpu_heads)
+        cpu = oracle_cpu_baseline(x, cu, w, N, n_tok, w.scale, args.cpu_seconds, args.cpu_heads)
     rec = {"metric": "KDA fwd tokens/s, segmented scan (context parallelism inside one GPU); ms/call",
            "value": round(n_tok / (step_ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-           "config": {"workload": w.name, "B": B, "T": T, "Hq": w.Hq, "Hv": w.Hv, "dk": 128, "dv": 128, "chunk": 64,
-                      "segment_chunks": L, "first_segment_chunks": L0, "segments_per_row": P,
+           "config": {"workload": w.name, "B": B, "T": T, "N_sequences": N, "Hq": w.Hq, "Hv": w.Hv, "dk": 128,
+                      "dv": 128, "chunk": 64, "segment_chunks": L, "first_segment_chunks": L0,
+                      "max_segments_per_sequence": P, "packed": cu is not None,
                       "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0)},
            "call_ms_avg": round(call_ms, 5), "ordinary_kda_fwd_ms_avg": round(plain_call_ms, 5),
            "speedup_vs_ordinary": round(plain_call_ms / call_ms, 3),
@@ -499,7 +584,13 @@ def main():
                     help="instead of the forward, time the backward kda_bwd on --workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the benchmark, run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU: turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of this "
+                         "benchmark on --workload, then of --calibrate-copy) into profiles/traffic_kda_fwd_<workload>.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic)
+        return
     if args.calibrate_copy:
         import torch
         a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB

@@ -23,7 +23,7 @@ STATUS_NAMES = ["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_DTYPE", "KDA_ERR_SHAPE", "KDA
                 "KDA_ERR_UNSUPPORTED", "KDA_ERR_VALUE", "KDA_ERR_HIP", "KDA_ERR_WORKSPACE"]
 EXPORTED = ["kda_fwd", "kda_fwd_fused", "kda_fwd_ws", "kda_fwd_qg", "kda_fwd_noalloc", "kda_fwd_noalloc_max_bytes", "kda_fwd_intra",
             "kda_fwd_scan", "kda_fwd_trace", "kda_fwd_cp", "kda_decode", "kda_bwd", "kda_fwd_workspace_size",
-            "kda_fwd_cp_workspace_size", "kda_fwd_cp_plan", "kda_bwd_workspace_size", "kda_status_string",
+            "kda_fwd_cp_workspace_size", "kda_fwd_cp_packed_workspace_size", "kda_fwd_cp_plan", "kda_bwd_workspace_size", "kda_status_string",
             "kda_dv_slices"]
 
 
@@ -78,11 +78,13 @@ def load_library(path=None):
     lib.kda_fwd_trace.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_void_p,
                                   ctypes.c_int64, ctypes.POINTER(KdaTrace), ctypes.c_void_p]
     lib.kda_fwd_trace.restype = ctypes.c_int
-    lib.kda_fwd_cp.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, ctypes.c_int64, ctypes.c_int64,
+    lib.kda_fwd_cp.argtypes = [tp, tp, tp, tp, tp, ctypes.c_float, tp, tp, tp, tp, ctypes.c_int64, ctypes.c_int64,
                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.kda_fwd_cp.restype = ctypes.c_int
     lib.kda_fwd_cp_workspace_size.argtypes = [ctypes.c_int64] * 5
     lib.kda_fwd_cp_workspace_size.restype = ctypes.c_int64
+    lib.kda_fwd_cp_packed_workspace_size.argtypes = [ctypes.c_int64] * 5
+    lib.kda_fwd_cp_packed_workspace_size.restype = ctypes.c_int64
     lib.kda_fwd_cp_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.kda_fwd_cp_plan.restype = ctypes.c_int32
@@ -304,6 +306,12 @@ def kda_fwd_cp_workspace_size(batch, seq_len, num_value_heads, segment_chunks, f
                                                         first_segment_chunks))
 
 
+def kda_fwd_cp_packed_workspace_size(total_tokens, num_sequences, num_value_heads, segment_chunks,
+                                     first_segment_chunks=0):
+    return int(load_library().kda_fwd_cp_packed_workspace_size(total_tokens, num_sequences, num_value_heads,
+                                                               segment_chunks, first_segment_chunks))
+
+
 def kda_fwd_cp_plan(batch, seq_len, num_value_heads, num_cus=None):
     """(segment_chunks, first_segment_chunks) for kda_fwd_cp, or None when kda_fwd
     is about as fast.  num_cus defaults to the current GPU's compute units."""
@@ -316,36 +324,42 @@ def kda_fwd_cp_plan(batch, seq_len, num_value_heads, num_cus=None):
 
 
 def kda_fwd_cp(q, k, v, g, beta, scale, segment_chunks, first_segment_chunks=0, initial_state=None, out=None,
-               final_state=None, stream=None, workspace=None):
-    """kda_fwd for a fixed-length batch with each sequence cut into segments (the
-    first of `first_segment_chunks` chunks, 0: `segment_chunks`, the others of
-    `segment_chunks`) that the scan walks side by side (see include/kda.h).
-    Returns (out, final_state); final_state=True allocates it.  `workspace`: a
-    uint8 device tensor of at least kda_fwd_cp_workspace_size() bytes, or None
-    (allocated here from torch's caching allocator)."""
+               final_state=None, stream=None, workspace=None, cu_seqlens=None):
+    """kda_fwd with each sequence cut into segments (the first of
+    `first_segment_chunks` chunks, 0: `segment_chunks`, the others of
+    `segment_chunks`) that the scan walks side by side (see include/kda.h); a
+    fixed-length batch, or packed sequences with `cu_seqlens`.  Returns (out,
+    final_state); final_state=True allocates it.  `workspace`: a uint8 device
+    tensor of at least kda_fwd_cp_workspace_size() (fixed length) or
+    kda_fwd_cp_packed_workspace_size() bytes (packed), or None (allocated here
+    from torch's caching allocator)."""
     lib = load_library()
     if out is None:
         out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    n_seq = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
     if final_state is True:
-        final_state = torch.empty((q.shape[0], v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32,
+        final_state = torch.empty((n_seq, v.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32,
                                   device=v.device)
-    tensors = (q, k, v, g, beta, initial_state, out, final_state)
+    tensors = (q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
     for t in tensors:
         if t is not None and not t.is_cuda:
             raise ValueError("kda_fwd_cp needs every tensor on the GPU")
     descs = [describe(t) for t in tensors]
     s = _stream_handle(stream, tensors)
     if workspace is None and q.dim() == 4 and v.dim() == 4:
-        size = kda_fwd_cp_workspace_size(q.shape[0], q.shape[1], v.shape[2], max(int(segment_chunks), 1),
-                                         max(int(first_segment_chunks), 0))
+        L, L0 = max(int(segment_chunks), 1), max(int(first_segment_chunks), 0)
+        if cu_seqlens is None:
+            size = kda_fwd_cp_workspace_size(q.shape[0], q.shape[1], v.shape[2], L, L0)
+        else:
+            size = kda_fwd_cp_packed_workspace_size(q.shape[0] * q.shape[1], max(n_seq, 0), v.shape[2], L, L0)
         workspace = torch.empty(max(size, 0), dtype=torch.uint8, device=v.device)
         if stream is not None and isinstance(stream, torch.cuda.Stream):
             workspace.record_stream(stream)
     ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
     ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib, lib.kda_fwd_cp(_ref(descs[0]), _ref(descs[1]), _ref(descs[2]), _ref(descs[3]), _ref(descs[4]),
-                               float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), int(segment_chunks),
-                               int(first_segment_chunks), ws_ptr, ws_size, s))
+                               float(scale), _ref(descs[5]), _ref(descs[6]), _ref(descs[7]), _ref(descs[8]),
+                               int(segment_chunks), int(first_segment_chunks), ws_ptr, ws_size, s))
     return out, final_state
 
 

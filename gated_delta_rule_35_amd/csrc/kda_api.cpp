@@ -8,6 +8,7 @@
 // #131", review of the public forward: inputs made contiguous after validation).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -234,6 +235,45 @@ SegLayout seg_layout(int64_t B, int64_t T, int64_t Hv, int64_t seg_chunks, int64
     return c;
 }
 
+// Workspace of a segmented call over packed sequences (planned on the device):
+// the records of every segment, the maps M and offsets b of the middle segments
+// and the states entering the later segments (each [lat_max][Hv][128][128] fp32),
+// then the plan's tables.  Sizes are bounds: with TC = ceil(T / 64) + N chunks at
+// most, there are at most TC / L + min(N, TC / (L0 + 1)) + 1 later segments.
+struct PackedLayout {
+    int64_t S_max = 0, lat_max = 0, nslots = 0;
+    int64_t rec = 0, maps = 0, cu_seg = 0, first = 0, mid_m = 0, mid_b = 0, later = 0, chains = 0, total = 0;
+};
+
+PackedLayout packed_layout(int64_t T, int64_t N, int64_t Hv, int64_t L, int64_t L0) {
+    PackedLayout c;
+    auto al = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    const int64_t tc = (T + 63) / 64 + N;
+    c.lat_max = tc / L + std::min<int64_t>(N, tc / (L0 + 1)) + 1;
+    c.S_max = N + c.lat_max;
+    c.nslots = (T + 63) / 64 + c.S_max + 1;
+    const int64_t blk = Hv * kHeadDim * kHeadDim * 4;   // one state
+    int64_t o = al(kda::workspace_bytes(0, c.nslots, Hv));   // records: one per slot and value head
+    c.rec = 0;
+    c.maps = o;                       // M, then b, then the entering states
+    o = al(o + 3 * c.lat_max * blk);
+    c.cu_seg = o;
+    o = al(o + (c.S_max + 2) * 4);
+    const int64_t es = (int64_t)sizeof(kda::ScanEntry);
+    c.first = o;
+    o = al(o + N * es);
+    c.mid_m = o;
+    o = al(o + c.lat_max * es);
+    c.mid_b = o;
+    o = al(o + c.lat_max * es);
+    c.later = o;
+    o = al(o + c.lat_max * es);
+    c.chains = o;
+    o = al(o + N * 3 * 4);
+    c.total = o;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,16 +424,101 @@ int32_t kda_fwd_cp_plan(int64_t batch, int64_t seq_len, int64_t num_value_heads,
     return 1;
 }
 
+int64_t kda_fwd_cp_packed_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads,
+                                         int64_t segment_chunks, int64_t first_segment_chunks) {
+    if (total_tokens < 0 || num_sequences < 0 || num_value_heads < 0 || segment_chunks < 1 || first_segment_chunks < 0)
+        return -1;
+    const int64_t first_chunks = first_segment_chunks ? first_segment_chunks : segment_chunks;
+    return packed_layout(total_tokens, num_sequences, num_value_heads, segment_chunks, first_chunks).total;
+}
+
 kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v, const kda_tensor_t* g,
-                        const kda_tensor_t* beta, float scale, const kda_tensor_t* initial_state,
-                        const kda_tensor_t* out, const kda_tensor_t* final_state, int64_t segment_chunks,
-                        int64_t first_segment_chunks, void* workspace, int64_t workspace_size, void* stream) {
+                        const kda_tensor_t* beta, float scale, const kda_tensor_t* cu_seqlens,
+                        const kda_tensor_t* initial_state, const kda_tensor_t* out, const kda_tensor_t* final_state,
+                        int64_t segment_chunks, int64_t first_segment_chunks, void* workspace, int64_t workspace_size,
+                        void* stream) {
     kda::KdaParams p;
     int64_t B, T, N;
-    kda_status_t st = prepare(q, k, v, g, beta, scale, nullptr, initial_state, out, final_state, p, B, T, N);
+    kda_status_t st = prepare(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, p, B, T, N);
     if (st != KDA_OK) return st;
     if (segment_chunks < 1 || first_segment_chunks < 0) return KDA_ERR_VALUE;
     const int64_t first_chunks = first_segment_chunks ? first_segment_chunks : segment_chunks;
+    if (cu_seqlens) {
+        // Packed sequences: the segment boundaries depend on cu_seqlens, which the
+        // host does not read; a plan kernel derives them (and every job's list)
+        // on the device, within bounds the host computes from the shapes.
+        const int64_t Hv = p.Hv;
+        const PackedLayout c = packed_layout(T, N, Hv, segment_chunks, first_chunks);
+        if (!workspace || workspace_size < c.total || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return KDA_ERR_WORKSPACE;
+        const int S = kda::scan_slices();
+        if (c.nslots * Hv > kMaxBlocks || (N + 2 * c.lat_max) * Hv * S > kMaxBlocks || c.S_max > (int64_t(1) << 24))
+            return KDA_ERR_UNSUPPORTED;
+        if (N == 0 || (T == 0 && !final_state)) return KDA_OK;
+        char* ws = static_cast<char*>(workspace);
+        const int64_t blk_f = Hv * kHeadDim * kHeadDim;
+        kda::CpPlan pl{};
+        pl.cu = static_cast<const int32_t*>(cu_seqlens->data);
+        pl.N = static_cast<int32_t>(N);
+        pl.T = T;
+        pl.L = segment_chunks;
+        pl.L0 = first_chunks;
+        pl.hv_dd = blk_f;
+        pl.h0 = p.h0;
+        pl.hT = p.hT;
+        pl.Mb = reinterpret_cast<float*>(ws + c.maps);
+        pl.Bb = pl.Mb + c.lat_max * blk_f;
+        pl.Hin = pl.Bb + c.lat_max * blk_f;
+        pl.cu_seg = reinterpret_cast<int32_t*>(ws + c.cu_seg);
+        pl.S_max = static_cast<int32_t>(c.S_max);
+        pl.lat_max = static_cast<int32_t>(c.lat_max);
+        pl.first = reinterpret_cast<kda::ScanEntry*>(ws + c.first);
+        pl.mid_m = reinterpret_cast<kda::ScanEntry*>(ws + c.mid_m);
+        pl.mid_b = reinterpret_cast<kda::ScanEntry*>(ws + c.mid_b);
+        pl.later = reinterpret_cast<kda::ScanEntry*>(ws + c.later);
+        pl.chains = reinterpret_cast<int32_t*>(ws + c.chains);
+        const hipStream_t hs = static_cast<hipStream_t>(stream);
+        hipError_t e = kda::launch_kda_cp_plan(pl, hs);
+        // 1. intra kernel over every segment (record sequence = segment)
+        kda::KdaParams ps = p;
+        ps.cu = pl.cu_seg;
+        ps.N = static_cast<int32_t>(c.S_max + 1);
+        ps.nslots = c.nslots;
+        ps.ws = ws + c.rec;
+        ps.h0 = nullptr;
+        ps.hT = nullptr;
+        if (e == hipSuccess && T > 0) e = kda::launch_kda_intra(ps, false, hs);
+        // 2. segment 0 of every sequence, and the maps of the middle segments
+        kda::ScanJobs J1{};
+        J1.njobs = 3;
+        J1.job[0] = ps;
+        J1.job[0].N = static_cast<int32_t>(N);
+        J1.job[0].entries = pl.first;
+        J1.job[1] = ps;
+        J1.job[1].N = static_cast<int32_t>(c.lat_max);
+        J1.job[1].entries = pl.mid_m;
+        J1.job[1].h0_identity = 1;
+        J1.job[1].v_zero = 1;
+        J1.job[1].o = nullptr;
+        J1.job[2] = ps;
+        J1.job[2].N = static_cast<int32_t>(c.lat_max);
+        J1.job[2].entries = pl.mid_b;
+        J1.job[2].o = nullptr;
+        if (e == hipSuccess) e = kda::launch_kda_scan_jobs(J1, hs);
+        // 3. the states entering the later segments, per sequence
+        if (e == hipSuccess)
+            e = kda::launch_kda_compose_chains(pl.Mb, pl.Bb, pl.Hin, pl.chains, static_cast<int>(N),
+                                               static_cast<int>(Hv), hs);
+        // 4. every later segment from its entering state (the last one of a sequence
+        //    writes its final state)
+        kda::ScanJobs J2{};
+        J2.njobs = 1;
+        J2.job[0] = ps;
+        J2.job[0].N = static_cast<int32_t>(c.lat_max);
+        J2.job[0].entries = pl.later;
+        if (e == hipSuccess) e = kda::launch_kda_scan_jobs(J2, hs);
+        return finish(e, hs);
+    }
     const int64_t Hv = p.Hv;
     const SegLayout c = seg_layout(B, T, Hv, segment_chunks, first_chunks);
     if (c.P < 3)   // one or two segments: nothing runs side by side; the ordinary path

@@ -5,6 +5,16 @@
 
 namespace kda {
 
+// One sequence of a scan job given by a list: its record sequence (an index into
+// cu), and the [Hv][128][128] blocks its state enters from and leaves to (NULL:
+// zero, or the identity with h0_identity; not written).
+struct ScanEntry {
+    const float* h0;
+    float* hT;
+    int32_t rec;
+    int32_t pad;
+};
+
 struct KdaParams {
     const uint16_t* q;     // [tokens, Hq, 128] bf16 bits
     const uint16_t* k;     // [tokens, Hq, 128] bf16 bits
@@ -34,6 +44,9 @@ struct KdaParams {
     // Scan job variants: the state enters as the identity (h0 ignored), and / or v
     // reads as zero.  o == nullptr: no output is written.
     int32_t h0_identity, v_zero;
+    // Scan jobs only: sequence n of the job is entries[n] (its token range from cu,
+    // its states from the entry), instead of sequence n with h0 / hT indexed by n.
+    const ScanEntry* entries;
     // Optional fp32 dumps of the intermediates (all nullptr in production launches).
     float* tr_G;
     float* tr_Aqk;
@@ -133,6 +146,36 @@ hipError_t launch_kda_scan_jobs(ScanJobs jobs, hipStream_t stream);
 // Affine maps of consecutive segments composed in order, per (row, value head):
 // h_in[s + 1] = M[s] h_in[s] + b[s] for s = 0 .. nsteps - 1, where h_in[0] is given.
 // All arrays segment-major: [segment][rows][Hv][128][128] fp32.
+// Packed sequences: one chain per sequence, chains[3 n .. 3 n + 2] = (first map,
+// first entering state, steps): h[ls + s + 1] = M[ms + s] h[ls + s] + b[ms + s] for
+// s < steps, every array [index][Hv][128][128].
+hipError_t launch_kda_compose_chains(const float* M, const float* b, float* h_in, const int32_t* chains, int nchains,
+                                     int Hv, hipStream_t stream);
+
+// The segmented forward over packed sequences, planned on the device from
+// cu_seqlens: segment boundaries (cu_seg, S_max + 2 entries), the scan jobs'
+// entry lists and the chains of the maps to compose (see kda_fwd_cp).
+struct CpPlan {
+    const int32_t* cu;
+    int32_t N;
+    int64_t T;                 // tokens of the packed row (clamp bound)
+    int64_t L, L0;             // chunks per segment, of the first segment
+    int64_t hv_dd;             // Hv * 128 * 128 floats per state
+    const float* h0;           // [N][Hv][128][128] or NULL
+    float* hT;                 // [N][Hv][128][128] or NULL
+    float* Hin;                // [lat_max]: states entering the later segments
+    float* Mb;                 // [lat_max]: maps of the middle segments
+    float* Bb;                 // [lat_max]: offsets of the middle segments
+    int32_t* cu_seg;           // [S_max + 2]
+    int32_t S_max, lat_max;
+    ScanEntry* first;          // [N]: segment 0 of every sequence
+    ScanEntry* mid_m;          // [lat_max]: middle segments, maps
+    ScanEntry* mid_b;          // [lat_max]: middle segments, offsets
+    ScanEntry* later;          // [lat_max]: segments 1 .. P-1 of every sequence
+    int32_t* chains;           // [N][3]
+};
+hipError_t launch_kda_cp_plan(const CpPlan& pl, hipStream_t stream);
+
 hipError_t launch_kda_compose(const float* M, const float* b, float* h_in, int rows, int Hv, int nsteps,
                               hipStream_t stream);
 

@@ -136,7 +136,20 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const ScanJob
     const int n = pair / p.Hv, hv = pair % p.Hv;
     int64_t bos, len;
     int n_rec;   // the record sequence (equal to n without segments)
-    job_seq(p, n, bos, len, n_rec);
+    // this sequence's state blocks ([Hv][128][128]; NULL: zero or identity / not written)
+    const float* h0b;
+    float* hTb;
+    if (p.entries) {
+        const ScanEntry e = p.entries[n];
+        n_rec = e.rec;
+        h0b = e.h0;
+        hTb = e.hT;
+        seq_bounds(p, n_rec, bos, len);
+    } else {
+        job_seq(p, n, bos, len, n_rec);
+        h0b = p.h0 ? p.h0 + (int64_t)n * p.Hv * DK * DK : nullptr;
+        hTb = p.hT ? p.hT + (int64_t)n * p.Hv * DK * DK : nullptr;
+    }
     const int64_t nch = (len + CH - 1) / CH;
     const int64_t v_tok = (int64_t)p.Hv * DK;   // token stride of v, o
     const int dv0 = (PAIRS * s + pr) * DVW;     // this pair's dv columns
@@ -243,8 +256,8 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const ScanJob
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 hacc[tt][r] = (32 * (2 * role + tt) + 8 * (r >> 2) + 4 * hl + (r & 3) == dv0 + cl) ? 1.f : 0.f;
-        } else if (p.h0) {
-            const float* src = p.h0 + ((int64_t)n * p.Hv + hv) * DK * DK + dv0;
+        } else if (h0b) {
+            const float* src = h0b + (int64_t)hv * DK * DK + dv0;
             const int lo = cl + 4 * hl * DK;
 #pragma unroll
             for (int r = 0; r < 16; ++r) hacc[tt][r] = src[lo + (32 * (2 * role + tt) + 8 * (r >> 2) + (r & 3)) * DK];
@@ -501,12 +514,12 @@ __global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_kernel(const ScanJob
     }
 
     // ---- final state ----
-    if (p.hT) {
+    if (hTb) {
         // The lane offset is recomputed here from an opaque copy of the lane index,
         // so that it is not kept live (with the h0 addresses) through the chunk loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        float* dst = p.hT + ((int64_t)n * p.Hv + hv) * DK * DK + dv0;
+        float* dst = hTb + (int64_t)hv * DK * DK + dv0;
         const int lo = (ln & 31) + 4 * (ln >> 5) * DK;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {

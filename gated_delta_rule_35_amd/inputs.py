@@ -40,6 +40,7 @@ class Workload:
     varlen_total: int = 0        # >0: packed variable-length batch of this many tokens
     seed: int = 0
     length_seed: int = 7
+    lengths: tuple = ()          # a packed batch of these sequence lengths (instead of drawn ones)
 
     @property
     def scale(self) -> float:
@@ -59,6 +60,10 @@ WORKLOADS = {
     # under 8-way head sharding (the segmented forward's workloads)
     "mha_b1_h8_t65536": Workload("mha_b1_h8_t65536", 1, 65536, 8, 8, torch.float32, True),
     "mha_b2_h8_t8192": Workload("mha_b2_h8_t8192", 2, 8192, 8, 8, torch.float32, True),
+    # a packed batch with one long sequence among short ones, few heads (the
+    # segmented forward on packed sequences)
+    "packed_h8_long": Workload("packed_h8_long", 1, 65536 + 3000 + 100 + 7, 8, 8, torch.float32, True,
+                               lengths=(3000, 65536, 100, 7)),
 }
 
 
@@ -98,10 +103,10 @@ def make_inputs(B: int, T: int, Hq: int, Hv: int, beta_dtype=torch.float32, h0: 
 
 def workload_inputs(w: Workload, T: Optional[int] = None):
     """Inputs for a named workload; returns (dict of tensors, cu_seqlens or None)."""
-    if w.varlen_total:
-        lens = varlen_lengths(w.varlen_total, w.length_seed)
+    if w.varlen_total or w.lengths:
+        lens = list(w.lengths) if w.lengths else varlen_lengths(w.varlen_total, w.length_seed)
         cu = cu_from_lengths(lens)
-        x = make_inputs(1, w.varlen_total, w.Hq, w.Hv, w.beta_dtype, w.has_h0, N=len(lens), seed=w.seed)
+        x = make_inputs(1, sum(lens), w.Hq, w.Hv, w.beta_dtype, w.has_h0, N=len(lens), seed=w.seed)
         return x, cu
     x = make_inputs(w.B, T or w.T, w.Hq, w.Hv, w.beta_dtype, w.has_h0, seed=w.seed)
     return x, None

@@ -207,9 +207,9 @@ kda_status_t kda_fwd_noalloc(const kda_tensor_t* q, const kda_tensor_t* k, const
 int64_t kda_fwd_noalloc_max_bytes(void);
 
 /*
- * kda_fwd_cp -- kda_fwd for fixed-length batches, with each sequence cut into
- * segments that the scan walks side by side (context parallelism inside one
- * GPU), for batches whose B * Hv is too small to fill the chip.
+ * kda_fwd_cp -- kda_fwd with each sequence cut into segments that the scan walks
+ * side by side (context parallelism inside one GPU), for batches whose number of
+ * (sequence, value head) pairs is too small to fill the chip.
  *
  * The scan walks a sequence's chunks one after another, so B * Hv * 2
  * work-groups are all that can run at once: with few heads most of the GPU
@@ -231,15 +231,26 @@ int64_t kda_fwd_noalloc_max_bytes(void);
  * below the number of CUs and the sequences are long.  A first segment longer
  * than the others lets the maps run in several waves beside it.
  *
- * Arguments are kda_fwd's (no cu_seqlens: the segment boundaries are computed
- * on the host from the shapes), plus segment_chunks >= 1 and
- * first_segment_chunks >= 0 (KDA_ERR_VALUE otherwise).  workspace (required,
- * 16-byte aligned, caller-owned, no initialisation) must hold
- * kda_fwd_cp_workspace_size() bytes.  With fewer
- * than three segments the call is exactly kda_fwd.  Results are bitwise
- * repeatable; they agree with kda_fwd to within the rounding of the fp16 MFMA
- * operands (the maps are formed with the same operand precision as the
- * state), not bit for bit.  initial_state may alias final_state.
+ * Arguments are kda_fwd's, plus segment_chunks >= 1 and first_segment_chunks >= 0
+ * (KDA_ERR_VALUE otherwise).  workspace (required, caller-owned, no
+ * initialisation) must hold kda_fwd_cp_workspace_size() bytes (16-byte aligned)
+ * for a fixed-length batch, kda_fwd_cp_packed_workspace_size() bytes (256-byte
+ * aligned) with cu_seqlens.
+ * Fixed length (cu_seqlens NULL): the segment boundaries follow from the shapes;
+ * with fewer than three segments per row the call is exactly kda_fwd.
+ * Packed sequences (cu_seqlens given, B = 1): every sequence is cut the same way
+ * from its own start (P = 1 segment when it has at most first_segment_chunks
+ * chunks); since the host never reads cu_seqlens, a plan kernel derives the
+ * segments, the steps' work lists and the composition chains on the device,
+ * within bounds computed from the shapes (at most N + TC / L + min(N, TC / (L0 +
+ * 1)) + 1 segments for TC = ceil(T / 64) + N chunks), and the steps run over the
+ * bounds (work past the actual counts exits at once).  A sequence with one or two
+ * segments gets kda_fwd's results bit for bit; with malformed cu_seqlens the
+ * results are undefined but every access stays in bounds.  The call launches
+ * kernels only and can be captured into a HIP graph.
+ * Results are bitwise repeatable; they agree with kda_fwd to within the rounding
+ * of the fp16 MFMA operands (the maps are formed with the same operand precision
+ * as the state), not bit for bit.  initial_state may alias final_state.
  */
 /*
  * kda_fwd_cp_plan -- segment lengths (in 64-token chunks) for kda_fwd_cp on a
@@ -255,10 +266,14 @@ int32_t kda_fwd_cp_plan(int64_t batch, int64_t seq_len, int64_t num_value_heads,
 /* Workspace bytes of a kda_fwd_cp call; -1 for negative sizes or segment_chunks < 1. */
 int64_t kda_fwd_cp_workspace_size(int64_t batch, int64_t seq_len, int64_t num_value_heads, int64_t segment_chunks,
                                   int64_t first_segment_chunks);
+/* Workspace bytes of a kda_fwd_cp call on packed sequences: total_tokens = T of
+ * the packed row, num_sequences = N; -1 for negative sizes or segment_chunks < 1. */
+int64_t kda_fwd_cp_packed_workspace_size(int64_t total_tokens, int64_t num_sequences, int64_t num_value_heads,
+                                         int64_t segment_chunks, int64_t first_segment_chunks);
 kda_status_t kda_fwd_cp(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,
                         const kda_tensor_t* g, const kda_tensor_t* beta, float scale,
-                        const kda_tensor_t* initial_state, const kda_tensor_t* out,
-                        const kda_tensor_t* final_state, int64_t segment_chunks,
+                        const kda_tensor_t* cu_seqlens, const kda_tensor_t* initial_state,
+                        const kda_tensor_t* out, const kda_tensor_t* final_state, int64_t segment_chunks,
                         int64_t first_segment_chunks, void* workspace, int64_t workspace_size, void* stream);
 
 /*

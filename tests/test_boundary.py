@@ -327,10 +327,10 @@ def test_decode_empty_batch_needs_no_launch(lib):
 
 # ---- kda_fwd_cp ----
 
-def call_cp(lib, a, seg, first=0, scale=0.088, h0=None, hT=None, ws=None, ws_size=0):
+def call_cp(lib, a, seg, first=0, scale=0.088, h0=None, hT=None, ws=None, ws_size=0, cu=None):
     r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
     return lib.kda_fwd_cp(r(a.get("q")), r(a.get("k")), r(a.get("v")), r(a.get("g")), r(a.get("beta")), scale,
-                          r(h0), r(a.get("out")), r(hT), seg, first, ws, ws_size, None)
+                          r(cu), r(h0), r(a.get("out")), r(hT), seg, first, ws, ws_size, None)
 
 
 def test_cp_workspace_size(lib):
@@ -548,3 +548,37 @@ def test_qg_output_is_checked_before_any_hip_call(lib):
     a["v"] = None
     assert name(call_qg(lib, a, T([1, 64, 2, 128], data=qg_addr))) == "KDA_ERR_NULL"
     assert name(call_qg(lib, good(), T([1, 64, 2, 128], data=qg_addr), scale=-1.0)) == "KDA_ERR_VALUE"
+
+
+def test_cp_packed_workspace_size_and_checks(lib):
+    """Packed segmented calls: the workspace bound, and the checks before any HIP
+    call (B must be 1 with cu_seqlens; the workspace is required, sized by
+    kda_fwd_cp_packed_workspace_size and 256-byte aligned)."""
+    rec, blk = 61952, 2 * 128 * 128 * 4
+    # T = 2000 tokens, N = 3 sequences, Hv = 2, L = 4, L0 = 4: TC = 32 + 3 = 35 chunks at
+    # most, 35 // 4 + min(3, 35 // 5) + 1 = 12 later segments, 15 segments, 48 slots
+    size = lib.kda_fwd_cp_packed_workspace_size(2000, 3, 2, 4, 0)
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    lat, smax = 12, 15
+    expect = al(48 * 2 * rec)
+    expect = al(expect + 3 * lat * blk)
+    expect = al(expect + (smax + 2) * 4)
+    expect = al(expect + 3 * 24)
+    expect = al(expect + lat * 24)
+    expect = al(expect + lat * 24)
+    expect = al(expect + lat * 24)
+    expect = al(expect + 3 * 12)
+    assert size == expect, (size, expect)
+    for bad in ((-1, 3, 2, 4, 0), (10, -1, 2, 4, 0), (10, 3, -2, 4, 0), (10, 3, 2, 0, 0), (10, 3, 2, 4, -1)):
+        assert lib.kda_fwd_cp_packed_workspace_size(*bad) == -1
+    a = good(B=1, T_=2000)
+    cu = T([4], binding.KDA_I32, data=FAKE + (1 << 28))
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, cu=cu)] == "KDA_ERR_WORKSPACE"
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, cu=cu, ws=FAKE, ws_size=size - 1)] == "KDA_ERR_WORKSPACE"
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, cu=cu, ws=FAKE + 16, ws_size=size)] == "KDA_ERR_WORKSPACE"
+    b = good(B=2, T_=1000)
+    assert binding.STATUS_NAMES[call_cp(lib, b, 4, cu=cu, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_UNSUPPORTED"
+    bad_cu = T([4], binding.KDA_F32, data=FAKE + (1 << 28))
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, cu=bad_cu, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_DTYPE"
+    st = T([2, 2, 128, 128], binding.KDA_F32)   # N = 3 sequences need [3, 2, 128, 128]
+    assert binding.STATUS_NAMES[call_cp(lib, a, 4, cu=cu, h0=st, ws=FAKE, ws_size=1 << 40)] == "KDA_ERR_SHAPE"

@@ -133,3 +133,83 @@ def test_bench_workloads_with_the_plan(name, heads):
     srel = state_rel_frob(hT, h_ref)
     _say(f"{name}: o relF={rel:.3e} maxabs={mx:.3e} state relF={srel:.3e}")
     assert rel <= O_REL_F and mx <= O_MAX_ABS and srel <= STATE_REL_F, (rel, mx, srel)
+
+
+# ---- packed sequences (cu_seqlens): the plan is made on the device ----
+
+def _packed(lens, Hq, Hv, seed, h0=True, beta=torch.float32, tail=0):
+    from gated_delta_rule_35_amd.inputs import cu_from_lengths
+    cu = cu_from_lengths(lens)
+    T = int(cu[-1]) + tail
+    x = make_inputs(1, T, Hq, Hv, beta, h0=h0, N=len(lens), seed=seed)
+    return x, cu
+
+
+def _check_packed(x, cu, seg, first, label, fill=None):
+    d = to_device(x)
+    out = None
+    if fill is not None:
+        out = torch.full_like(d["v"], fill)
+    o, hT = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, seg, first, initial_state=d["h0"],
+                       out=out, final_state=True, cu_seqlens=cu.cuda())
+    torch.cuda.synchronize()
+    o_np, h_np = o.float().cpu().numpy(), hT.cpu().numpy()
+    o_ref, h_ref = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], SCALE, cu_seqlens=cu, h0=x["h0"])
+    cuv = [int(c) for c in cu]
+    worst, mx = 0.0, 0.0
+    for n in range(len(cuv) - 1):
+        a, e = cuv[n], cuv[n + 1]
+        if e > a:
+            worst = max(worst, rel_frob_per_head(o_np[:, a:e], o_ref[:, a:e]))
+            mx = max(mx, float(np.max(np.abs(o_np[:, a:e] - o_ref[:, a:e]))))
+    srel = state_rel_frob(h_np, h_ref)
+    _say(f"{label}: o relF={worst:.3e} maxabs={mx:.3e} state relF={srel:.3e}")
+    assert np.all(np.isfinite(h_np))
+    assert worst <= O_REL_F, worst
+    assert mx <= O_MAX_ABS, mx
+    assert srel <= STATE_REL_F, srel
+    return o, hT
+
+
+@pytest.mark.parametrize("lens,Hq,Hv,seg,first", [
+    ([1, 63, 65, 700, 0, 2000, 5], 2, 2, 3, 0),     # empty, one-token, tail and long sequences
+    ([1300, 64, 1], 2, 4, 1, 4),                    # one-chunk segments after a 4-chunk first one
+    ([4096, 3000, 129], 1, 4, 8, 16),               # grouped values, three long sequences
+    ([640] * 5, 3, 3, 2, 0),                        # equal lengths, 5 segments each
+])
+def test_packed_segmented_matches_oracle(lens, Hq, Hv, seg, first):
+    _say(f"kda_fwd_cp packed lens={lens} Hq={Hq} Hv={Hv} segment_chunks={seg} first={first}")
+    x, cu = _packed(lens, Hq, Hv, seed=300 + sum(lens))
+    _check_packed(x, cu, seg, first, f"cp packed {lens}")
+
+
+def test_packed_segmented_leaves_other_rows_and_repeats():
+    """Rows past cu[N] keep what the caller put there; repeated calls are bitwise
+    equal; with at most two segments per sequence the call equals kda_fwd_ws bit
+    for bit (no map is composed)."""
+    from gated_delta_rule_35_amd import kda_fwd_ws
+    lens = [200, 0, 1000, 65]
+    _say(f"kda_fwd_cp packed lens={lens} with 37 trailing tokens, repeats and kda_fwd_ws comparison")
+    x, cu = _packed(lens, 2, 2, seed=310, tail=37)
+    o1, h1 = _check_packed(x, cu, 4, 0, "cp packed trailing rows", fill=3.0)
+    assert torch.all(o1[:, int(cu[-1]):] == 3.0)
+    o2, h2 = _check_packed(x, cu, 4, 0, "cp packed repeat", fill=3.0)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(h1, h2)
+    d = to_device(x)
+    # 16 chunks per segment: every sequence has one or two segments
+    o3, h3 = kda_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 16, initial_state=d["h0"],
+                        final_state=True, cu_seqlens=cu.cuda())
+    o4, h4 = kda_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, cu_seqlens=cu.cuda(),
+                        initial_state=d["h0"], final_state=True)
+    torch.cuda.synchronize()
+    n = int(cu[-1])
+    assert torch.equal(o3[:, :n].view(torch.int16), o4[:, :n].view(torch.int16)) and torch.equal(h3, h4)
+
+
+def test_packed_segmented_long_sequence_among_short_ones():
+    """One 32,768-token sequence among three short ones, 8 heads, 16-chunk segments
+    after a 32-chunk first one (the case the segmented form is for)."""
+    lens = [100, 32768, 1, 500]
+    _say(f"kda_fwd_cp packed lens={lens} H=8 segment_chunks=16 first=32")
+    x, cu = _packed(lens, 8, 8, seed=320)
+    _check_packed(x, cu, 16, 32, "cp packed long")

@@ -1,14 +1,15 @@
 """The library's launches under HIP graph capture (torch.cuda.graph): kda_fwd_fused,
-kda_fwd_ws, kda_fwd_cp, kda_decode and kda_bwd are captured once with caller-owned outputs and
+kda_fwd_ws, kda_fwd_cp (fixed length and packed), kda_decode and kda_bwd are captured once with caller-owned outputs and
 workspaces (nothing is allocated and no memset is recorded), then replayed
 several times with eager work and synchronisation in between; every replay
 must reproduce the eager result bit for bit."""
 import pytest
 import torch
 
-from gated_delta_rule_35_amd import (kda_decode, kda_fwd, kda_fwd_cp, kda_fwd_cp_workspace_size, kda_fwd_fused,
-                                     kda_fwd_workspace_size, kda_fwd_ws, load_library)
-from gated_delta_rule_35_amd.inputs import make_inputs
+from gated_delta_rule_35_amd import (kda_decode, kda_fwd, kda_fwd_cp, kda_fwd_cp_packed_workspace_size,
+                                     kda_fwd_cp_workspace_size, kda_fwd_fused, kda_fwd_workspace_size, kda_fwd_ws,
+                                     load_library)
+from gated_delta_rule_35_amd.inputs import cu_from_lengths, make_inputs
 from tests.kda_check import to_device
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +85,24 @@ def test_kda_fwd_cp_in_a_graph():
     out, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
     ws = torch.empty(kda_fwd_cp_workspace_size(1, 2048, 2, 4, 8), dtype=torch.uint8, device="cuda")
     capture_and_replay(lambda: kda_fwd_cp(*args, initial_state=d["h0"], out=out, final_state=hT, workspace=ws),
+                       (out, hT), (o_ref, h_ref))
+
+
+def test_kda_fwd_cp_packed_in_a_graph():
+    """The packed segmented call plans on the device (a kernel writes the segment
+    tables into the workspace), so it too is launches only."""
+    lens = [1500, 3, 700]
+    _say(f"graph: kda_fwd_cp packed lens={lens} H=2, first segment 8 chunks, then 3")
+    cu = cu_from_lengths(lens).cuda()
+    x = make_inputs(1, sum(lens), 2, 2, torch.float32, h0=True, N=len(lens), seed=303)
+    d = to_device(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE, 3, 8)
+    o_ref, h_ref = kda_fwd_cp(*args, initial_state=d["h0"], final_state=True, cu_seqlens=cu)
+    out, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    ws = torch.empty(kda_fwd_cp_packed_workspace_size(sum(lens), len(lens), 2, 3, 8), dtype=torch.uint8,
+                     device="cuda")
+    capture_and_replay(lambda: kda_fwd_cp(*args, initial_state=d["h0"], out=out, final_state=hT, workspace=ws,
+                                          cu_seqlens=cu),
                        (out, hT), (o_ref, h_ref))
 
 
