@@ -269,7 +269,7 @@ PackedLayout packed_layout(int64_t T, int64_t N, int64_t Hv, int64_t L, int64_t 
     c.later = o;
     o = al(o + c.lat_max * es);
     c.chains = o;
-    o = al(o + N * 3 * 4);
+    o = al(o + N * 4 * 4);
     c.total = o;
     return c;
 }

@@ -29,8 +29,8 @@ constexpr int M_LOADS = DK * DK / 4 / CMP_THREADS;   // 16-byte pieces of M per 
 // pieces (consecutive threads, consecutive 16 bytes) while the previous step's
 // products run, and writes them to the other LDS buffer afterwards.
 // With `chains` (packed sequences), row n is chain n: its steps read M and b from
-// index chains[3 n] on and its states from index chains[3 n + 1] on, each index
-// one [Hv][128][128] block, for chains[3 n + 2] steps (`nsteps` is ignored).
+// index chains[4 n] on and its states from index chains[4 n + 1] on, each index
+// one [Hv][128][128] block, for chains[4 n + 2] steps (`nsteps` is ignored).
 __global__ void __launch_bounds__(CMP_THREADS) kda_compose_kernel(const float* M, const float* b, float* h, int rows,
                                                                  int Hv, int nsteps, const int32_t* chains) {
     __shared__ __attribute__((aligned(16))) float sM[2][DK * MS];   // M of two steps
@@ -43,8 +43,8 @@ __global__ void __launch_bounds__(CMP_THREADS) kda_compose_kernel(const float* M
     int64_t me = (int64_t)item * head + (int64_t)i * DK + col0 + 4 * jq;
     if (chains) {
         const int n = item / Hv, hv = item % Hv;
-        const int64_t ms = chains[3 * n], ls = chains[3 * n + 1];
-        nsteps = chains[3 * n + 2];
+        const int64_t ms = chains[4 * n], ls = chains[4 * n + 1];
+        nsteps = chains[4 * n + 2];
         if (nsteps <= 0) return;   // (uniform per work-group)
         seg = (int64_t)Hv * head;
         M += ms * seg;
@@ -118,8 +118,16 @@ hipError_t launch_kda_compose_chains(const float* M, const float* b, float* h_in
 // be shorter).  Segments get global indices in token order; segment j of sequence
 // n starts at a (j = 0) or a + 64 (L0 + (j - 1) L).  Later segments (j >= 1) and
 // middle segments (1 <= j <= P - 2) are numbered by prefix sums over the
-// sequences, so each sequence's are consecutive.  List entries past the totals
-// point at the empty segment S_max and write nothing.
+// sequences, so each sequence's are consecutive.
+// Two phases: per sequence (rounds of 256, prefix sums across the round) the
+// counts, segment 0's entry and the chain; then per segment (all threads, the
+// owning sequence found by binary search over the first-segment indices) the
+// boundary and the later / middle entries, so one long sequence does not leave
+// the work to one thread.  List entries past the totals point at the empty
+// segment S_max and write nothing.  Every index is checked against the sizes the
+// host planned for: with well-formed cu_seqlens they always fit; with malformed
+// ones (overlapping sequences) the results are undefined but every access stays
+// in bounds.
 __global__ void __launch_bounds__(256) kda_cp_plan_kernel(const CpPlan pl) {
     __shared__ int s_cnt[3][256];
     __shared__ int s_carry[3];
@@ -132,11 +140,13 @@ __global__ void __launch_bounds__(256) kda_cp_plan_kernel(const CpPlan pl) {
         a = a < 0 ? 0 : (a > pl.T ? pl.T : a);
         e = e < a ? a : (e > pl.T ? pl.T : e);
     };
+    const int64_t hd = pl.hv_dd;
+    // ---- phase 1: per sequence ----
     for (int base = 0; base < pl.N; base += 256) {
         const int n = base + t;
         int P = 0;
-        int64_t a = 0, e = 0;
         if (n < pl.N) {
+            int64_t a, e;
             bounds(n, a, e);
             const int64_t nch = (e - a + CH - 1) / CH;
             P = nch <= pl.L0 ? 1 : (int)(1 + (nch - pl.L0 + pl.L - 1) / pl.L);
@@ -158,46 +168,20 @@ __global__ void __launch_bounds__(256) kda_cp_plan_kernel(const CpPlan pl) {
         const int ls = s_carry[1] + s_cnt[1][t] - later;
         const int ms = s_carry[2] + s_cnt[2][t] - mid;
         if (n < pl.N) {
-            // Every index is checked against the sizes the host planned for: with
-            // well-formed cu_seqlens they always fit; with malformed ones (overlapping
-            // sequences) the results are undefined but every access stays in bounds.
-            const int64_t hd = pl.hv_dd;
-            auto rec_of = [&](int j) { return segb + j <= pl.S_max ? segb + j : pl.S_max; };
-            for (int j = 0; j < P; ++j) {
-                const int64_t st = j == 0 ? a : a + (int64_t)CH * (pl.L0 + (int64_t)(j - 1) * pl.L);
-                if (segb + j <= pl.S_max + 1) pl.cu_seg[segb + j] = (int32_t)(st < e ? st : e);
-            }
             ScanEntry f;
-            f.rec = rec_of(0);
+            f.rec = segb <= pl.S_max ? segb : pl.S_max;
             f.pad = 0;
             f.h0 = pl.h0 ? pl.h0 + (int64_t)n * hd : nullptr;
             f.hT = P >= 2 ? (ls < pl.lat_max ? pl.Hin + (int64_t)ls * hd : nullptr)
                           : (pl.hT ? pl.hT + (int64_t)n * hd : nullptr);
             pl.first[n] = f;
-            for (int j = 1; j < P && ls + j - 1 < pl.lat_max; ++j) {
-                ScanEntry l;
-                l.rec = rec_of(j);
-                l.pad = 0;
-                l.h0 = pl.Hin + (int64_t)(ls + j - 1) * hd;
-                l.hT = (j == P - 1 && pl.hT) ? pl.hT + (int64_t)n * hd : nullptr;
-                pl.later[ls + j - 1] = l;
-            }
-            for (int j = 1; j + 1 < P && ms + j - 1 < pl.lat_max; ++j) {
-                ScanEntry m;
-                m.rec = rec_of(j);
-                m.pad = 0;
-                m.h0 = nullptr;
-                m.hT = pl.Mb + (int64_t)(ms + j - 1) * hd;
-                pl.mid_m[ms + j - 1] = m;
-                m.hT = pl.Bb + (int64_t)(ms + j - 1) * hd;
-                pl.mid_b[ms + j - 1] = m;
-            }
             int steps = mid;
             if (ms + steps > pl.lat_max) steps = pl.lat_max - ms;
             if (ls + steps + 1 > pl.lat_max) steps = pl.lat_max - ls - 1;
-            pl.chains[3 * n] = ms;
-            pl.chains[3 * n + 1] = ls;
-            pl.chains[3 * n + 2] = steps > 0 ? steps : 0;
+            pl.chains[4 * n] = ms;
+            pl.chains[4 * n + 1] = ls;
+            pl.chains[4 * n + 2] = steps > 0 ? steps : 0;
+            pl.chains[4 * n + 3] = segb;   // first segment (for phase 2)
         }
         __syncthreads();
         if (t == 255) {
@@ -207,14 +191,53 @@ __global__ void __launch_bounds__(256) kda_cp_plan_kernel(const CpPlan pl) {
         }
         __syncthreads();
     }
+    const int S_total = s_carry[0];
+    // ---- phase 2: per segment ----
+    const int S_lim = S_total < pl.S_max + 2 ? S_total : pl.S_max + 2;
+    for (int sg = t; sg < S_lim; sg += 256) {
+        int lo = 0, hi = pl.N - 1;   // the last sequence whose first segment is <= sg
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pl.chains[4 * mid + 3] <= sg) lo = mid; else hi = mid - 1;
+        }
+        const int n = lo, segb = pl.chains[4 * n + 3];
+        const int P = (n + 1 < pl.N ? pl.chains[4 * (n + 1) + 3] : S_total) - segb;
+        const int ms = pl.chains[4 * n], ls = pl.chains[4 * n + 1];
+        const int j = sg - segb;
+        int64_t a, e;
+        bounds(n, a, e);
+        const int64_t st = j == 0 ? a : a + (int64_t)CH * (pl.L0 + (int64_t)(j - 1) * pl.L);
+        pl.cu_seg[sg] = (int32_t)(st < e ? st : e);
+        const int rec = sg <= pl.S_max ? sg : pl.S_max;
+        if (j >= 1 && ls + j - 1 < pl.lat_max) {
+            ScanEntry l;
+            l.rec = rec;
+            l.pad = 0;
+            l.h0 = pl.Hin + (int64_t)(ls + j - 1) * hd;
+            l.hT = (j == P - 1 && pl.hT) ? pl.hT + (int64_t)n * hd : nullptr;
+            pl.later[ls + j - 1] = l;
+        }
+        if (j >= 1 && j + 1 < P && ms + j - 1 < pl.lat_max) {
+            ScanEntry m;
+            m.rec = rec;
+            m.pad = 0;
+            m.h0 = nullptr;
+            m.hT = pl.Mb + (int64_t)(ms + j - 1) * hd;
+            pl.mid_m[ms + j - 1] = m;
+            m.hT = pl.Bb + (int64_t)(ms + j - 1) * hd;
+            pl.mid_b[ms + j - 1] = m;
+        }
+    }
     // The end of the last segment, the empty padding segments, and the padding
     // entries of the lists.
-    const int S = s_carry[0] < pl.S_max ? s_carry[0] : pl.S_max;
+    const int S = S_total < pl.S_max ? S_total : pl.S_max;
     const int LT = s_carry[1] < pl.lat_max ? s_carry[1] : pl.lat_max;
     const int MD = s_carry[2] < pl.lat_max ? s_carry[2] : pl.lat_max;
     int64_t end = pl.N > 0 ? pl.cu[pl.N] : 0;
     end = end < 0 ? 0 : (end > pl.T ? pl.T : end);
-    for (int x = S + t; x <= pl.S_max + 1; x += 256) pl.cu_seg[x] = (int32_t)end;
+    __syncthreads();   // (phase 2's boundary writes come first: S_total may exceed S)
+    for (int x = S + t; x <= pl.S_max + 1; x += 256)
+        if (x >= S_total) pl.cu_seg[x] = (int32_t)end;
     ScanEntry z;
     z.rec = pl.S_max;
     z.pad = 0;

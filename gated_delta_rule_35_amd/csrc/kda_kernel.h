@@ -146,9 +146,10 @@ hipError_t launch_kda_scan_jobs(ScanJobs jobs, hipStream_t stream);
 // Affine maps of consecutive segments composed in order, per (row, value head):
 // h_in[s + 1] = M[s] h_in[s] + b[s] for s = 0 .. nsteps - 1, where h_in[0] is given.
 // All arrays segment-major: [segment][rows][Hv][128][128] fp32.
-// Packed sequences: one chain per sequence, chains[3 n .. 3 n + 2] = (first map,
+// Packed sequences: one chain per sequence, chains[4 n .. 4 n + 2] = (first map,
 // first entering state, steps): h[ls + s + 1] = M[ms + s] h[ls + s] + b[ms + s] for
-// s < steps, every array [index][Hv][128][128].
+// s < steps, every array [index][Hv][128][128] (chains[4 n + 3]: the sequence's
+// first segment, for the plan).
 hipError_t launch_kda_compose_chains(const float* M, const float* b, float* h_in, const int32_t* chains, int nchains,
                                      int Hv, hipStream_t stream);
 
@@ -172,7 +173,7 @@ struct CpPlan {
     ScanEntry* mid_m;          // [lat_max]: middle segments, maps
     ScanEntry* mid_b;          // [lat_max]: middle segments, offsets
     ScanEntry* later;          // [lat_max]: segments 1 .. P-1 of every sequence
-    int32_t* chains;           // [N][3]
+    int32_t* chains;           // [N][4]
 };
 hipError_t launch_kda_cp_plan(const CpPlan& pl, hipStream_t stream);
 

@@ -567,7 +567,7 @@ def test_cp_packed_workspace_size_and_checks(lib):
     expect = al(expect + lat * 24)
     expect = al(expect + lat * 24)
     expect = al(expect + lat * 24)
-    expect = al(expect + 3 * 12)
+    expect = al(expect + 3 * 16)
     assert size == expect, (size, expect)
     for bad in ((-1, 3, 2, 4, 0), (10, -1, 2, 4, 0), (10, 3, -2, 4, 0), (10, 3, 2, 0, 0), (10, 3, 2, 4, -1)):
         assert lib.kda_fwd_cp_packed_workspace_size(*bad) == -1
