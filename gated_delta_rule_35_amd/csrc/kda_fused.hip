@@ -97,7 +97,7 @@ struct FL {
 enum : int {
     C_OPS = 0,     // +1 per intra wave when chunk c's operands are stored
     C_S1 = 1,      // +1 per scan wave when S1 of chunk c has read them
-    C_T = 2,       // +1 (scan wave 1) when chunk c's T diag(beta) is stored
+    C_T = 2,       // +1 per scan wave when chunk c's T diag(beta) is stored
     C_I = 3,       // intra waves' own rendezvous
     C_G = 4,       // [4], [5]: exact-path word of chunk parity 0, 1
     C_ABORT = 6,   // a wait ran past its limit
@@ -326,10 +326,11 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         // sum_{K=J}^{1} A_IK T_KJ:
         //   level 1  w0: T_10 = -T_11 (A_10 T_00)   w1: T_32 = -T_33 (A_32 T_22)
         //            w2: X_21 = A_21 T_11            w3: X_31 = A_31 T_11
-        //   level 2  w0: X_20, T_20 = -T_22 X_20     w1: X_30
+        //   level 2  w0: X_20, T_20 = -T_22 X_20
+        //            w1: X_20, X_30, T_30 = -(T_32 X_20 + T_33 X_30)
         //            w2: T_21 = -T_22 X_21           w3: T_31 = -(T_32 X_21 + T_33 X_31)
-        //   level 3  w1: T_30 = -(T_32 X_20 + T_33 X_30)
-        // with a scan-wave rendezvous between levels.
+        // with a scan-wave rendezvous between levels (waves 0 and 1 each form X_20,
+        // so the block row 3 needs no third level).
         int tv = 0;   // running target of the scan waves' rendezvous counter
         auto vsync = [&]() {
             signal(C_V);
@@ -421,18 +422,28 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
                                mm16_mac(mm16_ops(A(I, 1), S68, sTtD + 16 * TS, TS, ln), z4), ln);
             }
             vsync();
-            if (wave == 0) {
-                // X_20 = A_20 T_00 + A_21 T_10 ; T_20 = -T_22 X_20
+            // levels 2 and 3 together: X_20 is formed by both waves that need it
+            if (wave == 0 || wave == 1) {
+                // X_20 = A_20 T_00 + A_21 T_10 (a private copy per wave)
                 const Mm16Ops a = mm16_ops(A(2, 0), S68, sTtD, TS, ln);
                 const Mm16Ops b = mm16_ops(A(2, 1), S68, sT1t, TS, ln);
-                store_colmajor(sXt, mm16_mac(b, mm16_mac(a, z4)), ln);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, sXt, TS, ln), z4)), 2, 0, sb, ln);
-            } else if (wave == 1) {
-                // X_30 = A_30 T_00 + A_31 T_10
-                const Mm16Ops a = mm16_ops(A(3, 0), S68, sTtD, TS, ln);
-                const Mm16Ops b = mm16_ops(A(3, 1), S68, sT1t, TS, ln);
-                store_colmajor(sXt + 2 * 16 * TS, mm16_mac(b, mm16_mac(a, z4)), ln);
+                float* xs = sXt + (wave == 0 ? 0 : 2) * 16 * TS;
+                store_colmajor(xs, mm16_mac(b, mm16_mac(a, z4)), ln);
+                if (wave == 0) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    // T_20 = -T_22 X_20
+                    store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, xs, TS, ln), z4)), 2, 0, sb, ln);
+                } else {
+                    // X_30 = A_30 T_00 + A_31 T_10 ; T_30 = -(T_32 X_20 + T_33 X_30)
+                    const Mm16Ops a3 = mm16_ops(A(3, 0), S68, sTtD, TS, ln);
+                    const Mm16Ops b3 = mm16_ops(A(3, 1), S68, sT1t, TS, ln);
+                    float* x30 = sT1t + 16 * TS;   // wave 1's level-1 scratch, free now
+                    store_colmajor(x30, mm16_mac(b3, mm16_mac(a3, z4)), ln);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    const Mm16Ops c2 = mm16_ops(A(3, 2), S68, xs, TS, ln);
+                    const Mm16Ops c3 = mm16_ops(A(3, 3), S68, x30, TS, ln);
+                    store_tb(smem, tbo, neg(mm16_mac(c3, mm16_mac(c2, z4))), 3, 0, sb, ln);
+                }
             } else if (wave == 2) {
                 // T_21 = -T_22 X_21
                 store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, sXt + 16 * TS, TS, ln), z4)), 2, 1, sb, ln);
@@ -441,13 +452,6 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
                 const Mm16Ops a = mm16_ops(A(3, 2), S68, sXt + 16 * TS, TS, ln);
                 const Mm16Ops b = mm16_ops(A(3, 3), S68, sXt + 3 * 16 * TS, TS, ln);
                 store_tb(smem, tbo, neg(mm16_mac(b, mm16_mac(a, z4))), 3, 1, sb, ln);
-            }
-            vsync();
-            if (wave == 1) {
-                // T_30 = -(T_32 X_20 + T_33 X_30)
-                const Mm16Ops a = mm16_ops(A(3, 2), S68, sXt, TS, ln);
-                const Mm16Ops b = mm16_ops(A(3, 3), S68, sXt + 2 * 16 * TS, TS, ln);
-                store_tb(smem, tbo, neg(mm16_mac(b, mm16_mac(a, z4))), 3, 0, sb, ln);
             }
         };
         if (nch > 0) {
@@ -536,8 +540,8 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
             // set is dead; written to v^T at the end of S2 and read in the next S1
             load_vs(c + 1);   // (past the last chunk: a zero-length range)
             inversion_rest(s);
-            if (wave == 1) signal(C_T);
-            wait_ge(C_T, c + 1);
+            signal(C_T);
+            wait_ge(C_T, 4 * (c + 1));
             // ---- S2 ----
             // T diag(beta): tiles (mt, k step) (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
             half8 ftb[6];
@@ -646,7 +650,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
     i32x4 qraw[4], kraw[4];   // [row t] element d: bf16 pair (channels cc + 2 d, + 1)
     i32x4 graw[4][2];         // [row t][half] element e: g of channel cc + 4 half + e
     uint32_t braw_bits = 0;
-    auto load_into = [&](int c, i32x4 (&q)[4], i32x4 (&k)[4], i32x4 (&gg)[4][2], uint32_t& bb) {
+    auto load_into = [&](int c, i32x4 (&q)[4], i32x4 (&k)[4], i32x4 (&gg)[4][2], uint32_t& bb, int part = 3) {
         const int ln = opaque(lane);
         const int row0 = 4 * (ln & 15), cc = 32 * wi + 8 * octet(ln);
         const int gb = (int)((row0 * v_tok + cc) * 4), qb = (int)((row0 * qk_tok + cc) * 2);
@@ -658,14 +662,21 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
             make_rsrc(p.q + t0 * qk_tok + (int64_t)hq * DK, Lc ? ((Lc - 1) * qk_tok + DK) * 2 : 0);
         const __amdgpu_buffer_rsrc_t rk =
             make_rsrc(p.k + t0 * qk_tok + (int64_t)hq * DK, Lc ? ((Lc - 1) * qk_tok + DK) * 2 : 0);
+        if (part & 1) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            q[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, qb + (int)(t * qk_tok * 2), 0, 0);
-            k[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, qb + (int)(t * qk_tok * 2), 0, 0);
-            gg[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rg, gb + (int)(t * v_tok * 4), 0, 0);
-            gg[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rg, gb + (int)(t * v_tok * 4) + 16, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                q[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, qb + (int)(t * qk_tok * 2), 0, 0);
+                k[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, qb + (int)(t * qk_tok * 2), 0, 0);
+            }
         }
-        if (wi == 0) {
+        if (part & 2) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                gg[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rg, gb + (int)(t * v_tok * 4), 0, 0);
+                gg[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rg, gb + (int)(t * v_tok * 4) + 16, 0, 0);
+            }
+        }
+        if (wi == 0 && (part & 2)) {
             // beta of token ln (the dtype is a template parameter: no branch around
             // the load, so no wait for it at a join)
             const int esz = BETA_F32 ? 4 : 2;
@@ -679,8 +690,10 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
     };
     // Chunk c's inputs (past the last chunk: a zero-length range, so no access and
     // zeros; issuing it anyway keeps the load out of a branch, whose join would
-    // make the compiler wait for it).
-    auto load_raw = [&](int c) { load_into(c, qraw, kraw, graw, braw_bits); };
+    // make the compiler wait for it).  part: 1 = q and k, 2 = g and beta, 3 = both;
+    // the intra loop issues the two halves apart, q and k only once the current
+    // chunk's q and k operands are out of their registers.
+    auto load_raw = [&](int c, int part = 3) { load_into(c, qraw, kraw, graw, braw_bits, part); };
     // Local inclusive cumsum of g within the 4 rows (log2 units), the cumsum of the
     // earlier row groups (an inclusive prefix over u, on the lanes of one 16-lane
     // row) and the chunk total (from lane 15 of the row).  Returns whether some
@@ -935,7 +948,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         const bool exact = ctr_load(C_G + s) != 0;
         if (wi == 0) sync_ctr[C_G + (s ^ 1)] = 0;   // the next chunk's word (its readers are past the rendezvous)
         const uint32_t beta_bits = braw_bits;
-        load_raw(c + 1);   // the next chunk's inputs, in flight until its a1
+        load_raw(c + 1, 2);   // the next chunk's g and beta, in flight until its a1
         wait_ge(C_S1, 4 * c);   // the scan waves are done with chunk c - 1's q/k operands
         // The fast path's operands are stored either way (the exact path then
         // overwrites them), so that nothing computed above stays live across the
@@ -945,10 +958,11 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         store_rows(FL::KI, oki);
         store_kt(s, okt);
         store_scalars(s, tot2, dsum_rows, beta_bits);
+        load_raw(c + 1, 1);   // the next chunk's q and k (the operands of chunk c are out of their registers)
         if (!exact) {
             signal(C_OPS);
             wait_ge(C_OPS, 4 * (c + 1));   // every intra wave's operands are in
-            wait_ge(C_T, c);               // chunk c - 1's inversion is done with Akk's space
+            wait_ge(C_T, 4 * c);           // chunk c - 1's inversion is done with Akk's space
             switch (wi) {
                 case 0: intra_products(std::integral_constant<int, 0>{}, s); break;
                 case 1: intra_products(std::integral_constant<int, 1>{}, s); break;
@@ -957,7 +971,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
             }
         } else {
             isync();   // every intra wave's fast-path stores are done (staging overwrites them)
-            wait_ge(C_T, c);               // chunk c - 1's inversion is done with Akk's space (k^T is staged there)
+            wait_ge(C_T, 4 * c);           // chunk c - 1's inversion is done with Akk's space (k^T is staged there)
             // Exact path (rare: a chunk decaying past e^-16).  The chunk's inputs are
             // loaded again (the registers already hold the next chunk's) into a
             // staging area, and everything else is computed from there.
