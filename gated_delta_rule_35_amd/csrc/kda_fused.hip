@@ -678,14 +678,15 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         }
         if (wi == 0 && (part & 2)) {
             // beta of token ln (the dtype is a template parameter: no branch around
-            // the load, so no wait for it at a join)
+            // the load, so no wait for it at a join; a bf16 value is kept as loaded
+            // and widened to fp32 where it is stored, so nothing here waits for it)
             const int esz = BETA_F32 ? 4 : 2;
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(
                 reinterpret_cast<const char*>(p.beta) + (t0 * p.Hv + hv) * esz, Lc ? ((Lc - 1) * (int64_t)p.Hv + 1) * esz : 0);
             if constexpr (BETA_F32)
                 bb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, ln * p.Hv * 4, 0, 0);
             else
-                bb = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, ln * p.Hv * 2, 0, 0) << 16;
+                bb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, ln * p.Hv * 2, 0, 0);
         }
     };
     // Chunk c's inputs (past the last chunk: a zero-length range, so no access and
@@ -832,7 +833,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) dg[4 * t] = dsum_rows[t];
         }
-        if (wi == 0) beta_slot(s)[ln] = __uint_as_float(beta_bits);
+        if (wi == 0) beta_slot(s)[ln] = __uint_as_float(BETA_F32 ? beta_bits : beta_bits << 16);
     };
     // Intra products on MFMA: the ten lower-triangular 16x16 tiles of Aqk^T and of
     // Akk^T, five per wave: Aqk tiles wi and wi + 4, Akk tiles wi and wi + 4, then
@@ -1000,7 +1001,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
                     *reinterpret_cast<uint2*>(sQ + (cc + ch) * 64 + row0) = make_uint2(q4[0] | (q4[1] << 16), q4[2] | (q4[3] << 16));
                     *reinterpret_cast<uint2*>(sK + (cc + ch) * 64 + row0) = make_uint2(k4[0] | (k4[1] << 16), k4[2] | (k4[3] << 16));
                 }
-                if (wi == 0) beta_slot(s)[ln] = __uint_as_float(beta_bits);
+                if (wi == 0) beta_slot(s)[ln] = __uint_as_float(BETA_F32 ? beta_bits : beta_bits << 16);
             }
             isync();   // staging complete
             // This lane's operands anchored at A = 0: q e^G, -(k e^G) and the transposed
