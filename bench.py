@@ -5,19 +5,23 @@
 
 A step is one KDA forward over the whole batch of the workload (default: B=2,
 H=64, T=8192, dk=dv=128, chunk 64, fp32 beta, initial state ~ 0.1 N(0,1)) with
-all inputs, outputs and the workspace already resident in HBM: the two kernels
-of kda_fwd, launched through its two stage entry points (kda_fwd_intra, then
-kda_fwd_scan, which together are exactly kda_fwd) so that HIP events on the
-launch stream bracket each kernel.  The K timed steps are bracketed by device
-synchronisation; value = tokens / wall time per step.
+all inputs, outputs and the workspace already resident in HBM, in one of the
+library's two forms: kda_fwd_fused (one launch of the single-pass kernel) or
+kda_fwd_ws (the two kernels of kda_fwd on a caller-owned workspace).  With
+--form auto (the default) both forms are timed, each for 20 calls after a
+settle phase of its own, and the faster one is the step (settled again before
+its warm-up); the JSON names it and gives both probe times.  The K timed steps are bracketed by device synchronisation;
+value = tokens / wall time per step.
 
 Roofline (HBM-bound): the forward's algorithmic bytes (q, k, v, g, beta read
 once, o written once, the initial state read if given, the final state
-written) divided by the summed average durations of the two kernels, against
-8 TB/s.  Each kernel is also reported against its own algorithmic bytes (what
-it must move in this design: the intra kernel reads q, k, g, beta and writes
-one 61,952-byte record per chunk and value head; the scan kernel reads v and
-the records and writes o and the states).  The MFMA side uses the
+written) divided by the step's kernel time (HIP events on the launch stream):
+the average duration of kda_fused_kernel, or the summed average durations of
+the two-pass kernels, timed in batches of their own through the stage entry
+points kda_fwd_intra and kda_fwd_scan.  Each two-pass kernel is also reported
+against its own algorithmic bytes (the intra kernel reads q, k, g, beta and
+writes one 61,952-byte record per chunk and value head; the scan kernel reads
+v and the records and writes o and the states).  The MFMA side uses the
 algorithmic flop count of the chunked method (4,512,416 MAC per full 64-token
 chunk and value head).
 
@@ -568,6 +572,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha_b2_h64_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--form", choices=("auto", "two-pass", "fused"), default="auto",
+                    help="forward form of the timed step (auto: the faster of the two in a short probe)")
     ap.add_argument("--cpu-heads", type=int, default=64, help="value heads in the oracle's timing sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the oracle's sample is run repeatedly until this much wall time has passed")
@@ -635,20 +641,51 @@ def main():
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
 
-    from gated_delta_rule_35_amd import kda_fwd, kda_fwd_ws
+    from gated_delta_rule_35_amd import kda_fwd, kda_fwd_fused, kda_fwd_ws
 
-    def step():
+    def step_two_pass():
         # the whole forward with a caller-owned workspace (kda_fwd_ws): the two
         # kernels and nothing else
         kda_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
                    out=out, final_state=hT, workspace=ws)
 
+    def step_fused():
+        # the whole forward in one launch of kda_fused_kernel (nothing allocated)
+        kda_fwd_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
+                      out=out, final_state=hT)
+
+    forms = {"two-pass": step_two_pass, "fused": step_fused}
+    entry = {"two-pass": "kda_fwd_ws", "fused": "kda_fwd_fused"}
+
+    def events_ms(call, n):
+        # average of n calls, HIP events on the launch stream around each call
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for e in ev:
+            e[0].record(stream)
+            call()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in ev) / n
+
+    probe = None
+    if args.form == "auto":
+        # each form in its own steady state: a settle phase of its own, then 20
+        # calls (the first calls of one form after the other run slower)
+        probe = {}
+        for k, f in forms.items():
+            settle(f)
+            probe[k] = round(events_ms(f, 20), 5)
+        form = min(probe, key=probe.get)
+        log(f"form probe (ms per call, 20 calls each after its own settle phase): {probe} -> {form}")
+    else:
+        form = args.form
+    step = forms[form]
     settle(step)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps of kda_fwd_ws")
+    log(f"timing {args.steps} steps of {entry[form]}")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -717,25 +754,15 @@ def main():
     cold = [e[0].elapsed_time(e[1]) for e in evc]
     t_cold = sum(cold) / len(cold) / 1e3
     del flush, flush_sum
-    log(f"kda_fwd_ws after a cache flush: {t_cold * 1e3:.4f} ms per call (min {min(cold):.4f})")
+    log(f"{entry[form]} after a cache flush: {t_cold * 1e3:.4f} ms per call (min {min(cold):.4f})")
 
     # kda_fwd_fused, the single-pass kernel, on the same inputs (HIP events around
     # each call: one launch of kda_fused_kernel)
-    from gated_delta_rule_35_amd import kda_fwd_fused
     for _ in range(2):
-        kda_fwd_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
-                      out=out, final_state=hT)
+        step_fused()
     torch.cuda.synchronize()
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in evf:
-        e[0].record(stream)
-        kda_fwd_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
-                      out=out, final_state=hT)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    callf = [e[0].elapsed_time(e[1]) for e in evf]
-    t_fused = sum(callf) / len(callf) / 1e3
-    log(f"kda_fwd_fused avg {t_fused * 1e3:.4f} ms per call (min {min(callf):.4f})")
+    t_fused = events_ms(step_fused, args.steps) / 1e3
+    log(f"kda_fwd_fused avg {t_fused * 1e3:.4f} ms per call")
 
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes(n_tok, N, w.Hq, w.Hv, beta_bytes, w.has_h0)
@@ -750,21 +777,27 @@ def main():
         kernels[name] = {"ms_avg": round(kt[name] * 1e3, 5), "algorithmic_bytes": kbytes[name],
                          "achieved": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
                          "traffic": traffic.get(name) if traffic else None}
-    achieved_gbs = nbytes / t_kern / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+    two_gbs = nbytes / t_kern / 1e9
+    two_pass = {"ms_avg": round(t_kern * 1e3, 5), "achieved": round(two_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(two_gbs / HBM_PEAK_GBS, 4),
                 "traffic": sum(traffic[k] for k in KERNELS) if traffic else None,
-                "scope": "whole forward: algorithmic bytes of the forward over the summed average durations of "
+                "scope": "kda_fwd_ws: algorithmic bytes of the forward over the summed average durations of "
                          "kda_intra_kernel and kda_scan_kernel",
                 "kernels": kernels}
     fused_gbs = nbytes / t_fused / 1e9
     fused = {"ms_avg": round(t_fused * 1e3, 5), "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
              "traffic": traffic.get("kda_fused_kernel") if traffic else None,
-             "scope": "kda_fwd_fused (one launch of kda_fused_kernel): algorithmic bytes of the forward over its "
-                      "average duration; not the headline path (kda_fwd runs the two-pass kernels)"}
-    mfma = {"achieved": round(flops / t_kern / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(flops / t_kern / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+             "scope": "kda_fwd_fused: algorithmic bytes of the forward over the average duration of "
+                      "kda_fused_kernel"}
+    # the roofline of the step's own form; the other form's figures stay beside it
+    t_step_kern = t_fused if form == "fused" else t_kern
+    roofline = {"bound": "hbm", **{k: v for k, v in (fused if form == "fused" else two_pass).items()
+                                   if k in ("achieved", "peak", "unit", "frac", "traffic", "scope")}}
+    roofline["kernel"] = "kda_fused_kernel" if form == "fused" else "kda_intra_kernel + kda_scan_kernel"
+    roofline["kernel_ms_avg"] = round(t_step_kern * 1e3, 5)
+    mfma = {"achieved": round(flops / t_step_kern / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / t_step_kern / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "algorithmic_flop_per_launch": flops}
 
     cpu = None
@@ -792,19 +825,23 @@ def main():
                    "beta_dtype": "fp32" if beta_bytes == 4 else "bf16", "initial_state": bool(w.has_h0),
                    "dv_slices": kda_dv_slices(N, w.Hv), "mfma_operands": "f16", "accumulate": "f32",
                    "io": "bf16 q/k/v/o, f32 g/state"},
-        "step": "kda_fwd_ws: the whole forward on a caller-owned workspace (the two kernels)",
+        "step": ("kda_fwd_fused: the whole forward in one launch of kda_fused_kernel" if form == "fused" else
+                 "kda_fwd_ws: the whole forward on a caller-owned workspace (the two kernels)"),
+        "form": form,
+        "form_probe_ms": probe,
         "settle_s": SETTLE_S,
-        "kernel_ms_avg": round(t_kern * 1e3, 5),
+        "kernel_ms_avg": round(t_step_kern * 1e3, 5),
         "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
-        "host_enqueue_ms": {"kda_fwd_ws": round(t_enq * 1e3, 4), "kda_fwd": round(t_enq11 * 1e3, 4),
+        "host_enqueue_ms": {entry[form]: round(t_enq * 1e3, 4), "kda_fwd": round(t_enq11 * 1e3, 4),
                             "scope": "host time from the first call of the timed loop to the return of the last, "
                                      "before the synchronisation, per call (argument checks, descriptor "
                                      "marshalling, launches; kda_fwd also its stream-ordered allocation)"},
         "cold_cache": {"ms_avg": round(t_cold * 1e3, 5), "tokens_per_s": round(n_tok / t_cold, 1),
-                       "scope": "kda_fwd_ws with a 1 GiB buffer read before each call (outside the HIP events), "
-                                "so no input is left in the 256 MB last-level cache"},
+                       "scope": f"{entry[form]} with a 1 GiB buffer read before each call (outside the HIP "
+                                "events), so no input is left in the 256 MB last-level cache"},
         "algorithmic_bytes_per_step": nbytes,
         "roofline": roofline,
+        "two_pass": two_pass,
         "fused": fused,
         "mfma": mfma,
         "cpu_baseline": cpu,
