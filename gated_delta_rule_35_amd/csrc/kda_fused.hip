@@ -75,10 +75,10 @@ struct FL {
     // Intra waves only:
     static constexpr int A32 = TB + 2 * AB_SZ;       // [64][68] fp32 Akk, then T's blocks
     static constexpr int TtD = A32 + 64 * S68 * 4;   // 4 diagonal T blocks, column-major
-    static constexpr int T1t = TtD + 4 * 16 * TS * 4;
-    static constexpr int Xt = T1t + 2 * 16 * TS * 4;
+    static constexpr int T1t = TtD + 4 * 16 * TS * 4;   // T_10, column-major
+    static constexpr int Xt = T1t + 16 * TS * 4;         // X_21, column-major
     static constexpr int SC_SZ = 3 * 128 * 4;
-    static constexpr int SC = Xt + 4 * 16 * TS * 4;  // two slots: per channel a [128], b [128], d [128] fp32
+    static constexpr int SC = Xt + 16 * TS * 4;      // two slots: per channel a [128], b [128], d [128] fp32
     static constexpr int BETA = SC + 2 * SC_SZ;      // two slots: [64] fp32
     static constexpr int DIAG = BETA + 2 * 64 * 4;   // [64 row][4] fp32: q_i . k_i over each intra wave's channels
     static constexpr int VT = DIAG + 4 * 64 * 4;     // [64 dv][64 token] v^T of the chunk (bf16, swizzled rows)
@@ -330,7 +330,9 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         //            w1: X_20, X_30, T_30 = -(T_32 X_20 + T_33 X_30)
         //            w2: T_21 = -T_22 X_21           w3: T_31 = -(T_32 X_21 + T_33 X_31)
         // with a scan-wave rendezvous between levels (waves 0 and 1 each form X_20,
-        // so the block row 3 needs no third level).
+        // so the block row 3 needs no third level).  A product's accumulators serve as
+        // the next product's B operand in registers; only T_10, T_32 and X_21, which
+        // other waves read, go through LDS.
         int tv = 0;   // running target of the scan waves' rendezvous counter
         auto vsync = [&]() {
             signal(C_V);
@@ -339,17 +341,9 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         };
         auto inversion = [&](int s) {
             float* sTtD = reinterpret_cast<float*>(smem + FL::TtD);
-            float* sT1t = reinterpret_cast<float*>(smem + FL::T1t);
-            float* sXt = reinterpret_cast<float*>(smem + FL::Xt);
             const int tbo = FL::TB + s * FL::AB_SZ;
             const float* sb = beta_slot(s);
             const int ln = opaque(lane);
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            auto neg = [](f32x4 v) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = -v[e];
-                return v;
-            };
             auto A = [&](int I, int J) { return sA32 + (16 * I) * S68 + 16 * J; };   // row-major block
             {
                 // level 0: block B = wave; lanes 16 .. 63 repeat lanes 0 .. 15
@@ -402,56 +396,64 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
                 return v;
             };
             auto A = [&](int I, int J) { return sA32 + (16 * I) * S68 + 16 * J; };   // row-major block
+            // This lane's A operand rows of block (I, J) of A32 (row-major).
+            auto arow = [&](int I, int J) {
+                return *reinterpret_cast<const f32x4*>(A(I, J) + (ln & 15) * S68 + 4 * (ln >> 4));
+            };
+            // A product's accumulators as the B operand of the next product: mm16's B
+            // operand of lane (g, j) is rows 4 g .. 4 g + 3 of column j, exactly the rows
+            // the lane's accumulator registers hold, so a block stays in registers
+            // unless another wave reads it.
+            auto chained = [](f32x4 a, f32x4 b) { return Mm16Ops{a, b}; };
+            f32x4 x31 = z4;   // wave 3's X_31, kept for the second level
             if (wave < 2) {
                 // T_I,I-1 = -T_II (A_I,I-1 T_I-1,I-1), I = 1 (wave 0), 3 (wave 1)
                 const int I = 2 * wave + 1;
-                float* y = sT1t + wave * 16 * TS;
-                store_colmajor(y, mm16_mac(mm16_ops(A(I, I - 1), S68, sTtD + (I - 1) * 16 * TS, TS, ln), z4), ln);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                const f32x4 t = neg(mm16_mac(mm16_ops(A(I, I), S68, y, TS, ln), z4));
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the reads of y before its overwrite
+                const f32x4 tii = arow(I, I);   // T_II, row-major over A_II
+                const f32x4 x = mm16_mac(mm16_ops(A(I, I - 1), S68, sTtD + (I - 1) * 16 * TS, TS, ln), z4);
+                const f32x4 t = neg(mm16_mac(chained(tii, x), z4));
                 if (wave == 0)
-                    store_colmajor(y, t, ln);                  // T_10, column-major
+                    store_colmajor(sT1t, t, ln);               // T_10, column-major
                 else
                     store_rowmajor(A(3, 2), S68, t, ln);       // T_32 over A_32, row-major
                 store_tb(smem, tbo, t, I, I - 1, sb, ln);
             } else {
-                // X_21 (wave 2), X_31 (wave 3) = A_I1 T_11
-                const int I = wave;
-                store_colmajor(sXt + (2 * (I - 2) + 1) * 16 * TS,
-                               mm16_mac(mm16_ops(A(I, 1), S68, sTtD + 16 * TS, TS, ln), z4), ln);
+                // X_21 (wave 2; waves 2 and 3 read it), X_31 (wave 3) = A_I1 T_11
+                const f32x4 x = mm16_mac(mm16_ops(A(wave, 1), S68, sTtD + 16 * TS, TS, ln), z4);
+                if (wave == 2)
+                    store_colmajor(sXt, x, ln);
+                else
+                    x31 = x;
             }
             vsync();
-            // levels 2 and 3 together: X_20 is formed by both waves that need it
-            if (wave == 0 || wave == 1) {
-                // X_20 = A_20 T_00 + A_21 T_10 (a private copy per wave)
+            // the second level; X_20 is formed by both waves that need it
+            if (wave < 2) {
+                // X_20 = A_20 T_00 + A_21 T_10
                 const Mm16Ops a = mm16_ops(A(2, 0), S68, sTtD, TS, ln);
                 const Mm16Ops b = mm16_ops(A(2, 1), S68, sT1t, TS, ln);
-                float* xs = sXt + (wave == 0 ? 0 : 2) * 16 * TS;
-                store_colmajor(xs, mm16_mac(b, mm16_mac(a, z4)), ln);
                 if (wave == 0) {
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                     // T_20 = -T_22 X_20
-                    store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, xs, TS, ln), z4)), 2, 0, sb, ln);
+                    const f32x4 t22 = arow(2, 2);
+                    const f32x4 x20 = mm16_mac(b, mm16_mac(a, z4));
+                    store_tb(smem, tbo, neg(mm16_mac(chained(t22, x20), z4)), 2, 0, sb, ln);
                 } else {
                     // X_30 = A_30 T_00 + A_31 T_10 ; T_30 = -(T_32 X_20 + T_33 X_30)
                     const Mm16Ops a3 = mm16_ops(A(3, 0), S68, sTtD, TS, ln);
                     const Mm16Ops b3 = mm16_ops(A(3, 1), S68, sT1t, TS, ln);
-                    float* x30 = sT1t + 16 * TS;   // wave 1's level-1 scratch, free now
-                    store_colmajor(x30, mm16_mac(b3, mm16_mac(a3, z4)), ln);
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    const Mm16Ops c2 = mm16_ops(A(3, 2), S68, xs, TS, ln);
-                    const Mm16Ops c3 = mm16_ops(A(3, 3), S68, x30, TS, ln);
-                    store_tb(smem, tbo, neg(mm16_mac(c3, mm16_mac(c2, z4))), 3, 0, sb, ln);
+                    const f32x4 t32 = arow(3, 2), t33 = arow(3, 3);
+                    const f32x4 x20 = mm16_mac(b, mm16_mac(a, z4));
+                    const f32x4 x30 = mm16_mac(b3, mm16_mac(a3, z4));
+                    store_tb(smem, tbo, neg(mm16_mac(chained(t33, x30), mm16_mac(chained(t32, x20), z4))), 3, 0, sb,
+                             ln);
                 }
             } else if (wave == 2) {
                 // T_21 = -T_22 X_21
-                store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, sXt + 16 * TS, TS, ln), z4)), 2, 1, sb, ln);
+                store_tb(smem, tbo, neg(mm16_mac(mm16_ops(A(2, 2), S68, sXt, TS, ln), z4)), 2, 1, sb, ln);
             } else {
                 // T_31 = -(T_32 X_21 + T_33 X_31)
-                const Mm16Ops a = mm16_ops(A(3, 2), S68, sXt + 16 * TS, TS, ln);
-                const Mm16Ops b = mm16_ops(A(3, 3), S68, sXt + 3 * 16 * TS, TS, ln);
-                store_tb(smem, tbo, neg(mm16_mac(b, mm16_mac(a, z4))), 3, 1, sb, ln);
+                const Mm16Ops a = mm16_ops(A(3, 2), S68, sXt, TS, ln);
+                const f32x4 t33 = arow(3, 3);
+                store_tb(smem, tbo, neg(mm16_mac(chained(t33, x31), mm16_mac(a, z4))), 3, 1, sb, ln);
             }
         };
         if (nch > 0) {
