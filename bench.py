@@ -10,8 +10,10 @@ library's two forms: kda_fwd_fused (one launch of the single-pass kernel) or
 kda_fwd_ws (the two kernels of kda_fwd on a caller-owned workspace).  With
 --form auto (the default) both forms are timed, each for 20 calls after a
 settle phase of its own, and the faster one is the step (settled again before
-its warm-up); the JSON names it and gives both probe times.  The K timed steps are bracketed by device synchronisation;
-value = tokens / wall time per step.
+its warm-up); the JSON names it and gives both probe times.  The K timed
+steps are bracketed by device synchronisation; value = tokens / wall time per
+step.  `call_events` then times 50 more calls of the same form, each between
+HIP events on the launch stream: median, minimum, mean and maximum.
 
 Roofline (HBM-bound): the forward's algorithmic bytes (q, k, v, g, beta read
 once, o written once, the initial state read if given, the final state
@@ -657,15 +659,18 @@ def main():
     forms = {"two-pass": step_two_pass, "fused": step_fused}
     entry = {"two-pass": "kda_fwd_ws", "fused": "kda_fwd_fused"}
 
-    def events_ms(call, n):
-        # average of n calls, HIP events on the launch stream around each call
+    def events_list(call, n):
+        # n calls, HIP events on the launch stream around each call: ms per call
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
         for e in ev:
             e[0].record(stream)
             call()
             e[1].record(stream)
         torch.cuda.synchronize()
-        return sum(e[0].elapsed_time(e[1]) for e in ev) / n
+        return [e[0].elapsed_time(e[1]) for e in ev]
+
+    def events_ms(call, n):
+        return sum(events_list(call, n)) / n
 
     probe = None
     if args.form == "auto":
@@ -696,6 +701,12 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     tokens_per_s = n_tok / (ms_per_step / 1e3)
     log(f"{ms_per_step:.4f} ms/step (wall), {tokens_per_s / 1e6:.2f} M tokens/s")
+    # the same form call by call: 50 calls, each between HIP events
+    per_call = sorted(events_list(step, 50))
+    call_events = {"calls": 50, "median_ms": round((per_call[24] + per_call[25]) / 2, 5), "min_ms": round(per_call[0], 5),
+                   "mean_ms": round(sum(per_call) / 50, 5), "max_ms": round(per_call[-1], 5)}
+    log(f"{entry[form]} per call (HIP events, 50 calls): median {call_events['median_ms']:.4f} ms, "
+        f"min {call_events['min_ms']:.4f} ms")
 
     # Per-kernel durations, in passes of their own so that no timing event sits inside
     # the timed steps: args.steps launches of each kernel back to back (the scan reads
@@ -831,6 +842,7 @@ def main():
         "form_probe_ms": probe,
         "settle_s": SETTLE_S,
         "kernel_ms_avg": round(t_step_kern * 1e3, 5),
+        "call_events": call_events,
         "kda_fwd_call_ms_avg": round(t_call11 * 1e3, 5),
         "host_enqueue_ms": {entry[form]: round(t_enq * 1e3, 4), "kda_fwd": round(t_enq11 * 1e3, 4),
                             "scope": "host time from the first call of the timed loop to the return of the last, "
