@@ -730,9 +730,10 @@ def main():
     t_kern = t_intra + t_scan
     log(f"intra kernel avg {t_intra * 1e3:.4f} ms, scan kernel avg {t_scan * 1e3:.4f} ms")
 
-    # The eleven-argument kda_fwd, whose workspace comes from hipMallocAsync /
-    # hipFreeAsync on the stream inside the call, timed like the steps above right
-    # after its own warm-up.
+    # The eleven-argument kda_fwd (the single-pass kernel on fixed-length batches
+    # that fill the device; else the two-pass kernels on a workspace from
+    # hipMallocAsync / hipFreeAsync on the stream inside the call), timed like the
+    # steps above right after its own warm-up.
     def call11():
         kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
                 out=out, final_state=hT)
@@ -745,7 +746,7 @@ def main():
     t_enq11 = (time.perf_counter() - t0) / args.steps
     torch.cuda.synchronize()
     t_call11 = (time.perf_counter() - t0) / args.steps
-    log(f"kda_fwd (eleven arguments, workspace allocated in the call) {t_call11 * 1e3:.4f} ms per call (wall)")
+    log(f"kda_fwd (eleven arguments) {t_call11 * 1e3:.4f} ms per call (wall)")
 
     # The same step with the last-level cache flushed before each call: a 1 GiB
     # buffer (four times the 256 MB MALL) is read between the calls, outside the

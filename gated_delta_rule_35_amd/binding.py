@@ -207,8 +207,10 @@ def kda_fwd(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None, out=No
             stream=None, workspace=None):
     """KDA forward.  Returns (out, final_state); allocates them when not given
     (final_state is allocated only when `final_state=True` is passed).
-    Without `workspace` this is the C kda_fwd; with a uint8 device tensor of at
-    least kda_fwd_workspace_size() bytes it is kda_fwd_ws on that workspace."""
+    Without `workspace` this is the C kda_fwd (the single-pass kernel on
+    fixed-length batches that fill the device, else the two-pass kernels); with a
+    uint8 device tensor of at least kda_fwd_workspace_size() bytes it is
+    kda_fwd_ws (the two-pass kernels) on that workspace."""
     out, final_state = _outputs(q, v, cu_seqlens, out, final_state)
     entry = "kda_fwd" if workspace is None else "kda_fwd_ws"
     _call(q, k, v, g, beta, scale, cu_seqlens, initial_state, out, final_state, stream, None, workspace, entry)

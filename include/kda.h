@@ -82,6 +82,15 @@ typedef enum {
 /*
  * kda_fwd -- the KDA forward pass over a batch.
  *
+ * Two forms compute it: the single-pass kernel of kda_fwd_fused, and two
+ * kernels (chunk-parallel intra work, then the sequential scan) that hand each
+ * chunk's operands over through a device workspace.  kda_fwd takes the
+ * single-pass kernel for fixed-length batches (no cu_seqlens) of at least 1024
+ * tokens per row whose B * Hv * 2 work-groups cover every compute unit of the
+ * current device, and the two-pass kernels otherwise; the two forms round
+ * differently in the last bits (see Precision), and for a given shape and
+ * device the choice never changes.
+ *
  * Enqueues the work on `stream` (a hipStream_t; NULL is the null stream) and
  * returns without waiting: the host never reads device memory, so the number of
  * sequences comes from the shape of cu_seqlens, not its values.  Every argument
@@ -91,17 +100,19 @@ typedef enum {
  * initial_state may alias final_state (each state tile is read before it is
  * written, by the same work-group); a partial overlap of the two returns
  * KDA_ERR_LAYOUT.
- * Device memory beyond the caller's tensors, if the call needs any, is
- * allocated with hipMallocAsync on `stream` and released with hipFreeAsync on
- * it, so calls on different streams never share it.
+ * The two-pass form needs a workspace: kda_fwd allocates it with
+ * hipMallocAsync on `stream` and releases it with hipFreeAsync on it, so calls
+ * on different streams never share it (kda_fwd_ws takes the caller's instead);
+ * the single-pass form allocates nothing.
  * cu_seqlens must be non-decreasing with cu_seqlens[0] = 0 and
  * cu_seqlens[N] <= T.  That is a precondition the host cannot check without a
  * device read; the kernel clamps every sequence to [0, T) so that malformed
  * values never cause an out-of-bounds access.
  * Precision: q, k, v are bf16; the MFMA operands derived from them are fp16
  * and all accumulation, the gate cumsum, the inversion and the state are
- * fp32.  A chunk whose decay within a 16-token block exceeds exp(-8) on some
- * channel takes an exact fp32 path for its diagonal blocks.  The fp16
+ * fp32.  In the two-pass form, a chunk whose decay within a 16-token block
+ * exceeds exp(-8) on some channel takes an exact fp32 path for its diagonal
+ * blocks; the single-pass form anchors per chunk (see kda_fwd_fused).  The fp16
  * operands bound the range: entries of the state and of v_new must stay
  * below 65504 in magnitude (L2-normalised q and k, values of order one and
  * g <= 0 keep them orders of magnitude below it).
@@ -123,9 +134,11 @@ kda_status_t kda_fwd(const kda_tensor_t* q, const kda_tensor_t* k, const kda_ten
  * Precision: as kda_fwd's, except that the decay anchor is per 64-token chunk:
  * a chunk whose total decay exceeds exp(-16) on some channel takes an exact fp32
  * path (Aqk and Akk element by element, operands with every factor <= 1).
- * It runs N * Hv * 2 work-groups of 512 threads with about 158 KB of LDS each,
- * one per CU: it is meant for batches with at least that many (sequence, head)
- * pairs; with fewer, kda_fwd is faster.  More than 2^31 - 1 work-groups return
+ * It runs N * Hv * 2 work-groups of 512 threads with about 153 KB of LDS each,
+ * one per CU: it is meant for batches with at least that many work-groups and
+ * sequences of equal length; kda_fwd takes it by itself where that holds (see
+ * kda_fwd), and with fewer work-groups or packed sequences of unequal length
+ * the two-pass form is faster.  More than 2^31 - 1 work-groups return
  * KDA_ERR_UNSUPPORTED.
  */
 kda_status_t kda_fwd_fused(const kda_tensor_t* q, const kda_tensor_t* k, const kda_tensor_t* v,

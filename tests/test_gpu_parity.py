@@ -21,9 +21,13 @@ def _say(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-# Every forward test runs on both forms of the forward: kda_fwd (the two-pass
-# kernels) and kda_fwd_fused (the single-pass kernel).  Tests of one form's own
-# machinery (stage traces, workspaces, stage calls) carry the two_pass_only mark.
+# Every forward test runs on both forms of the forward: kda_fwd, which takes the
+# two-pass kernels at the sizes these tests use (below 1024 tokens per row, fewer
+# work-groups than CUs, or packed batches), and kda_fwd_fused (the single-pass
+# kernel).  The full-size tests call the two-pass form as kda_fwd_ws, since
+# kda_fwd takes the single-pass kernel on batches that fill the device (tested
+# bit for bit below).  Tests of one form's own machinery (stage traces,
+# workspaces, stage calls) carry the two_pass_only mark.
 ENTRIES = {"kda_fwd": kda_fwd, "kda_fwd_fused": kda_fwd_fused}
 FWD = kda_fwd
 
@@ -389,10 +393,13 @@ FULL = ["mha_b2_h64_t4096", "mha_b2_h64_t8192", "gva_b1_hq16_hv64_t4096", "varle
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_workloads_every_head(name):
-    """The full workload, in the launch configuration bench.py times (kda_fwd),
-    into outputs prefilled with NaN: every element of o and of the final state
-    must be written, and every (sequence, value head) must match the oracle."""
+def test_full_size_workloads_every_head(name, entry):
+    """The full workload in each form (the two-pass kernels as kda_fwd_ws, and
+    kda_fwd_fused), in the launch configuration bench.py times, into outputs
+    prefilled with NaN: every element of o and of the final state must be
+    written, and every (sequence, value head) must match the oracle."""
+    from gated_delta_rule_35_amd import kda_fwd_ws
+    fwd = kda_fwd_ws if entry == "kda_fwd" else FWD
     w = WORKLOADS[name]
     x, cu = workload_inputs(w)
     d = to_device(x)
@@ -400,9 +407,9 @@ def test_full_size_workloads_every_head(name):
     N = x["q"].shape[0] if cu is None else cu.shape[0] - 1
     out = torch.full_like(d["v"], float("nan"))
     hT = torch.full((N, w.Hv, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
-    _say(f"full workload {name}: kda_fwd into NaN-filled outputs")
-    FWD(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, cu_seqlens=cu_d, initial_state=d["h0"], out=out,
-            final_state=hT)
+    _say(f"full workload {name}: {'kda_fwd_ws' if entry == 'kda_fwd' else entry} into NaN-filled outputs")
+    fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, cu_seqlens=cu_d, initial_state=d["h0"], out=out,
+        final_state=hT)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     h = hT.cpu().numpy()
@@ -438,6 +445,32 @@ def test_full_size_two_pass_form_agrees(name):
                   out=o2, final_state=h2)
     kda_fwd_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, ws, cu_seqlens=cu_d, initial_state=d["h0"],
                  out=o2, final_state=h2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
+
+
+@pytest.mark.two_pass_only
+@pytest.mark.parametrize("B,T,Hq,Hv,packed", [(2, 1024, 64, 64, False), (2, 2048, 8, 64, False),
+                                              (1, 1024, 16, 64, False), (2, 512, 64, 64, False),
+                                              (1, 2048, 64, 64, True)])
+def test_kda_fwd_chooses_its_form(B, T, Hq, Hv, packed):
+    """kda_fwd takes the single-pass kernel for fixed-length batches of at least
+    1024 tokens per row whose B * Hv * 2 work-groups cover the device's CUs, and
+    the two-pass kernels otherwise: its outputs equal that form's bit for bit."""
+    from gated_delta_rule_35_amd import kda_fwd_ws
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cu = cu_from_lengths([700, T - 700]) if packed else None
+    x = make_inputs(B, T, Hq, Hv, torch.float32, h0=True, N=2 if packed else None, seed=111 + T + Hv)
+    expect_fused = not packed and T >= 1024 and B * Hv * 2 >= cus
+    _say(f"kda_fwd form choice B={B} T={T} Hq={Hq} Hv={Hv} packed={packed}: expect "
+         f"{'kda_fwd_fused' if expect_fused else 'kda_fwd_ws'} ({cus} CUs)")
+    d = to_device(x)
+    cu_d = cu.to("cuda") if cu is not None else None
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], SCALE)
+    o1, h1 = kda_fwd(*args, cu_seqlens=cu_d, initial_state=d["h0"], final_state=True)
+    ref = kda_fwd_fused if expect_fused else kda_fwd_ws
+    o2, h2 = ref(*args, cu_seqlens=cu_d, initial_state=d["h0"], final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
