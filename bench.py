@@ -17,10 +17,10 @@ HIP events on the launch stream: median, minimum, mean and maximum.
 
 Roofline (HBM-bound): the forward's algorithmic bytes (q, k, v, g, beta read
 once, o written once, the initial state read if given, the final state
-written) divided by the step's kernel time (HIP events on the launch stream):
-the average duration of kda_fused_kernel, or the summed average durations of
-the two-pass kernels, timed in batches of their own through the stage entry
-points kda_fwd_intra and kda_fwd_scan.  Each two-pass kernel is also reported
+written) divided by the step's kernel time (HIP events on the launch stream): the
+mean of `call_events` when kda_fused_kernel is the step, or the summed average
+durations of the two-pass kernels, timed in batches of their own through the
+stage entry points kda_fwd_intra and kda_fwd_scan.  Each two-pass kernel is also reported
 against its own algorithmic bytes (the intra kernel reads q, k, g, beta and
 writes one 61,952-byte record per chunk and value head; the scan kernel reads
 v and the records and writes o and the states).  The MFMA side uses the
@@ -737,6 +737,7 @@ def main():
     def call11():
         kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, cu_seqlens=cu_d, initial_state=d["h0"],
                 out=out, final_state=hT)
+    settle(call11)
     for _ in range(args.warmup):
         call11()
     torch.cuda.synchronize()
@@ -768,12 +769,14 @@ def main():
     del flush, flush_sum
     log(f"{entry[form]} after a cache flush: {t_cold * 1e3:.4f} ms per call (min {min(cold):.4f})")
 
-    # kda_fwd_fused, the single-pass kernel, on the same inputs (HIP events around
-    # each call: one launch of kda_fused_kernel)
-    for _ in range(2):
-        step_fused()
-    torch.cuda.synchronize()
-    t_fused = events_ms(step_fused, args.steps) / 1e3
+    # kda_fwd_fused, the single-pass kernel (one launch of kda_fused_kernel): when
+    # it is the step, the 50 calls between HIP events right after the timed steps;
+    # else a settle phase of its own and then K calls between HIP events
+    if form == "fused":
+        t_fused = call_events["mean_ms"] / 1e3
+    else:
+        settle(step_fused)
+        t_fused = events_ms(step_fused, args.steps) / 1e3
     log(f"kda_fwd_fused avg {t_fused * 1e3:.4f} ms per call")
 
     beta_bytes = 4 if w.beta_dtype == torch.float32 else 2
