@@ -817,7 +817,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
 #pragma unroll
             for (int ch = 0; ch < 8; ++ch) {
                 sa[ch] = fexp2(0.5f * tot2[ch]);
-                sd[ch] = fexp2(tot2[ch] - 0.5f * tot2[ch]);
+                sd[ch] = sa[ch];   // e^{G_last - A} = e^A: tot2 - tot2 / 2 is tot2 / 2 exactly
             }
             char* scs = smem + FL::SC + s * FL::SC_SZ;
 #pragma unroll
@@ -838,16 +838,17 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         if (wi == 0) beta_slot(s)[ln] = __uint_as_float(BETA_F32 ? beta_bits : beta_bits << 16);
     };
     // Intra products on MFMA: the ten lower-triangular 16x16 tiles of Aqk^T and of
-    // Akk^T, five per wave: Aqk tiles wi and wi + 4, Akk tiles wi and wi + 4, then
-    // Aqk tile wi + 8 (waves 0, 1) or Akk tile wi + 6 (waves 2, 3); tile t is block
-    // (I, J) of the lower triangle in row order.  Instantiated per wave, so tile
+    // Akk^T, five per wave: Aqk and Akk tile wi, Aqk and Akk tile wi + 4 (each pair
+    // back to back, sharing its k e^{A-G} fragments), then Aqk tile wi + 8 (waves 0,
+    // 1) or Akk tile wi + 6 (waves 2, 3); tile t is block (I, J) of the lower
+    // triangle in row order.  Instantiated per wave, so tile
     // indices and masks are compile-time.  A tile's row scalar is read before the
     // next tile's fragments, so the epilogue waits only for its own data; the next
     // tile's fragments are read while this tile's MFMAs run.
     auto intra_products = [&](auto wi_c, int s) {
         constexpr int WI = decltype(wi_c)::value;
-        auto tile_m = [](int k) { return k < 4 ? (k >> 1) : (WI < 2 ? 0 : 1); };
-        auto tile_t = [](int k) { return k < 4 ? WI + 4 * (k & 1) : (WI < 2 ? WI + 8 : WI + 6); };
+        auto tile_m = [](int k) { return k < 4 ? (k & 1) : (WI < 2 ? 0 : 1); };
+        auto tile_t = [](int k) { return k < 4 ? WI + 4 * (k >> 1) : (WI < 2 ? WI + 8 : WI + 6); };
         auto tile_I = [](int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); };
         auto tile_J = [&](int t) { const int I = tile_I(t); return t - I * (I + 1) / 2; };
         const int ln = opaque(lane);
@@ -855,16 +856,16 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
         const int a0 = jj * RA + 16 * (g ^ jj);   // piece (g + 4 kk) of row 16 T + jj: (g ^ jj) ^ (4 kk ^ T)
         const float* sb = beta_slot(s);
         half8 fa[2][4], fb[2][4];
-        auto load_tile = [&](int k, half8 (&a)[4], half8 (&b)[4]) {
+        auto load_tile = [&](int k, half8 (&a)[4], half8 (&b)[4], const half8 (&prev_a)[4]) {
             const int t = tile_t(k), I = tile_I(t), J = tile_J(t);
             const int xb = tile_m(k) == 0 ? FL::QG : FL::KG;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                a[kk] = ld8(smem, FL::KI + (a0 ^ (16 * (4 * kk ^ J))) + 16 * J * RA);
+                a[kk] = (k & 1) && k < 4 ? prev_a[kk] : ld8(smem, FL::KI + (a0 ^ (16 * (4 * kk ^ J))) + 16 * J * RA);
                 b[kk] = ld8(smem, xb + (a0 ^ (16 * (4 * kk ^ I))) + 16 * I * RA);
             }
         };
-        load_tile(0, fa[0], fb[0]);
+        load_tile(0, fa[0], fb[0], fa[1]);
 #pragma unroll
         for (int k = 0; k < 5; ++k) {
             const int m = tile_m(k), t = tile_t(k), I = tile_I(t), J = tile_J(t);
@@ -879,7 +880,7 @@ __global__ void __launch_bounds__(FT, 1) kda_fused_kernel(const KdaParams p) {
             } else if (m == 1) {
                 rs = sb[i];
             }
-            if (k < 4) load_tile(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
+            if (k < 4) load_tile(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1], fa[k & 1]);
             __builtin_amdgcn_sched_barrier(0);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
